@@ -1,0 +1,96 @@
+/*
+ * nvfp4_oracle.h -- CPU oracle for the NVFP4-weight dense SwiGLU FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
+ * or call this code: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant
+ * with the HIP library.
+ *
+ * What it computes (plain, slow, obviously correct; fp64 accumulation):
+ *   - NVFP4 decode: value = e2m1(code) * e4m3(block scale) * tensor scale,
+ *     one E4M3 scale per 16 consecutive K elements.  The pages use NVFP4
+ *     weights without defining the format; the element/scale encodings are
+ *     the standard ones (OCP MX v1.0: E2M1 element, E4M3 "FN" scale).
+ *   - W4A16 projection y = x . W^T (page layers/dense_ffn_prefill.rs,
+ *     `w4a16_prefill_gemm`: one NVFP4 projection of m rows, n outputs, k in).
+ *   - silu_mul: a = silu(g) * u elementwise (page layers/dense_ffn_fixed.rs,
+ *     `forward_fixed`, the `ops::silu_mul` step, output written over gate).
+ *   - per-row NVFP4 activation quantizer and W4A4 projection (page
+ *     layers/dense_ffn_fixed.rs, module doc and `Fixed::W4a4`: NVFP4
+ *     activations with a row's bits independent of the row count).
+ *   - the dense FFN: gate, up, silu_mul, down (page
+ *     layers/dense_ffn_fixed.rs, `forward_fixed`; page
+ *     layers/dense_ffn_prefill.rs, `forward_prefill_inner`).
+ *
+ * Layout (host memory, row-major):
+ *   x, g, u, a, y : bf16 bit patterns (uint16_t) [rows][cols]
+ *   codes         : uint8 [n][k/2]; element 2j in the low nibble, 2j+1 high
+ *   scales        : uint8 [n][k/16], E4M3 (FN variant)
+ *   nibble bits   : s e1 e0 m
+ */
+#ifndef NVFP4_ORACLE_H
+#define NVFP4_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  const uint8_t *codes;  /* [n][k/2] */
+  const uint8_t *scales; /* [n][k/16] */
+  float ts;              /* per-tensor fp32 scale */
+  int n, k;
+} nvo_weight;
+
+/* Element and scale decoders (closed form). */
+double nvo_e2m1_value(uint8_t code);
+double nvo_e4m3_value(uint8_t byte);
+double nvo_bf16_value(uint16_t bits);
+/* One rounding of a double to bf16, round-to-nearest-even. */
+uint16_t nvo_bf16_from_double(double v);
+/* fp32 -> E4M3 / E2M1 code: round to nearest, ties to the even code,
+ * saturate to the largest finite magnitude, sign kept. */
+uint8_t nvo_e4m3_encode(float t);
+uint8_t nvo_e2m1_encode(float t);
+double nvo_silu(double t);
+void nvo_e4m3_encode_n(const float *t, uint8_t *out, int64_t n);
+void nvo_e2m1_encode_n(const float *t, uint8_t *out, int64_t n);
+void nvo_bf16_from_double_n(const double *v, uint16_t *out, int64_t n);
+
+/* W[r][kk] as doubles, [n][k]. */
+void nvo_dequant(const nvo_weight *w, double *out);
+
+/* y[m][n] = bf16(sum_k x[r][k] * W[c][k]); y_exact (optional) keeps the
+ * double sum before rounding.  nthreads <= 0: one per online CPU.
+ * Returns 0, or -1 on a shape error. */
+int nvo_gemm_w4a16(const uint16_t *x, int m, const nvo_weight *w,
+                   uint16_t *y, double *y_exact, int nthreads);
+
+void nvo_silu_mul(const uint16_t *g, const uint16_t *u, uint16_t *out,
+                  int64_t count);
+
+/* Per-row NVFP4 activation quantizer (fp32 steps, see the .c file). */
+int nvo_quantize_rows(const uint16_t *x, int m, int k, uint8_t *codes,
+                      uint8_t *scales, float *row_scale);
+
+/* W4A4: quantize x per row, then y = bf16(sum_k xhat * W). */
+int nvo_gemm_w4a4(const uint16_t *x, int m, const nvo_weight *w,
+                  uint16_t *y, double *y_exact, int nthreads);
+
+/* Dense SwiGLU FFN.  g/u/a (optional, [m][inter]) receive the bf16
+ * intermediates; y_exact (optional, [m][hidden]) the double down sum. */
+int nvo_dense_ffn(const uint16_t *x, int m, int hidden, int inter,
+                  const nvo_weight *wg, const nvo_weight *wu,
+                  const nvo_weight *wd, uint16_t *y, double *y_exact,
+                  uint16_t *g, uint16_t *u, uint16_t *a, int nthreads);
+int nvo_dense_ffn_w4a4(const uint16_t *x, int m, int hidden, int inter,
+                       const nvo_weight *wg, const nvo_weight *wu,
+                       const nvo_weight *wd, uint16_t *y, double *y_exact,
+                       uint16_t *g, uint16_t *u, uint16_t *a, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,112 @@
+"""Seeded synthetic inputs for the dense NVFP4 FFN workloads.
+
+Shared by the tests, the benchmark and the smoke check as *inputs* only: it
+holds none of the FFN's arithmetic (no NVFP4 decode, no GEMM, no quantizer).
+Value distributions are drawn with torch's CPU generator and cast with torch's
+own dtype conversions; no trained weights or datasets are involved.
+
+Workloads (the pages quote no shapes for their FFN measurements, so these
+stand in for them):
+
+* ``tiny``     m=4, hidden=256, inter=768
+* ``decode``   m=1, hidden=4096, inter=12288 (single-row decode)
+* ``smallm``   m=64, hidden=5120, inter=17408 (deep-K down projection)
+* ``prefill``  m=2048, hidden=5120, inter=17408, 1% of X entries x20
+* ``w4a4``     hidden=4096, inter=14336, m in {1, 8, 64, 512} sharing rows
+
+Weight recipe: E2M1 codes uniform over all 16 nibbles (so -0 appears),
+E4M3 block scales 2^u with u ~ U(-4, 0) cast to float8_e4m3fn by torch,
+tensor scale 1.0.  X ~ N(0, 1) cast to bf16 by torch.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+WORKLOADS = {
+    "tiny": dict(m=4, hidden=256, inter=768, outliers=False),
+    "decode": dict(m=1, hidden=4096, inter=12288, outliers=False),
+    "smallm": dict(m=64, hidden=5120, inter=17408, outliers=False),
+    "prefill": dict(m=2048, hidden=5120, inter=17408, outliers=True),
+    "w4a4": dict(m=512, hidden=4096, inter=14336, outliers=False),
+}
+
+W4A4_ROW_COUNTS = (1, 8, 64, 512)
+
+# stream ids under one seed
+_X, _WG_C, _WG_S, _WU_C, _WU_S, _WD_C, _WD_S, _OUTLIER = range(8)
+
+
+def _gen(seed: int, stream: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 256 + stream)
+    return g
+
+
+@dataclass
+class NvWeight:
+    """Host (or device) tensors of one NVFP4 matrix [n, k]."""
+    codes: torch.Tensor   # uint8 [n, k/2]
+    scales: torch.Tensor  # uint8 [n, k/16] (E4M3 bit patterns)
+    ts: float = 1.0
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.codes.shape[1] * 2)
+
+    def to(self, device) -> "NvWeight":
+        return NvWeight(self.codes.to(device), self.scales.to(device), self.ts)
+
+
+def activations(m: int, k: int, seed: int = 0, outliers: bool = False,
+                stream: int = _X) -> torch.Tensor:
+    """bf16 [m, k], N(0,1); with outliers, each entry x20 with p = 0.01."""
+    x = torch.randn((m, k), generator=_gen(seed, stream), dtype=torch.float32)
+    if outliers:
+        mask = torch.rand((m, k), generator=_gen(seed, _OUTLIER)) < 0.01
+        x = torch.where(mask, x * 20.0, x)
+    return x.to(torch.bfloat16)
+
+
+def weight(n: int, k: int, seed: int, code_stream: int, scale_stream: int,
+           ts: float = 1.0) -> NvWeight:
+    assert k % 32 == 0
+    codes = torch.randint(0, 256, (n, k // 2), generator=_gen(seed, code_stream),
+                          dtype=torch.uint8)
+    u = torch.rand((n, k // 16), generator=_gen(seed, scale_stream),
+                   dtype=torch.float32) * -4.0
+    scales = torch.exp2(u).to(torch.float8_e4m3fn).view(torch.uint8)
+    return NvWeight(codes, scales.contiguous(), ts)
+
+
+def ffn_weights(hidden: int, inter: int, seed: int = 0):
+    wg = weight(inter, hidden, seed, _WG_C, _WG_S)
+    wu = weight(inter, hidden, seed, _WU_C, _WU_S)
+    wd = weight(hidden, inter, seed, _WD_C, _WD_S)
+    return wg, wu, wd
+
+
+def workload(name: str, seed: int = 0, m: int | None = None):
+    """(x bf16 [m, hidden], wg, wu, wd) on the CPU."""
+    spec = WORKLOADS[name]
+    rows = spec["m"] if m is None else m
+    x = activations(rows, spec["hidden"], seed, spec["outliers"])
+    return (x,) + ffn_weights(spec["hidden"], spec["inter"], seed)
+
+
+def exact_case(m: int, n: int, k: int, seed: int = 0):
+    """Inputs on which every fp32 partial sum is exact: X integer in [-2, 2],
+    block scales powers of two in [2^-4, 1], tensor scale 1.  Any summation
+    order then gives the same fp32 value."""
+    x = torch.randint(-2, 3, (m, k), generator=_gen(seed, 100)).to(torch.bfloat16)
+    codes = torch.randint(0, 256, (n, k // 2), generator=_gen(seed, 101),
+                          dtype=torch.uint8)
+    e = torch.randint(-4, 1, (n, k // 16), generator=_gen(seed, 102)).to(torch.float32)
+    scales = torch.exp2(e).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return x, NvWeight(codes, scales, 1.0)
