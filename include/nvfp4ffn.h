@@ -1,0 +1,143 @@
+/*
+ * nvfp4ffn.h -- C ABI of the MI355X (gfx950) dense SwiGLU FFN with NVFP4
+ * weights.
+ *
+ * The FFN is the one on the pages (rustdoc source of the crate
+ * metrale_model_layers): page layers/dense_ffn_fixed.rs,
+ * `DenseFfnLayer::forward_fixed`, and page layers/dense_ffn_prefill.rs,
+ * `forward_prefill_inner` / `w4a16_prefill_gemm`:
+ *
+ *     gate = X . Wg^T        [m, inter]   (projection with n = inter, k = hidden)
+ *     up   = X . Wu^T        [m, inter]
+ *     act  = silu(gate) * up [m, inter]   (`ops::silu_mul`, written over gate)
+ *     Y    = act . Wd^T      [m, hidden]  (projection with n = hidden, k = inter)
+ *
+ * NVFP4 (not defined on the pages; the standard format): each weight
+ * element is an E2M1 code, each run of 16 consecutive elements along K
+ * shares one E4M3 ("FN": max 448, no inf) scale, and the tensor has one
+ * fp32 scale:  W[r][k] = e2m1(code[r][k]) * e4m3(scale[r][k/16]) * ts.
+ *
+ * Common rules for every entry point
+ * ----------------------------------
+ * Memory: every array argument is a DEVICE pointer on the current HIP
+ *   device, caller-owned, contiguous row-major and 16-byte aligned.  The
+ *   library never frees or keeps a caller pointer past the stream work the
+ *   call enqueues.  Weights are only read.
+ * bf16: activations and outputs are bf16 bit patterns (2 bytes each).
+ * Stream: `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   Work is enqueued asynchronously; nothing synchronizes unless
+ *   NVFP4_PROFILE=1 is set in the environment.
+ * Accumulation: fp32.  Intermediates (gate, up, act) are rounded to bf16,
+ *   round-to-nearest-even, like the bf16 buffers the pages pass between
+ *   the FFN's launches.
+ * Rows: only output rows 0..m-1 are written (page layers/dense_ffn_fixed.rs,
+ *   module invariants); m == 0 is a no-op returning NVFP4_OK.
+ * Errors: a negative status; every check runs before anything is enqueued,
+ *   so outputs are untouched on error.  nvfp4_last_error() returns the
+ *   calling thread's last message.
+ * Scratch: intermediates and split-K partials live in a per-device arena
+ *   owned by the library (grown on first use of a larger shape, freed by
+ *   nvfp4_release).  Calls that may run concurrently on different streams
+ *   of one device race on it; calls on one stream are ordered.
+ */
+#ifndef NVFP4FFN_H
+#define NVFP4FFN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define NVFP4_OK 0
+#define NVFP4_EINVAL (-1) /* null/misaligned pointer, negative m, bad count */
+#define NVFP4_ESHAPE (-2) /* n or k <= 0, k % 32 != 0, inconsistent shapes */
+#define NVFP4_ENOMEM (-3) /* the scratch arena could not grow */
+#define NVFP4_EHIP (-4)   /* a HIP launch or runtime call failed */
+
+/* One NVFP4 matrix W[n][k] (PyTorch Linear orientation: y = x . W^T).
+ *   codes : device, uint8 [n][k/2]; element 2j in the low nibble, 2j+1 in
+ *           the high nibble; nibble bits s e1 e0 m.
+ *   scales: device, uint8 [n][k/16]; E4M3FN bit patterns.
+ *   tensor_scale: fp32 multiplier applied to every element.
+ *   k must be a positive multiple of 32. */
+typedef struct nvfp4_weight {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  float tensor_scale;
+  int32_t n;
+  int32_t k;
+} nvfp4_weight;
+
+/* W4A16 projection: y[m][n] = bf16( sum_k x[m][k] * W[n][k] ).
+ * x: bf16 [m][k]; y: bf16 [m][n].  One NVFP4 projection GEMM of m rows
+ * (page layers/dense_ffn_prefill.rs, `w4a16_prefill_gemm`). */
+int nvfp4_gemm_w4a16(const void *x, int32_t m, const nvfp4_weight *w,
+                     void *y, void *stream);
+
+/* W4A4 projection: x is first quantized per row to NVFP4 (see
+ * nvfp4_quantize_rows), then y[r][c] = bf16( s_row[r] * ts *
+ * sum_k xq[r][k] * wq[c][k] ) with both operands' NVFP4 values exact.
+ * Row r's result bits are the same for every m (page
+ * layers/dense_ffn_fixed.rs, module doc and `Fixed::W4a4`:
+ * `ops::w4a4_proj::nvfp4_proj_mx`, which takes a bf16 input). */
+int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w,
+                    void *y, void *stream);
+
+/* Per-row NVFP4 activation quantizer (the activation half of the W4A4
+ * projection).  x: bf16 [m][k], k % 32 == 0.  Outputs: codes uint8
+ * [m][k/2] (packing as in nvfp4_weight), scales uint8 [m][k/16] (E4M3FN),
+ * row_scale fp32 [m].  Per row, in fp32 with IEEE rounding:
+ *   s_row = amax/2688 (1 for an all-zero row);
+ *   per 16-block: scale = E4M3(amax_block / (6*s_row)), nearest-even,
+ *                 saturating at 448;
+ *   code = E2M1(x / (e4m3(scale)*s_row)), nearest with ties to the even
+ *          code, saturating at 6; zero elements and elements of a
+ *          zero-scale block keep only their sign.
+ * Depends on nothing outside its row. */
+int nvfp4_quantize_rows(const void *x, int32_t m, int32_t k, uint8_t *codes,
+                        uint8_t *scales, float *row_scale, void *stream);
+
+/* out[e] = bf16( silu(gate[e]) * up[e] ), silu(t) = t / (1 + exp(-t)),
+ * computed in fp32 for e < count.  out may equal gate (every caller on the
+ * pages writes over gate: page layers/dense_ffn_fixed.rs, `forward_fixed`,
+ * `ops::silu_mul`). */
+int silu_mul(const void *gate, const void *up, void *out, int64_t count,
+             void *stream);
+
+/* act[m][inter] = bf16( silu(bf16(x.Wg^T)) * bf16(x.Wu^T) ): gate, up and
+ * silu_mul in one pass over both weights.  wg, wu: [inter][hidden]. */
+int nvfp4_gate_up_silu_w4a16(const void *x, int32_t m, const nvfp4_weight *wg,
+                             const nvfp4_weight *wu, void *act, void *stream);
+
+/* Dense SwiGLU FFN, W4A16: out[m][hidden] = down(silu(gate(x)) * up(x)).
+ * x: bf16 [m][hidden]; wg, wu: [inter][hidden]; wd: [hidden][inter]
+ * (page layers/dense_ffn_prefill.rs, `forward_prefill_inner`, NVFP4 leg;
+ * page layers/dense_ffn_fixed.rs, `forward_fixed` for the step order). */
+int dense_ffn_forward(const void *x, int32_t m, int32_t hidden, int32_t inter,
+                      const nvfp4_weight *wg, const nvfp4_weight *wu,
+                      const nvfp4_weight *wd, void *out, void *stream);
+
+/* Dense SwiGLU FFN, fixed-format W4A4: x and act are quantized per row to
+ * NVFP4 before each projection; row r's output bits do not depend on m
+ * (page layers/dense_ffn_fixed.rs, `forward_fixed`, W4A4 arm). */
+int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden,
+                           int32_t inter, const nvfp4_weight *wg,
+                           const nvfp4_weight *wu, const nvfp4_weight *wd,
+                           void *out, void *stream);
+
+/* The calling thread's last error message ("" if none). */
+const char *nvfp4_last_error(void);
+
+/* Frees the scratch arena of every device.  The caller must have
+ * synchronized all streams that used the library. */
+void nvfp4_release(void);
+
+/* ABI version of this header (bumped on incompatible change). */
+int32_t nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4FFN_H */

@@ -1,0 +1,239 @@
+"""Python binding of ``libnvfp4ffn.so``, the MI355X (gfx950) dense SwiGLU FFN
+with NVFP4 weights.
+
+Argument marshalling only: every step of the FFN runs in the library's HIP
+kernels; PyTorch supplies device memory and the current stream.  The names
+and argument order follow the C ABI in ``include/nvfp4ffn.h``.  There is no
+CPU fallback: if the library is not built, importing works but every call
+raises :class:`Nvfp4LibraryMissing`.
+
+Tensors: activations are ``torch.bfloat16`` ``[rows, cols]`` contiguous on
+the GPU; a weight is any object with ``codes`` (uint8 ``[n, k/2]``),
+``scales`` (uint8 ``[n, k/16]``, E4M3 bits) and ``tensor_scale`` (or
+``ts``) -- see :class:`NVFP4Weight`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4ffn.so")
+
+NVFP4_OK = 0
+NVFP4_EINVAL = -1
+NVFP4_ESHAPE = -2
+NVFP4_ENOMEM = -3
+NVFP4_EHIP = -4
+
+__all__ = [
+    "NVFP4Weight", "Nvfp4Error", "Nvfp4LibraryMissing",
+    "nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "nvfp4_quantize_rows", "silu_mul",
+    "nvfp4_gate_up_silu_w4a16", "dense_ffn_forward", "dense_ffn_forward_w4a4",
+    "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
+]
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"nvfp4ffn error {code}: {message}")
+        self.code = code
+
+
+class Nvfp4LibraryMissing(RuntimeError):
+    pass
+
+
+class _CWeight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("tensor_scale", ctypes.c_float),
+        ("n", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+    ]
+
+
+@dataclass
+class NVFP4Weight:
+    """One NVFP4 matrix W[n][k] on the GPU."""
+    codes: torch.Tensor    # uint8 [n, k/2], even k in the low nibble
+    scales: torch.Tensor   # uint8 [n, k/16], E4M3FN bit patterns
+    tensor_scale: float = 1.0
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the C-ABI library and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise Nvfp4LibraryMissing(
+            f"{path} is not built; run `python -m nvfp4_weight_dense_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    wp = ctypes.POINTER(_CWeight)
+    sig = {
+        "nvfp4_gemm_w4a16": [vp, i32, wp, vp, vp],
+        "nvfp4_gemm_w4a4": [vp, i32, wp, vp, vp],
+        "nvfp4_quantize_rows": [vp, i32, i32, vp, vp, vp, vp],
+        "silu_mul": [vp, vp, vp, i64, vp],
+        "nvfp4_gate_up_silu_w4a16": [vp, i32, wp, wp, vp, vp],
+        "dense_ffn_forward": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
+        "dense_ffn_forward_w4a4": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.nvfp4_last_error.argtypes = []
+    L.nvfp4_last_error.restype = ctypes.c_char_p
+    L.nvfp4_release.argtypes = []
+    L.nvfp4_release.restype = None
+    L.nvfp4_abi_version.argtypes = []
+    L.nvfp4_abi_version.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+# ---- marshalling helpers -------------------------------------------------------
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(rc: int):
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, nvfp4_last_error())
+
+
+def _act(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous 2-D bfloat16 tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    return t
+
+
+def _cweight(w) -> _CWeight:
+    codes, scales = w.codes, w.scales
+    ts = getattr(w, "tensor_scale", None)
+    if ts is None:
+        ts = w.ts
+    for t, nm in ((codes, "codes"), (scales, "scales")):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"weight {nm}: expected a contiguous uint8 GPU tensor")
+    n, half_k = codes.shape
+    return _CWeight(codes.data_ptr(), scales.data_ptr(), float(ts), int(n), int(half_k * 2))
+
+
+# ---- C ABI, same names --------------------------------------------------------
+
+def nvfp4_abi_version() -> int:
+    return int(load_library().nvfp4_abi_version())
+
+
+def nvfp4_last_error() -> str:
+    return load_library().nvfp4_last_error().decode()
+
+
+def nvfp4_release() -> None:
+    load_library().nvfp4_release()
+
+
+def nvfp4_gemm_w4a16(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
+    """y = bf16(x . W^T); x [m, k] bf16 -> y [m, n] bf16."""
+    L = load_library()
+    x = _act(x, "x")
+    cw = _cweight(w)
+    if y is None:
+        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    _check(L.nvfp4_gemm_w4a16(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
+    return y
+
+
+def nvfp4_gemm_w4a4(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
+    """W4A4 projection: x quantized per row to NVFP4, then x_q . W^T."""
+    L = load_library()
+    x = _act(x, "x")
+    cw = _cweight(w)
+    if y is None:
+        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    _check(L.nvfp4_gemm_w4a4(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
+    return y
+
+
+def nvfp4_quantize_rows(x: torch.Tensor, stream=None):
+    """Per-row NVFP4 quantizer -> (codes [m, k/2], scales [m, k/16], row_scale [m])."""
+    L = load_library()
+    x = _act(x, "x")
+    m, k = x.shape
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
+    rs = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(L.nvfp4_quantize_rows(_ptr(x), m, k, _ptr(codes), _ptr(scales), _ptr(rs),
+                                 _stream(stream)))
+    return codes, scales, rs
+
+
+def silu_mul(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """out = bf16(silu(gate) * up); out may be gate."""
+    L = load_library()
+    if gate.shape != up.shape or gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
+        raise ValueError("silu_mul: gate and up must be bf16 tensors of one shape")
+    if not (gate.is_contiguous() and up.is_contiguous() and gate.is_cuda and up.is_cuda):
+        raise ValueError("silu_mul: expected contiguous GPU tensors")
+    if out is None:
+        out = torch.empty_like(gate)
+    _check(L.silu_mul(_ptr(gate), _ptr(up), _ptr(out), gate.numel(), _stream(stream)))
+    return out
+
+
+def nvfp4_gate_up_silu_w4a16(x: torch.Tensor, wg, wu, act: torch.Tensor | None = None,
+                             stream=None):
+    """act = bf16(silu(bf16(x.Wg^T)) * bf16(x.Wu^T))."""
+    L = load_library()
+    x = _act(x, "x")
+    cg, cu = _cweight(wg), _cweight(wu)
+    if act is None:
+        act = torch.empty((x.shape[0], cg.n), dtype=torch.bfloat16, device=x.device)
+    _check(L.nvfp4_gate_up_silu_w4a16(_ptr(x), x.shape[0], ctypes.byref(cg), ctypes.byref(cu),
+                                      _ptr(act), _stream(stream)))
+    return act
+
+
+def _ffn(fn, x, wg, wu, wd, out, stream):
+    x = _act(x, "x")
+    cg, cu, cd = _cweight(wg), _cweight(wu), _cweight(wd)
+    m, hidden = x.shape
+    inter = cg.n
+    if out is None:
+        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
+    _check(fn(_ptr(x), m, hidden, inter, ctypes.byref(cg), ctypes.byref(cu), ctypes.byref(cd),
+              _ptr(out), _stream(stream)))
+    return out
+
+
+def dense_ffn_forward(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None = None, stream=None):
+    """W4A16 dense SwiGLU FFN: out = (silu(x.Wg^T) * (x.Wu^T)) . Wd^T."""
+    return _ffn(load_library().dense_ffn_forward, x, wg, wu, wd, out, stream)
+
+
+def dense_ffn_forward_w4a4(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None = None,
+                           stream=None):
+    """Fixed-format W4A4 FFN (activations quantized per row before each projection)."""
+    return _ffn(load_library().dense_ffn_forward_w4a4, x, wg, wu, wd, out, stream)

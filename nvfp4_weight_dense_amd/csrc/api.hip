@@ -1,0 +1,411 @@
+// api.hip -- C ABI of the NVFP4 dense SwiGLU FFN library (declared in
+// include/nvfp4ffn.h): argument validation, per-m path choice, the scratch
+// arena, error strings and the optional profile/log lines.
+//
+// Call structure (page layers/dense_ffn_fixed.rs, `forward_fixed`; page
+// layers/dense_ffn_prefill.rs, `forward_prefill` / `w4a16_prefill_gemm`):
+//   W4A16: gate+up(+silu) -> act, then down -> out.  Up to NVFP4_SMALLM_MAX_M
+//          rows (default 64, the pages' small-m edge) take the weight-streaming
+//          kernel with gate, up and silu_mul fused; more rows take the tiled
+//          kernel, then silu_mul.
+//   W4A4:  quantize x -> gate+up(+silu) -> act -> quantize act -> down.  One
+//          kernel and one K order for every m, so row bits do not depend on m.
+// Every check runs before the first launch; a forced path that cannot serve a
+// shape is an error, never a silent fallback (the pages refuse to start with
+// a requested but missing variant: page layers/mod.rs, `w4a16_v2_kernel`).
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+#include <tuple>
+
+#include "launchers.h"
+#include "nvfp4_common.h"
+#include "nvfp4ffn.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+enum class Force { Auto, Stream, Tiled };
+
+struct Config {
+  int smallm_max_m = 64;
+  Force force = Force::Auto;
+  bool profile = false;
+  bool log = false;
+  size_t arena_cap = 0;  // 0: no cap
+};
+
+const Config &cfg() {
+  static Config c = [] {
+    Config c;
+    if (const char *v = getenv("NVFP4_SMALLM_MAX_M")) c.smallm_max_m = atoi(v);
+    if (const char *v = getenv("NVFP4_FORCE_PATH")) {
+      if (!strcmp(v, "stream")) c.force = Force::Stream;
+      if (!strcmp(v, "tiled")) c.force = Force::Tiled;
+    }
+    if (const char *v = getenv("NVFP4_PROFILE")) c.profile = !strcmp(v, "1");
+    if (const char *v = getenv("NVFP4_LOG")) c.log = !strcmp(v, "1");
+    if (const char *v = getenv("NVFP4_ARENA_MAX_BYTES")) c.arena_cap = strtoull(v, nullptr, 10);
+    return c;
+  }();
+  return c;
+}
+
+// ---- scratch arena: one grow-only device buffer per device -------------------
+
+constexpr int kMaxDevices = 64;
+struct Arena {
+  void *ptr = nullptr;
+  size_t size = 0;
+};
+std::mutex g_arena_mu;
+Arena g_arena[kMaxDevices];
+
+int arena_get(size_t bytes, void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  Arena &a = g_arena[dev];
+  if (a.size < bytes) {
+    size_t want = (bytes + (2u << 20) - 1) & ~(size_t)((2u << 20) - 1);
+    if (cfg().arena_cap && want > cfg().arena_cap)
+      return fail(NVFP4_ENOMEM, "scratch arena needs %zu bytes, above NVFP4_ARENA_MAX_BYTES=%zu",
+                  want, cfg().arena_cap);
+    if (a.ptr) {
+      // kernels still in flight may read the old buffer
+      if (hipDeviceSynchronize() != hipSuccess) return fail(NVFP4_EHIP, "hipDeviceSynchronize failed");
+      (void)hipFree(a.ptr);
+      a.ptr = nullptr;
+      a.size = 0;
+    }
+    if (hipMalloc(&a.ptr, want) != hipSuccess) {
+      a.ptr = nullptr;
+      (void)hipGetLastError();
+      return fail(NVFP4_ENOMEM, "scratch arena: hipMalloc of %zu bytes failed", want);
+    }
+    a.size = want;
+  }
+  *out = a.ptr;
+  return NVFP4_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// ---- validation ------------------------------------------------------------------
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+int check_weight(const nvfp4_weight *w, const char *name) {
+  if (!w) return fail(NVFP4_EINVAL, "%s: null weight descriptor", name);
+  if (!w->codes || !w->scales) return fail(NVFP4_EINVAL, "%s: null codes or scales pointer", name);
+  if (w->n <= 0 || w->k <= 0) return fail(NVFP4_ESHAPE, "%s: n=%d k=%d must be positive", name, w->n, w->k);
+  if (w->k % 32 != 0) return fail(NVFP4_ESHAPE, "%s: k=%d is not a multiple of 32", name, w->k);
+  if (misaligned(w->codes) || misaligned(w->scales))
+    return fail(NVFP4_EINVAL, "%s: codes/scales must be 16-byte aligned", name);
+  return NVFP4_OK;
+}
+
+int check_act(const void *x, int m, const char *name) {
+  if (m < 0) return fail(NVFP4_EINVAL, "%s: m=%d is negative", name, m);
+  if (m > 0 && !x) return fail(NVFP4_EINVAL, "%s: null pointer", name);
+  if (m > 0 && misaligned(x)) return fail(NVFP4_EINVAL, "%s: must be 16-byte aligned", name);
+  if (m > 4194240) return fail(NVFP4_ESHAPE, "%s: m=%d exceeds 4194240 rows", name, m);
+  return NVFP4_OK;
+}
+
+MatRef mat(const nvfp4_weight *w) { return MatRef{w->codes, w->scales, w->tensor_scale}; }
+
+bool use_stream(int m) {
+  switch (cfg().force) {
+    case Force::Stream: return true;
+    case Force::Tiled: return false;
+    default: return m <= cfg().smallm_max_m;
+  }
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return NVFP4_OK;
+  return fail(NVFP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void log_path(const char *entry, const char *path, int m, int n, int k) {
+  if (!cfg().log) return;
+  static std::mutex mu;
+  static std::set<std::tuple<std::string, int, int, int>> seen;
+  std::lock_guard<std::mutex> lk(mu);
+  if (seen.insert({std::string(entry) + path, m, n, k}).second)
+    fprintf(stderr, "[nvfp4ffn] %s m=%d n=%d k=%d -> %s\n", entry, m, n, k, path);
+}
+
+struct ProfileScope {
+  const char *what;
+  int m;
+  hipStream_t s;
+  std::chrono::steady_clock::time_point t0;
+  bool on;
+  ProfileScope(const char *w, int m_, hipStream_t s_) : what(w), m(m_), s(s_), on(cfg().profile) {
+    if (on) {
+      (void)hipStreamSynchronize(s);
+      t0 = std::chrono::steady_clock::now();
+    }
+  }
+  ~ProfileScope() {
+    if (!on) return;
+    (void)hipStreamSynchronize(s);
+    auto us = std::chrono::duration_cast<std::chrono::microseconds>(
+                  std::chrono::steady_clock::now() - t0).count();
+    fprintf(stderr, "FFN [%s] m=%d: %lldus\n", what, m, (long long)us);
+  }
+};
+
+// ---- projections with caller-provided scratch ----------------------------------------
+
+// scratch bytes a W4A16 projection (nmat 1) or gate+up+silu (nmat 2) needs
+size_t proj_scratch_bytes(int m, int n, int k, int nmat, bool stream_path) {
+  if (stream_path) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+  return nmat == 2 ? 2 * align256((size_t)2 * m * n) : 0;
+}
+
+int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, void *y,
+             void *scratch, bool stream_path, hipStream_t s) {
+  if (stream_path) {
+    StreamPlan pl = stream_plan(n, k);
+    return hip_status(launch_stream(a, m, k, n, nmat, w, y, (float *)scratch, pl, s),
+                      "weight-streaming projection launch");
+  }
+  if (nmat == 1) return hip_status(launch_tiled(a.x_bf16, m, k, n, w[0], y, s), "tiled projection launch");
+  char *g = (char *)scratch;
+  char *u = g + align256((size_t)2 * m * n);
+  int rc = hip_status(launch_tiled(a.x_bf16, m, k, n, w[0], g, s), "tiled gate launch");
+  if (rc) return rc;
+  rc = hip_status(launch_tiled(a.x_bf16, m, k, n, w[1], u, s), "tiled up launch");
+  if (rc) return rc;
+  return hip_status(launch_silu_mul(g, u, y, (int64_t)m * n, s), "silu_mul launch");
+}
+
+int check_ffn(const void *x, int m, int hidden, int inter, const nvfp4_weight *wg,
+              const nvfp4_weight *wu, const nvfp4_weight *wd, const void *out) {
+  int rc;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(out, m, "out"))) return rc;
+  if (hidden <= 0 || inter <= 0)
+    return fail(NVFP4_ESHAPE, "hidden=%d inter=%d must be positive", hidden, inter);
+  if ((rc = check_weight(wg, "wg")) || (rc = check_weight(wu, "wu")) || (rc = check_weight(wd, "wd")))
+    return rc;
+  if (wg->n != inter || wg->k != hidden || wu->n != inter || wu->k != hidden)
+    return fail(NVFP4_ESHAPE, "wg/wu must be [inter=%d][hidden=%d], got [%d][%d] and [%d][%d]",
+                inter, hidden, wg->n, wg->k, wu->n, wu->k);
+  if (wd->n != hidden || wd->k != inter)
+    return fail(NVFP4_ESHAPE, "wd must be [hidden=%d][inter=%d], got [%d][%d]", hidden, inter,
+                wd->n, wd->k);
+  return NVFP4_OK;
+}
+
+struct QuantBuf {
+  uint8_t *codes;
+  uint8_t *scales;
+  float *rs;
+  size_t bytes;
+};
+
+QuantBuf quant_layout(char *base, int m, int k) {
+  QuantBuf q;
+  size_t c = align256((size_t)m * k / 2), s = align256((size_t)m * k / 16), r = align256((size_t)m * 4);
+  q.codes = (uint8_t *)base;
+  q.scales = base ? (uint8_t *)(base + c) : nullptr;
+  q.rs = base ? (float *)(base + c + s) : nullptr;
+  q.bytes = c + s + r;
+  return q;
+}
+
+}  // namespace
+
+// ---- C ABI ---------------------------------------------------------------------------
+
+extern "C" {
+
+int32_t nvfp4_abi_version(void) { return 1; }
+
+const char *nvfp4_last_error(void) { return g_err.c_str(); }
+
+void nvfp4_release(void) {
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (int d = 0; d < kMaxDevices; ++d) {
+    if (!g_arena[d].ptr) continue;
+    (void)hipSetDevice(d);
+    (void)hipFree(g_arena[d].ptr);
+    g_arena[d].ptr = nullptr;
+    g_arena[d].size = 0;
+  }
+  (void)hipSetDevice(cur);
+}
+
+int silu_mul(const void *gate, const void *up, void *out, int64_t count, void *stream) {
+  g_err.clear();
+  if (count < 0) return fail(NVFP4_EINVAL, "silu_mul: count=%lld is negative", (long long)count);
+  if (count == 0) return NVFP4_OK;
+  if (!gate || !up || !out) return fail(NVFP4_EINVAL, "silu_mul: null pointer");
+  if (misaligned(gate) || misaligned(up) || misaligned(out))
+    return fail(NVFP4_EINVAL, "silu_mul: pointers must be 16-byte aligned");
+  return hip_status(launch_silu_mul(gate, up, out, count, (hipStream_t)stream), "silu_mul launch");
+}
+
+int nvfp4_quantize_rows(const void *x, int32_t m, int32_t k, uint8_t *codes, uint8_t *scales,
+                        float *row_scale, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_act(x, m, "x"))) return rc;
+  if (k <= 0 || k % 32 != 0) return fail(NVFP4_ESHAPE, "quantize_rows: k=%d must be a positive multiple of 32", k);
+  if (m == 0) return NVFP4_OK;
+  if (!codes || !scales || !row_scale) return fail(NVFP4_EINVAL, "quantize_rows: null output pointer");
+  if (misaligned(codes) || ((uintptr_t)row_scale & 3u))
+    return fail(NVFP4_EINVAL, "quantize_rows: codes must be 16-byte and row_scale 4-byte aligned");
+  return hip_status(launch_quantize_rows(x, m, k, codes, scales, row_scale, (hipStream_t)stream),
+                    "quantize_rows launch");
+}
+
+int nvfp4_gemm_w4a16(const void *x, int32_t m, const nvfp4_weight *w, void *y, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(y, m, "y")) || (rc = check_weight(w, "w")))
+    return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const bool st = use_stream(m);
+  log_path("gemm_w4a16", st ? "stream" : "tiled", m, w->n, w->k);
+  void *scr = nullptr;
+  size_t need = proj_scratch_bytes(m, w->n, w->k, 1, st);
+  if (need && (rc = arena_get(need, &scr))) return rc;
+  ProfileScope ps("gemm_w4a16", m, s);
+  MatRef wm = mat(w);
+  return run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, w->k, w->n, 1, &wm, y, scr, st, s);
+}
+
+int nvfp4_gate_up_silu_w4a16(const void *x, int32_t m, const nvfp4_weight *wg,
+                             const nvfp4_weight *wu, void *act, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(act, m, "act")) ||
+      (rc = check_weight(wg, "wg")) || (rc = check_weight(wu, "wu")))
+    return rc;
+  if (wg->n != wu->n || wg->k != wu->k)
+    return fail(NVFP4_ESHAPE, "wg [%d][%d] and wu [%d][%d] differ", wg->n, wg->k, wu->n, wu->k);
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const bool st = use_stream(m);
+  log_path("gate_up_silu_w4a16", st ? "stream" : "tiled", m, wg->n, wg->k);
+  void *scr = nullptr;
+  size_t need = proj_scratch_bytes(m, wg->n, wg->k, 2, st);
+  if (need && (rc = arena_get(need, &scr))) return rc;
+  ProfileScope ps("gate_up_silu_w4a16", m, s);
+  MatRef w2[2] = {mat(wg), mat(wu)};
+  return run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, wg->k, wg->n, 2, w2, act, scr, st, s);
+}
+
+int dense_ffn_forward(const void *x, int32_t m, int32_t hidden, int32_t inter,
+                      const nvfp4_weight *wg, const nvfp4_weight *wu, const nvfp4_weight *wd,
+                      void *out, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_ffn(x, m, hidden, inter, wg, wu, wd, out))) return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const bool st = use_stream(m);
+  log_path("dense_ffn_forward", st ? "stream" : "tiled", m, inter, hidden);
+  const size_t act_b = align256((size_t)2 * m * inter);
+  size_t scr_b = proj_scratch_bytes(m, inter, hidden, 2, st);
+  size_t down_b = proj_scratch_bytes(m, hidden, inter, 1, st);
+  if (down_b > scr_b) scr_b = down_b;
+  void *base = nullptr;
+  if ((rc = arena_get(act_b + scr_b, &base))) return rc;
+  char *act = (char *)base;
+  char *scr = act + act_b;
+  ProfileScope ps(st ? "dense_total stream" : "dense_total tiled", m, s);
+  MatRef w2[2] = {mat(wg), mat(wu)};
+  MatRef wdm = mat(wd);
+  if ((rc = run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, hidden, inter, 2, w2, act, scr, st, s)))
+    return rc;
+  return run_proj(ActRef{act, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &wdm, out, scr, st, s);
+}
+
+int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(y, m, "y")) || (rc = check_weight(w, "w")))
+    return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  log_path("gemm_w4a4", "stream", m, w->n, w->k);
+  QuantBuf q = quant_layout(nullptr, m, w->k);
+  size_t part = proj_scratch_bytes(m, w->n, w->k, 1, true);
+  void *base = nullptr;
+  if ((rc = arena_get(q.bytes + part, &base))) return rc;
+  q = quant_layout((char *)base, m, w->k);
+  ProfileScope ps("gemm_w4a4", m, s);
+  if ((rc = hip_status(launch_quantize_rows(x, m, w->k, q.codes, q.scales, q.rs, s), "quantize launch")))
+    return rc;
+  MatRef wm = mat(w);
+  return run_proj(ActRef{nullptr, q.codes, q.scales, q.rs}, m, w->k, w->n, 1, &wm, y,
+                  (char *)base + q.bytes, true, s);
+}
+
+int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden, int32_t inter,
+                           const nvfp4_weight *wg, const nvfp4_weight *wu, const nvfp4_weight *wd,
+                           void *out, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_ffn(x, m, hidden, inter, wg, wu, wd, out))) return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  log_path("dense_ffn_forward_w4a4", "stream", m, inter, hidden);
+  QuantBuf qx = quant_layout(nullptr, m, hidden);
+  QuantBuf qa = quant_layout(nullptr, m, inter);
+  const size_t act_b = align256((size_t)2 * m * inter);
+  size_t part = proj_scratch_bytes(m, inter, hidden, 2, true);
+  size_t part_d = proj_scratch_bytes(m, hidden, inter, 1, true);
+  if (part_d > part) part = part_d;
+  void *base = nullptr;
+  if ((rc = arena_get(qx.bytes + qa.bytes + act_b + part, &base))) return rc;
+  char *p = (char *)base;
+  qx = quant_layout(p, m, hidden);
+  qa = quant_layout(p + qx.bytes, m, inter);
+  char *act = p + qx.bytes + qa.bytes;
+  char *scr = act + act_b;
+  ProfileScope ps("dense_total w4a4", m, s);
+  MatRef w2[2] = {mat(wg), mat(wu)};
+  MatRef wdm = mat(wd);
+  if ((rc = hip_status(launch_quantize_rows(x, m, hidden, qx.codes, qx.scales, qx.rs, s),
+                       "quantize launch")))
+    return rc;
+  if ((rc = run_proj(ActRef{nullptr, qx.codes, qx.scales, qx.rs}, m, hidden, inter, 2, w2, act, scr,
+                     true, s)))
+    return rc;
+  if ((rc = hip_status(launch_quantize_rows(act, m, inter, qa.codes, qa.scales, qa.rs, s),
+                       "quantize launch")))
+    return rc;
+  return run_proj(ActRef{nullptr, qa.codes, qa.scales, qa.rs}, m, inter, hidden, 1, &wdm, out, scr,
+                  true, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+// k_elementwise.hip -- silu_mul and the per-row NVFP4 activation quantizer
+// (gfx950).  Both are HBM-bound passes over bf16 rows.
+#include "launchers.h"
+#include "nvfp4_common.h"
+
+// The quantizer's codes must equal the CPU definition bit for bit: every
+// float operation below is one IEEE fp32 operation in the written order
+// (no FMA contraction; fp32 division is correctly rounded in this build).
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+
+namespace {
+
+// ---- silu_mul: out = bf16(silu(gate) * up), page layers/dense_ffn_fixed.rs,
+// `forward_fixed` (`ops::silu_mul`, written over gate) ------------------------
+
+__global__ __launch_bounds__(256) void k_silu_mul(const uint16_t *__restrict__ g,
+                                                 const uint16_t *__restrict__ u,
+                                                 uint16_t *out, int64_t count) {
+  const int64_t nvec = count >> 3;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
+    const uint4 gv = ((const uint4 *)g)[i];
+    const uint4 uv = ((const uint4 *)u)[i];
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t ow[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float g0 = bf16_bits_to_f32(gw[q] & 0xFFFFu), g1 = bf16_bits_to_f32(gw[q] >> 16);
+      float u0 = bf16_bits_to_f32(uw[q] & 0xFFFFu), u1 = bf16_bits_to_f32(uw[q] >> 16);
+      __bf16 o0 = (__bf16)(silu_f32(g0) * u0);
+      __bf16 o1 = (__bf16)(silu_f32(g1) * u1);
+      ow[q] = (uint32_t)__builtin_bit_cast(uint16_t, o0) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+    }
+    ((uint4 *)out)[i] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+  for (int64_t i = nvec * 8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += stride) {
+    float gv = bf16_bits_to_f32(g[i]), uv = bf16_bits_to_f32(u[i]);
+    out[i] = __builtin_bit_cast(uint16_t, (__bf16)(silu_f32(gv) * uv));
+  }
+}
+
+// ---- per-row NVFP4 quantizer ---------------------------------------------------
+
+// fp32 (>= 0, finite or +inf) -> E4M3FN byte, nearest-even, saturating.
+// Below 2^-6 the grid is m * 2^-9: scale by 2^9 (exact) and round to an
+// integer.  Above, round the fp32 mantissa to 3 bits (adding half an ulp of
+// the target minus one, plus the kept LSB, gives ties-to-even), then move
+// the fields (exponent bias 127 -> 7).
+__device__ __forceinline__ uint32_t e4m3_encode_sat(float t) {
+  const float a = fabsf(t);
+  if (!(a < 448.0f)) return 0x7Eu;
+  uint32_t v = __float_as_uint(a);
+  if (v < 0x3C800000u) return (uint32_t)rintf(a * 512.0f);  // 2^-6
+  v = v + 0x7FFFFu + ((v >> 20) & 1u);
+  v &= 0xFFF00000u;
+  return (((v >> 23) - 120u) << 3) | ((v >> 20) & 7u);
+}
+
+// fp32 -> E2M1 code, nearest with ties to the even code, saturating at 6,
+// sign kept.  The grid spacing is 0.5 on [0,2), 1 on [2,4), 2 on [4,6]; in
+// each interval the code parity equals the parity of the scaled integer.
+__device__ __forceinline__ uint32_t e2m1_encode_sat(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 31) << 3;
+  const float a = fabsf(q);
+  uint32_t mag;
+  if (!(a < 6.0f))
+    mag = 7u;
+  else if (a < 2.0f)
+    mag = (uint32_t)rintf(a * 2.0f);
+  else if (a < 4.0f)
+    mag = (uint32_t)rintf(a) + 2u;
+  else
+    mag = (uint32_t)rintf(a * 0.5f) + 4u;
+  return sign | mag;
+}
+
+// One workgroup per row; k % 32 == 0.
+__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restrict__ x, int k,
+                                                      uint8_t *__restrict__ codes,
+                                                      uint8_t *__restrict__ scales,
+                                                      float *__restrict__ row_scale) {
+  const int r = blockIdx.x;
+  const uint16_t *xr = x + (size_t)r * k;
+  const uint4 *xv4 = (const uint4 *)xr;
+
+  float amax = 0.0f;
+  for (int c = threadIdx.x; c < (k >> 3); c += 256) {
+    const uint4 v = xv4[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+  float s_row = amax / 2688.0f;
+  if (amax == 0.0f) s_row = 1.0f;
+  if (threadIdx.x == 0) row_scale[r] = s_row;
+
+  for (int b = threadIdx.x; b < (k >> 4); b += 256) {
+    const uint4 v0 = xv4[2 * b], v1 = xv4[2 * b + 1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float xv[16];
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      xv[2 * q] = bf16_bits_to_f32(w[q] & 0xFFFFu);
+      xv[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+      amax_b = fmaxf(amax_b, fabsf(xv[2 * q]));
+      amax_b = fmaxf(amax_b, fabsf(xv[2 * q + 1]));
+    }
+    const float d = 6.0f * s_row;
+    const float t = amax_b / d;
+    const uint32_t sb = e4m3_encode_sat(t);
+    const float v = e4m3_to_f32(sb);
+    const float den = v * s_row;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t code;
+      if (xv[i] == 0.0f || v == 0.0f)
+        code = (__float_as_uint(xv[i]) >> 31) << 3;
+      else
+        code = e2m1_encode_sat(xv[i] / den);
+      packed[i >> 3] |= code << (4 * (i & 7));
+    }
+    *(uint2 *)(codes + (size_t)r * (k >> 1) + 8 * b) = make_uint2(packed[0], packed[1]);
+    scales[(size_t)r * (k >> 4) + b] = (uint8_t)sb;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_silu_mul(const void *gate, const void *up, void *out, int64_t count,
+                           hipStream_t stream) {
+  int64_t nvec = (count + 7) / 8;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_silu_mul, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint16_t *)gate, (const uint16_t *)up, (uint16_t *)out, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const void *x, int m, int k, uint8_t *codes, uint8_t *scales,
+                                float *row_scale, hipStream_t stream) {
+  hipLaunchKernelGGL(k_quantize_rows, dim3(m), dim3(256), 0, stream, (const uint16_t *)x, k,
+                     codes, scales, row_scale);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,112 @@
+"""The C-ABI library loads and exports every function include/nvfp4ffn.h
+declares; host-side argument checks reject bad calls before any launch.
+CPU only: no call here reaches the GPU (every call fails validation or has
+m == 0 / count == 0)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_weight_dense_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4ffn.h")
+
+
+def _lib():
+    if not os.path.exists(nv.LIB_PATH):
+        from nvfp4_weight_dense_amd import build
+        build.build()
+    return nv.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    for want in ["nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "silu_mul", "dense_ffn_forward",
+                 "dense_ffn_forward_w4a4", "nvfp4_quantize_rows", "nvfp4_gate_up_silu_w4a16",
+                 "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert nv.nvfp4_abi_version() == 1
+
+
+def _w(n=64, k=64, codes=0x10000, scales=0x20000):
+    return nv._CWeight(codes, scales, 1.0, n, k)
+
+
+def test_validation_rejects_bad_arguments_without_launching():
+    L = _lib()
+    x = ctypes.c_void_p(0x40000)
+    y = ctypes.c_void_p(0x80000)
+    s = ctypes.c_void_p(None)
+    # null weight descriptor / pointers
+    assert L.nvfp4_gemm_w4a16(x, 4, None, y, s) == nv.NVFP4_EINVAL
+    assert "null weight descriptor" in nv.nvfp4_last_error()
+    w = _w(codes=0)
+    assert L.nvfp4_gemm_w4a16(x, 4, ctypes.byref(w), y, s) == nv.NVFP4_EINVAL
+    # k not a multiple of 32
+    w = _w(k=48)
+    assert L.nvfp4_gemm_w4a16(x, 4, ctypes.byref(w), y, s) == nv.NVFP4_ESHAPE
+    assert "multiple of 32" in nv.nvfp4_last_error()
+    # n <= 0
+    w = _w(n=0)
+    assert L.nvfp4_gemm_w4a4(x, 4, ctypes.byref(w), y, s) == nv.NVFP4_ESHAPE
+    # misaligned activation
+    w = _w()
+    assert L.nvfp4_gemm_w4a16(ctypes.c_void_p(0x40002), 4, ctypes.byref(w), y, s) == nv.NVFP4_EINVAL
+    # negative m
+    assert L.nvfp4_gemm_w4a16(x, -1, ctypes.byref(w), y, s) == nv.NVFP4_EINVAL
+    # m == 0 is a no-op that succeeds
+    assert L.nvfp4_gemm_w4a16(x, 0, ctypes.byref(w), y, s) == nv.NVFP4_OK
+    assert L.nvfp4_gemm_w4a4(x, 0, ctypes.byref(w), y, s) == nv.NVFP4_OK
+    # silu_mul
+    assert L.silu_mul(x, None, y, 16, s) == nv.NVFP4_EINVAL
+    assert L.silu_mul(x, x, y, -1, s) == nv.NVFP4_EINVAL
+    assert L.silu_mul(x, x, y, 0, s) == nv.NVFP4_OK
+    # quantizer
+    assert L.nvfp4_quantize_rows(x, 2, 40, y, y, y, s) == nv.NVFP4_ESHAPE
+    assert L.nvfp4_quantize_rows(x, 0, 64, y, y, y, s) == nv.NVFP4_OK
+
+
+def test_ffn_shape_consistency_checks():
+    L = _lib()
+    x = ctypes.c_void_p(0x40000)
+    out = ctypes.c_void_p(0x80000)
+    s = ctypes.c_void_p(None)
+    hidden, inter = 64, 96
+    wg, wu, wd = _w(inter, hidden), _w(inter, hidden), _w(hidden, inter)
+    args = lambda g, u, d: (x, 2, hidden, inter, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), out, s)
+    for fn in (L.dense_ffn_forward, L.dense_ffn_forward_w4a4):
+        assert fn(*args(wg, wu, _w(inter, hidden))) == nv.NVFP4_ESHAPE   # wd transposed
+        assert "wd must be" in nv.nvfp4_last_error()
+        assert fn(*args(_w(inter, 32), wu, wd)) == nv.NVFP4_ESHAPE        # wg k != hidden
+        assert fn(x, 0, hidden, inter, ctypes.byref(wg), ctypes.byref(wu), ctypes.byref(wd),
+                  out, s) == nv.NVFP4_OK
+        assert fn(x, 2, 0, inter, ctypes.byref(wg), ctypes.byref(wu), ctypes.byref(wd),
+                  out, s) == nv.NVFP4_ESHAPE
+    assert L.nvfp4_gate_up_silu_w4a16(x, 2, ctypes.byref(wg), ctypes.byref(_w(inter, 32)), out, s) \
+        == nv.NVFP4_ESHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    _lib()
+    x = torch.zeros((2, 64), dtype=torch.bfloat16)
+    w = nv.NVFP4Weight(torch.zeros((8, 32), dtype=torch.uint8), torch.zeros((8, 4), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        nv.nvfp4_gemm_w4a16(x, w)

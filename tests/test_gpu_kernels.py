@@ -1,0 +1,212 @@
+"""GPU parity of the individual C-ABI entry points against the oracle.
+
+Float outputs: max |gpu - oracle_exact| <= 2e-2 * rms(oracle_exact).
+Integer/byte outputs (quantizer codes, scales) and the exact-arithmetic
+projection: bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_weight_dense_amd as nv
+import oracle
+import synthetic_inputs as si
+from gpu_helpers import assert_close, bf16_f64, bits, from_bits, g_weight, o_weight, sync
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---- dequantization of every code byte and every finite scale byte ---------------
+
+def _all_bytes_weight():
+    # 256 weight rows of k = 32: row c holds code bytes 16c..16c+15 (mod 256)
+    # and scale bytes 2c, 2c+1; the two NaN scale bytes are replaced.
+    n, k = 256, 32
+    codes = (np.arange(n * 16).reshape(n, 16) % 256).astype(np.uint8)
+    scales = (np.arange(n * 2).reshape(n, 2) % 256).astype(np.uint8)
+    scales[scales == 0x7F] = 0x7E
+    scales[scales == 0xFF] = 0xFE
+    return si.NvWeight(torch.from_numpy(codes), torch.from_numpy(scales), 1.0)
+
+
+@pytest.mark.parametrize("m", [32, 96])  # 32: streaming kernel, 96: tiled kernel
+def test_dequant_every_code_and_scale_exact(m):
+    _say(f"dequant identity m={m}")
+    w = _all_bytes_weight()
+    x = torch.zeros((m, 32), dtype=torch.bfloat16)
+    x[:32, :32] = torch.eye(32)
+    y = nv.nvfp4_gemm_w4a16(x.cuda(), g_weight(w))
+    sync()
+    dense = oracle.dequant(o_weight(w))                  # [256, 32] doubles
+    expect = oracle.bf16_from_double_array(dense.T)      # exact in bf16
+    got = bits(y)
+    assert np.array_equal(got[:32], expect)
+    assert np.all(got[32:] & 0x7FFF == 0)
+
+
+# ---- W4A16 projection --------------------------------------------------------------
+
+SHAPES = [
+    (1, 16, 32), (1, 50, 96), (2, 200, 160), (4, 64, 4096), (15, 33, 128), (16, 64, 256),
+    (17, 80, 384), (33, 33, 512), (48, 100, 640), (64, 130, 1024),
+    (65, 130, 1024), (130, 300, 416), (257, 129, 96), (200, 64, 2048),
+]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_gemm_w4a16_matches_oracle(m, n, k):
+    _say(f"gemm_w4a16 m={m} n={n} k={k}")
+    x = si.activations(m, k, seed=m + n)
+    w = si.weight(n, k, seed=k, code_stream=1, scale_stream=2, ts=0.75)
+    y = nv.nvfp4_gemm_w4a16(x.cuda(), g_weight(w))
+    sync()
+    _, ye = oracle.gemm_w4a16(bits(x), o_weight(w))
+    assert_close(bits(y), ye, f"gemm m={m} n={n} k={k}")
+
+
+EXACT_SHAPES = [
+    ("decode gate", 1, 12288, 4096, None),
+    ("decode down", 1, 4096, 12288, None),
+    ("smallm gate", 64, 17408, 5120, 1024),
+    ("smallm down", 64, 5120, 17408, 512),
+    ("prefill gate", 2048, 17408, 5120, 256),
+    ("prefill down", 2048, 5120, 17408, 128),
+]
+
+
+@pytest.mark.parametrize("name,m,n,k,ncols", EXACT_SHAPES)
+def test_exact_case_bit_exact_at_full_shape(name, m, n, k, ncols):
+    """Integer X, power-of-two scales: every fp32 partial sum is exact, so the
+    GPU must equal the oracle bit for bit whatever its tiling or split."""
+    _say(f"exact case {name} m={m} n={n} k={k}")
+    x, w = si.exact_case(m, n, k, seed=3)
+    y = nv.nvfp4_gemm_w4a16(x.cuda(), g_weight(w))
+    sync()
+    got = bits(y)
+    rng = np.random.default_rng(5)
+    rows = np.arange(m) if m <= 64 else np.sort(rng.choice(m, 24, replace=False))
+    cols = np.arange(n) if ncols is None else np.sort(rng.choice(n, ncols, replace=False))
+    yo, _ = oracle.gemm_w4a16(bits(x)[rows], o_weight(w, cols))
+    assert np.array_equal(got[np.ix_(rows, cols)], yo)
+
+
+# ---- silu_mul -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("count", [1, 7, 8, 1000, 12288, 64 * 17408 + 3])
+def test_silu_mul_within_one_ulp(count):
+    _say(f"silu_mul count={count}")
+    g = (torch.randn(count, generator=torch.Generator().manual_seed(count)) * 4).to(torch.bfloat16)
+    u = (torch.randn(count, generator=torch.Generator().manual_seed(count + 1)) * 4).to(torch.bfloat16)
+    gd, ud = g.cuda(), u.cuda()
+    out = nv.silu_mul(gd.view(1, -1), ud.view(1, -1))
+    inplace = gd.clone().view(1, -1)
+    nv.silu_mul(inplace, ud.view(1, -1), out=inplace)
+    sync()
+    ref = oracle.silu_mul(bits(g), bits(u))
+    got = bits(out).reshape(-1)
+    assert np.array_equal(got, bits(inplace).reshape(-1))
+    d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    same_sign = (got & 0x8000) == (ref & 0x8000)
+    zero_pair = ((got & 0x7FFF) == 0) & ((ref & 0x7FFF) <= 1)
+    assert np.all((same_sign & (d <= 1)) | zero_pair)
+
+
+# ---- per-row quantizer (bit exact) -------------------------------------------------------
+
+def _quant_rows(m, k, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 1, (m, k)) * np.exp2(rng.integers(-20, 20, (m, 1)))
+    x[0] = 0.0
+    if m > 2:
+        x[1, : k // 2] = 0.0
+        x[2] *= 1e-30           # fp32-subnormal row scale
+    if m > 3:
+        x[3] = rng.integers(-6, 7, k) * 0.4375 / 4  # ties on the E2M1 grid
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("m,k", [(1, 32), (5, 4096), (7, 14336), (512, 4096)])
+def test_quantize_rows_bit_exact(m, k):
+    _say(f"quantize m={m} k={k}")
+    x = _quant_rows(m, k, seed=m * 7 + k)
+    c, s, r = nv.nvfp4_quantize_rows(x.cuda())
+    sync()
+    co, so, ro = oracle.quantize_rows(bits(x))
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(r.cpu().numpy().view(np.uint32), ro.view(np.uint32))
+    assert np.array_equal(c.cpu().numpy(), co)
+
+
+def test_quantize_golden_rows_on_gpu():
+    import test_oracle_compute as toc
+    rows = toc._read_quant_golden()
+    x = torch.tensor([r["x"] for r in rows], dtype=torch.float32).to(torch.bfloat16)
+    c, s, r = nv.nvfp4_quantize_rows(x.cuda())
+    sync()
+    for i, row in enumerate(rows):
+        assert list(s[i].cpu().numpy()) == row["scales"]
+        assert list(toc._unpack(c[i].cpu().numpy())) == row["codes"]
+        assert float(r[i]) == row["row_scale"]
+
+
+# ---- W4A4 projection ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 32), (3, 100, 160), (64, 130, 1024), (100, 64, 512)])
+def test_gemm_w4a4_matches_oracle(m, n, k):
+    _say(f"gemm_w4a4 m={m} n={n} k={k}")
+    x = si.activations(m, k, seed=m + 2 * n)
+    w = si.weight(n, k, seed=k + 1, code_stream=3, scale_stream=4, ts=1.25)
+    y = nv.nvfp4_gemm_w4a4(x.cuda(), g_weight(w))
+    sync()
+    _, ye = oracle.gemm_w4a4(bits(x), o_weight(w))
+    assert_close(bits(y), ye, f"w4a4 m={m} n={n} k={k}")
+
+
+def test_gemm_w4a4_rows_independent_of_m():
+    _say("w4a4 gemm invariance")
+    hidden, inter = 4096, 14336
+    x = si.activations(512, hidden, seed=9).cuda()
+    w = g_weight(si.weight(inter, hidden, seed=9, code_stream=1, scale_stream=2))
+    ref = nv.nvfp4_gemm_w4a4(x, w)
+    for m in si.W4A4_ROW_COUNTS[:-1]:
+        y = nv.nvfp4_gemm_w4a4(x[:m].contiguous(), w)
+        sync()
+        assert torch.equal(y.view(torch.int16), ref[:m].view(torch.int16)), m
+
+
+# ---- gate+up+silu entry point -----------------------------------------------------------------
+
+@pytest.mark.parametrize("m", [1, 5, 64, 96])
+def test_gate_up_silu_matches_oracle(m):
+    _say(f"gate_up_silu m={m}")
+    x, wg, wu, wd = si.workload("tiny", m=m)
+    act = nv.nvfp4_gate_up_silu_w4a16(x.cuda(), g_weight(wg), g_weight(wu))
+    sync()
+    _, _, g, u, a = oracle.dense_ffn(bits(x), o_weight(wg), o_weight(wu), o_weight(wd),
+                                     intermediates=True)
+    # act against silu(g)*u computed from the oracle's bf16 gate and up
+    exact = torch.nn.functional.silu(torch.from_numpy(bf16_f64(g))) * torch.from_numpy(bf16_f64(u))
+    assert_close(bits(act), exact.numpy(), f"gate_up_silu m={m}")
+
+
+# ---- rows beyond m and error paths ------------------------------------------------------------
+
+def test_rows_beyond_m_untouched_and_errors_leave_output():
+    x, wg, wu, wd = si.workload("tiny")
+    m, hidden = x.shape
+    out = torch.full((m + 3, hidden), 7.0, dtype=torch.bfloat16, device="cuda")
+    nv.dense_ffn_forward(x.cuda(), g_weight(wg), g_weight(wu), g_weight(wd), out=out[:m])
+    nv.dense_ffn_forward_w4a4(x.cuda(), g_weight(wg), g_weight(wu), g_weight(wd), out=out[:m])
+    sync()
+    assert torch.all(out[m:] == 7.0)
+    before = out.clone()
+    bad = nv.NVFP4Weight(g_weight(wd).codes, g_weight(wd).scales, 1.0)  # transposed role
+    with pytest.raises(nv.Nvfp4Error):
+        nv.dense_ffn_forward(x.cuda(), g_weight(wg), bad, g_weight(wd), out=out[:m])
+    sync()
+    assert torch.equal(out, before)
