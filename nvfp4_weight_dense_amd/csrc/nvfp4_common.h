@@ -61,8 +61,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// silu(t) = t * sigmoid(t), with the sigmoid built from exp(-|t|) in (0, 1]:
+// nothing overflows, so for very negative t the result stays the tiny (but
+// representable) t*e^t instead of t divided by an overflowed exp(-t).
 __device__ __forceinline__ float silu_f32(float t) {
-  return t / (1.0f + __expf(-t));
+  const float e = expf(-fabsf(t));
+  const float sig = t >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+  return t * sig;
 }
 
 // bf16(silu(bf16(g)) * bf16(u)): gate and up are rounded to bf16 first,

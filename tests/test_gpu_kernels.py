@@ -44,6 +44,8 @@ def test_dequant_every_code_and_scale_exact(m):
     sync()
     dense = oracle.dequant(o_weight(w))                  # [256, 32] doubles
     expect = oracle.bf16_from_double_array(dense.T)      # exact in bf16
+    # a -0 weight times 1 plus +0 products sums to +0
+    expect = np.where(expect == 0x8000, 0, expect).astype(np.uint16)
     got = bits(y)
     assert np.array_equal(got[:32], expect)
     assert np.all(got[32:] & 0x7FFF == 0)
@@ -97,10 +99,12 @@ def test_exact_case_bit_exact_at_full_shape(name, m, n, k, ncols):
 
 # ---- silu_mul -------------------------------------------------------------------------
 
-@pytest.mark.parametrize("count", [1, 7, 8, 1000, 12288, 64 * 17408 + 3])
-def test_silu_mul_within_one_ulp(count):
-    _say(f"silu_mul count={count}")
-    g = (torch.randn(count, generator=torch.Generator().manual_seed(count)) * 4).to(torch.bfloat16)
+@pytest.mark.parametrize("count,spread", [(1, 4), (7, 4), (8, 4), (1000, 4), (12288, 4),
+                                          (64 * 17408 + 3, 4), (100000, 60)])
+def test_silu_mul_within_one_ulp(count, spread):
+    """spread 60 reaches gates below -88, where exp(-g) overflows fp32."""
+    _say(f"silu_mul count={count} spread={spread}")
+    g = (torch.randn(count, generator=torch.Generator().manual_seed(count)) * spread).to(torch.bfloat16)
     u = (torch.randn(count, generator=torch.Generator().manual_seed(count + 1)) * 4).to(torch.bfloat16)
     gd, ud = g.cuda(), u.cuda()
     out = nv.silu_mul(gd.view(1, -1), ud.view(1, -1))
@@ -146,11 +150,14 @@ def test_quantize_golden_rows_on_gpu():
     import test_oracle_compute as toc
     rows = toc._read_quant_golden()
     x = torch.tensor([r["x"] for r in rows], dtype=torch.float32).to(torch.bfloat16)
-    c, s, r = nv.nvfp4_quantize_rows(x.cuda())
+    k = x.shape[1]                       # 48; the library takes k % 32 == 0
+    xp = torch.zeros((x.shape[0], 64), dtype=torch.bfloat16)
+    xp[:, :k] = x                        # a zero block changes no other block
+    c, s, r = nv.nvfp4_quantize_rows(xp.cuda())
     sync()
     for i, row in enumerate(rows):
-        assert list(s[i].cpu().numpy()) == row["scales"]
-        assert list(toc._unpack(c[i].cpu().numpy())) == row["codes"]
+        assert list(s[i].cpu().numpy()[: k // 16]) == row["scales"]
+        assert list(toc._unpack(c[i].cpu().numpy())[:k]) == row["codes"]
         assert float(r[i]) == row["row_scale"]
 
 
@@ -183,15 +190,26 @@ def test_gemm_w4a4_rows_independent_of_m():
 
 @pytest.mark.parametrize("m", [1, 5, 64, 96])
 def test_gate_up_silu_matches_oracle(m):
+    """gate and up meet the FFN tolerance against the oracle; the fused act
+    equals silu_mul of the GPU's own gate and up (same K order) within one
+    bf16 ulp.  act itself is heavy-tailed (max/rms >> 5), where a
+    correctly rounded bf16 value can sit more than 2e-2 rms from the exact
+    product, so the rms bound is not the right yardstick for it."""
     _say(f"gate_up_silu m={m}")
     x, wg, wu, wd = si.workload("tiny", m=m)
-    act = nv.nvfp4_gate_up_silu_w4a16(x.cuda(), g_weight(wg), g_weight(wu))
+    xd = x.cuda()
+    act = nv.nvfp4_gate_up_silu_w4a16(xd, g_weight(wg), g_weight(wu))
+    g = nv.nvfp4_gemm_w4a16(xd, g_weight(wg))
+    u = nv.nvfp4_gemm_w4a16(xd, g_weight(wu))
     sync()
-    _, _, g, u, a = oracle.dense_ffn(bits(x), o_weight(wg), o_weight(wu), o_weight(wd),
-                                     intermediates=True)
-    # act against silu(g)*u computed from the oracle's bf16 gate and up
-    exact = torch.nn.functional.silu(torch.from_numpy(bf16_f64(g))) * torch.from_numpy(bf16_f64(u))
-    assert_close(bits(act), exact.numpy(), f"gate_up_silu m={m}")
+    assert_close(bits(g), oracle.gemm_w4a16(bits(x), o_weight(wg))[1], f"gate m={m}")
+    assert_close(bits(u), oracle.gemm_w4a16(bits(x), o_weight(wu))[1], f"up m={m}")
+    ref = oracle.silu_mul(bits(g), bits(u))
+    got = bits(act)
+    d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    same_sign = (got & 0x8000) == (ref & 0x8000)
+    zero_pair = ((got & 0x7FFF) == 0) & ((ref & 0x7FFF) <= 1)
+    assert np.all((same_sign & (d <= 1)) | zero_pair)
 
 
 # ---- rows beyond m and error paths ------------------------------------------------------------
