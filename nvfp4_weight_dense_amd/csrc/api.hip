@@ -44,7 +44,12 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
-enum class Force { Auto, Stream, Tiled };
+enum class Force { Auto, Gemv, Stream, Tiled };
+enum class Path { Gemv, Stream, Tiled };
+
+const char *path_name(Path p) {
+  return p == Path::Gemv ? "gemv" : (p == Path::Stream ? "stream" : "tiled");
+}
 
 struct Config {
   int smallm_max_m = 64;
@@ -59,6 +64,7 @@ const Config &cfg() {
     Config c;
     if (const char *v = getenv("NVFP4_SMALLM_MAX_M")) c.smallm_max_m = atoi(v);
     if (const char *v = getenv("NVFP4_FORCE_PATH")) {
+      if (!strcmp(v, "gemv")) c.force = Force::Gemv;
       if (!strcmp(v, "stream")) c.force = Force::Stream;
       if (!strcmp(v, "tiled")) c.force = Force::Tiled;
     }
@@ -111,6 +117,39 @@ int arena_get(size_t bytes, void **out) {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Split-K arrival counters: a second grow-only buffer per device, zeroed
+// when allocated.  Every kernel that uses counters leaves them at zero.
+Arena g_counters[kMaxDevices];
+
+int counters_get(size_t words, unsigned **out) {
+  *out = nullptr;
+  if (words == 0) return NVFP4_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  Arena &a = g_counters[dev];
+  const size_t bytes = words * sizeof(unsigned);
+  if (a.size < bytes) {
+    size_t want = (bytes + 65535) & ~(size_t)65535;
+    if (a.ptr) {
+      if (hipDeviceSynchronize() != hipSuccess) return fail(NVFP4_EHIP, "hipDeviceSynchronize failed");
+      (void)hipFree(a.ptr);
+      a.ptr = nullptr;
+      a.size = 0;
+    }
+    if (hipMalloc(&a.ptr, want) != hipSuccess) {
+      a.ptr = nullptr;
+      (void)hipGetLastError();
+      return fail(NVFP4_ENOMEM, "split-K counters: hipMalloc of %zu bytes failed", want);
+    }
+    if (hipMemset(a.ptr, 0, want) != hipSuccess) return fail(NVFP4_EHIP, "hipMemset of counters failed");
+    a.size = want;
+  }
+  *out = (unsigned *)a.ptr;
+  return NVFP4_OK;
+}
+
 // ---- validation ------------------------------------------------------------------
 
 bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
@@ -120,6 +159,7 @@ int check_weight(const nvfp4_weight *w, const char *name) {
   if (!w->codes || !w->scales) return fail(NVFP4_EINVAL, "%s: null codes or scales pointer", name);
   if (w->n <= 0 || w->k <= 0) return fail(NVFP4_ESHAPE, "%s: n=%d k=%d must be positive", name, w->n, w->k);
   if (w->k % 32 != 0) return fail(NVFP4_ESHAPE, "%s: k=%d is not a multiple of 32", name, w->k);
+  if (w->k > 4194304) return fail(NVFP4_ESHAPE, "%s: k=%d exceeds 4194304", name, w->k);
   if (misaligned(w->codes) || misaligned(w->scales))
     return fail(NVFP4_EINVAL, "%s: codes/scales must be 16-byte aligned", name);
   return NVFP4_OK;
@@ -135,12 +175,27 @@ int check_act(const void *x, int m, const char *name) {
 
 MatRef mat(const nvfp4_weight *w) { return MatRef{w->codes, w->scales, w->tensor_scale}; }
 
-bool use_stream(int m) {
+// W4A16 path of one projection with m rows and reduction length k.  A
+// forced path that cannot serve the shape is an error (returns false).
+bool choose_path(int m, int k, Path *out) {
   switch (cfg().force) {
-    case Force::Stream: return true;
-    case Force::Tiled: return false;
-    default: return m <= cfg().smallm_max_m;
+    case Force::Gemv:
+      *out = Path::Gemv;
+      return gemv_eligible(m, k);
+    case Force::Stream: *out = Path::Stream; return true;
+    case Force::Tiled: *out = Path::Tiled; return true;
+    default:
+      if (gemv_eligible(m, k)) *out = Path::Gemv;
+      else *out = m <= cfg().smallm_max_m ? Path::Stream : Path::Tiled;
+      return true;
   }
+}
+
+int path_or_fail(int m, int k, Path *out) {
+  if (!choose_path(m, k, out))
+    return fail(NVFP4_ESHAPE, "NVFP4_FORCE_PATH=gemv cannot serve m=%d k=%d (needs m<=4 and a K "
+                "that fits four waves of register-resident activations)", m, k);
+  return NVFP4_OK;
 }
 
 int hip_status(hipError_t e, const char *what) {
@@ -180,17 +235,23 @@ struct ProfileScope {
 
 // ---- projections with caller-provided scratch ----------------------------------------
 
-// scratch bytes a W4A16 projection (nmat 1) or gate+up+silu (nmat 2) needs
-size_t proj_scratch_bytes(int m, int n, int k, int nmat, bool stream_path) {
-  if (stream_path) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+// scratch bytes a projection (nmat 1) or gate+up+silu (nmat 2) needs
+size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
+  if (path == Path::Gemv) return 0;
+  if (path == Path::Stream) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
   return nmat == 2 ? 2 * align256((size_t)2 * m * n) : 0;
 }
 
 int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, void *y,
-             void *scratch, bool stream_path, hipStream_t s) {
-  if (stream_path) {
+             void *scratch, Path path, hipStream_t s) {
+  if (path == Path::Gemv)
+    return hip_status(launch_gemv(a.x_bf16, m, k, n, nmat, w, y, s), "gemv projection launch");
+  if (path == Path::Stream) {
     StreamPlan pl = stream_plan(n, k);
-    return hip_status(launch_stream(a, m, k, n, nmat, w, y, (float *)scratch, pl, s),
+    unsigned *counters = nullptr;
+    int rc = counters_get(stream_counter_words(pl, m), &counters);
+    if (rc) return rc;
+    return hip_status(launch_stream(a, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
                       "weight-streaming projection launch");
   }
   if (nmat == 1) return hip_status(launch_tiled(a.x_bf16, m, k, n, w[0], y, s), "tiled projection launch");
@@ -252,11 +313,13 @@ void nvfp4_release(void) {
   int cur = 0;
   (void)hipGetDevice(&cur);
   for (int d = 0; d < kMaxDevices; ++d) {
-    if (!g_arena[d].ptr) continue;
-    (void)hipSetDevice(d);
-    (void)hipFree(g_arena[d].ptr);
-    g_arena[d].ptr = nullptr;
-    g_arena[d].size = 0;
+    for (Arena *a : {&g_arena[d], &g_counters[d]}) {
+      if (!a->ptr) continue;
+      (void)hipSetDevice(d);
+      (void)hipFree(a->ptr);
+      a->ptr = nullptr;
+      a->size = 0;
+    }
   }
   (void)hipSetDevice(cur);
 }
@@ -292,14 +355,15 @@ int nvfp4_gemm_w4a16(const void *x, int32_t m, const nvfp4_weight *w, void *y, v
     return rc;
   if (m == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
-  const bool st = use_stream(m);
-  log_path("gemm_w4a16", st ? "stream" : "tiled", m, w->n, w->k);
+  Path path;
+  if ((rc = path_or_fail(m, w->k, &path))) return rc;
+  log_path("gemm_w4a16", path_name(path), m, w->n, w->k);
   void *scr = nullptr;
-  size_t need = proj_scratch_bytes(m, w->n, w->k, 1, st);
+  size_t need = proj_scratch_bytes(m, w->n, w->k, 1, path);
   if (need && (rc = arena_get(need, &scr))) return rc;
   ProfileScope ps("gemm_w4a16", m, s);
   MatRef wm = mat(w);
-  return run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, w->k, w->n, 1, &wm, y, scr, st, s);
+  return run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, w->k, w->n, 1, &wm, y, scr, path, s);
 }
 
 int nvfp4_gate_up_silu_w4a16(const void *x, int32_t m, const nvfp4_weight *wg,
@@ -313,14 +377,15 @@ int nvfp4_gate_up_silu_w4a16(const void *x, int32_t m, const nvfp4_weight *wg,
     return fail(NVFP4_ESHAPE, "wg [%d][%d] and wu [%d][%d] differ", wg->n, wg->k, wu->n, wu->k);
   if (m == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
-  const bool st = use_stream(m);
-  log_path("gate_up_silu_w4a16", st ? "stream" : "tiled", m, wg->n, wg->k);
+  Path path;
+  if ((rc = path_or_fail(m, wg->k, &path))) return rc;
+  log_path("gate_up_silu_w4a16", path_name(path), m, wg->n, wg->k);
   void *scr = nullptr;
-  size_t need = proj_scratch_bytes(m, wg->n, wg->k, 2, st);
+  size_t need = proj_scratch_bytes(m, wg->n, wg->k, 2, path);
   if (need && (rc = arena_get(need, &scr))) return rc;
   ProfileScope ps("gate_up_silu_w4a16", m, s);
   MatRef w2[2] = {mat(wg), mat(wu)};
-  return run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, wg->k, wg->n, 2, w2, act, scr, st, s);
+  return run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, wg->k, wg->n, 2, w2, act, scr, path, s);
 }
 
 int dense_ffn_forward(const void *x, int32_t m, int32_t hidden, int32_t inter,
@@ -331,22 +396,24 @@ int dense_ffn_forward(const void *x, int32_t m, int32_t hidden, int32_t inter,
   if ((rc = check_ffn(x, m, hidden, inter, wg, wu, wd, out))) return rc;
   if (m == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
-  const bool st = use_stream(m);
-  log_path("dense_ffn_forward", st ? "stream" : "tiled", m, inter, hidden);
+  Path p_up, p_down;
+  if ((rc = path_or_fail(m, hidden, &p_up)) || (rc = path_or_fail(m, inter, &p_down))) return rc;
+  log_path("dense_ffn_forward gate+up", path_name(p_up), m, inter, hidden);
+  log_path("dense_ffn_forward down", path_name(p_down), m, hidden, inter);
   const size_t act_b = align256((size_t)2 * m * inter);
-  size_t scr_b = proj_scratch_bytes(m, inter, hidden, 2, st);
-  size_t down_b = proj_scratch_bytes(m, hidden, inter, 1, st);
+  size_t scr_b = proj_scratch_bytes(m, inter, hidden, 2, p_up);
+  size_t down_b = proj_scratch_bytes(m, hidden, inter, 1, p_down);
   if (down_b > scr_b) scr_b = down_b;
   void *base = nullptr;
   if ((rc = arena_get(act_b + scr_b, &base))) return rc;
   char *act = (char *)base;
   char *scr = act + act_b;
-  ProfileScope ps(st ? "dense_total stream" : "dense_total tiled", m, s);
+  ProfileScope ps("dense_total", m, s);
   MatRef w2[2] = {mat(wg), mat(wu)};
   MatRef wdm = mat(wd);
-  if ((rc = run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, hidden, inter, 2, w2, act, scr, st, s)))
+  if ((rc = run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, hidden, inter, 2, w2, act, scr, p_up, s)))
     return rc;
-  return run_proj(ActRef{act, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &wdm, out, scr, st, s);
+  return run_proj(ActRef{act, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &wdm, out, scr, p_down, s);
 }
 
 int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, void *stream) {
@@ -358,7 +425,7 @@ int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, vo
   hipStream_t s = (hipStream_t)stream;
   log_path("gemm_w4a4", "stream", m, w->n, w->k);
   QuantBuf q = quant_layout(nullptr, m, w->k);
-  size_t part = proj_scratch_bytes(m, w->n, w->k, 1, true);
+  size_t part = proj_scratch_bytes(m, w->n, w->k, 1, Path::Stream);
   void *base = nullptr;
   if ((rc = arena_get(q.bytes + part, &base))) return rc;
   q = quant_layout((char *)base, m, w->k);
@@ -367,7 +434,7 @@ int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, vo
     return rc;
   MatRef wm = mat(w);
   return run_proj(ActRef{nullptr, q.codes, q.scales, q.rs}, m, w->k, w->n, 1, &wm, y,
-                  (char *)base + q.bytes, true, s);
+                  (char *)base + q.bytes, Path::Stream, s);
 }
 
 int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden, int32_t inter,
@@ -382,8 +449,8 @@ int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden, int32_t int
   QuantBuf qx = quant_layout(nullptr, m, hidden);
   QuantBuf qa = quant_layout(nullptr, m, inter);
   const size_t act_b = align256((size_t)2 * m * inter);
-  size_t part = proj_scratch_bytes(m, inter, hidden, 2, true);
-  size_t part_d = proj_scratch_bytes(m, hidden, inter, 1, true);
+  size_t part = proj_scratch_bytes(m, inter, hidden, 2, Path::Stream);
+  size_t part_d = proj_scratch_bytes(m, hidden, inter, 1, Path::Stream);
   if (part_d > part) part = part_d;
   void *base = nullptr;
   if ((rc = arena_get(qx.bytes + qa.bytes + act_b + part, &base))) return rc;
@@ -399,13 +466,13 @@ int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden, int32_t int
                        "quantize launch")))
     return rc;
   if ((rc = run_proj(ActRef{nullptr, qx.codes, qx.scales, qx.rs}, m, hidden, inter, 2, w2, act, scr,
-                     true, s)))
+                     Path::Stream, s)))
     return rc;
   if ((rc = hip_status(launch_quantize_rows(act, m, inter, qa.codes, qa.scales, qa.rs, s),
                        "quantize launch")))
     return rc;
   return run_proj(ActRef{nullptr, qa.codes, qa.scales, qa.rs}, m, inter, hidden, 1, &wdm, out, scr,
-                  true, s);
+                  Path::Stream, s);
 }
 
 }  // extern "C"

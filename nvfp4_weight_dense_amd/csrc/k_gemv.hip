@@ -1,0 +1,275 @@
+// k_gemv.hip -- NVFP4 projection for 1..4 rows on the vector ALUs (gfx950).
+//
+// Regime: single-row decode (page layers/dense_ffn_overlays.rs,
+// `set_lora_weights`: the split-SiLU decode path is a W4A16 GEMV followed by
+// the activation).  At one to four rows a 16x16 MFMA would waste most of
+// its rows, and the weight stream from HBM is the whole cost, so the
+// dequantize+multiply work per weight must stay far below the bandwidth
+// budget (about 2.8 vector ops per weight at 8 TB/s).
+//
+// Per weight: the hardware fp4 conversion turns a code byte into an exact
+// bf16 pair (scale operand 1.0), one v_dot2_f32_bf16 multiplies the pair
+// with a register-resident activation pair and accumulates in fp32; each
+// 16-element block sum is then multiplied by its E4M3 scale (one fma per
+// block and row).  About 1.1 vector ops per weight at one row.
+//
+// Layout of the work:
+//   * A workgroup of KW waves splits K into KW contiguous chunks; lane l of
+//     wave w owns the 32-element K granules w*64*G + g*64 + l (g < G), so one
+//     128-bit load of a weight row covers 64 consecutive granules (1 KB,
+//     fully coalesced).  The lane keeps x for its granules in registers for
+//     the whole kernel.
+//   * The workgroup walks batches of 8 weight rows (8 columns, or 4 gate +
+//     4 up columns for the fused gate+up+silu).  Each lane produces 8 partial
+//     sums; a butterfly that halves the list at each exchange leaves lane
+//     group l>>3 with column l>>3 summed over all 64 lanes (17 shuffles per
+//     batch), then the waves add their chunk sums in fixed wave order.
+#include "launchers.h"
+#include "nvfp4_common.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kCB = 8;      // weight rows per batch
+constexpr int kMaxKW = 4;   // waves per workgroup
+
+struct GemvArgs {
+  const void *x;          // bf16 [m][k]
+  int m, k, n;
+  const uint8_t *codes0, *scales0;
+  const uint8_t *codes1, *scales1;
+  float ts0, ts1;
+  void *y;                // bf16 [m][n]
+  int nbatch;
+};
+
+__device__ __forceinline__ bf16x2 u32_as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+template <int M, int NMAT, int G>
+__global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
+  constexpr int NC = kCB / NMAT;  // output columns per batch
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kw = blockDim.x >> 6;
+  const int k = p.k;
+  const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
+  const uint32_t gran = (uint32_t)k >> 5;
+
+  uint32_t jg[G];
+  bool jok[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    jg[g] = (uint32_t)(wave * 64 * G + g * 64 + lane);
+    jok[g] = jg[g] < gran;
+  }
+
+  // activations of this lane's granules, as bf16 pairs
+  uint32_t xr[M][G][16];
+  {
+    const __amdgpu_buffer_rsrc_t xres = rsrc(p.x, (size_t)p.m * k * 2);
+#pragma unroll
+    for (int r = 0; r < M; ++r)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t off = (jok[g] && r < p.m) ? ((uint32_t)r * (uint32_t)k + jg[g] * 32u) * 2u : kOOB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = ld16(xres, off + 16u * q);
+          xr[r][g][4 * q + 0] = v.x;
+          xr[r][g][4 * q + 1] = v.y;
+          xr[r][g][4 * q + 2] = v.z;
+          xr[r][g][4 * q + 3] = v.w;
+        }
+      }
+  }
+
+  __shared__ float red[kMaxKW][kCB][M];
+
+  for (int b = blockIdx.x; b < p.nbatch; b += gridDim.x) {
+    const int c0 = b * NC;
+    const int ncols = min(NC, p.n - c0);
+    __amdgpu_buffer_rsrc_t wres[NMAT], sres[NMAT];
+    wres[0] = rsrc(p.codes0 + (size_t)c0 * kb2, (size_t)ncols * kb2);
+    sres[0] = rsrc(p.scales0 + (size_t)c0 * kb16, (size_t)ncols * kb16);
+    if constexpr (NMAT > 1) {
+      wres[1] = rsrc(p.codes1 + (size_t)c0 * kb2, (size_t)ncols * kb2);
+      sres[1] = rsrc(p.scales1 + (size_t)c0 * kb16, (size_t)ncols * kb16);
+    }
+    uint4 cw[kCB][G];
+    uint32_t sw[kCB][G];
+#pragma unroll
+    for (int i = 0; i < kCB; ++i) {
+      const int mat = i % NMAT;
+      const uint32_t col = (uint32_t)(i / NMAT);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        cw[i][g] = ld16(wres[mat], jok[g] ? col * kb2 + jg[g] * 16u : kOOB);
+        sw[i][g] = ld2(sres[mat], jok[g] ? col * kb16 + jg[g] * 2u : kOOB);
+      }
+    }
+
+    float v[kCB][M];
+#pragma unroll
+    for (int i = 0; i < kCB; ++i) {
+#pragma unroll
+      for (int r = 0; r < M; ++r) v[i][r] = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float s[2] = {e4m3_to_f32_sel<0>(sw[i][g]), e4m3_to_f32_sel<1>(sw[i][g])};
+        const uint32_t words[4] = {cw[i][g].x, cw[i][g].y, cw[i][g].z, cw[i][g].w};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // the two 16-element scale blocks
+          float blk[M];
+#pragma unroll
+          for (int r = 0; r < M; ++r) blk[r] = 0.f;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t w = words[2 * h + q];
+            bf16x2 c2[4];
+            c2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+            c2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+            c2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+            c2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int r = 0; r < M; ++r)
+                blk[r] = __builtin_amdgcn_fdot2_f32_bf16(
+                    c2[e], u32_as_bf16x2(xr[r][g][(2 * h + q) * 4 + e]), blk[r], false);
+          }
+#pragma unroll
+          for (int r = 0; r < M; ++r) v[i][r] = fmaf(blk[r], s[h], v[i][r]);
+        }
+      }
+    }
+
+    // butterfly: after the exchanges at 32, 16, 8 lane l holds list entry
+    // (l >> 3) summed over 8 lanes; then a full sum over the remaining bits
+    float tot[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      float a[kCB];
+#pragma unroll
+      for (int i = 0; i < kCB; ++i) a[i] = v[i][r];
+#pragma unroll
+      for (int o = 32, h = kCB / 2; h >= 1; o >>= 1, h >>= 1) {
+        const bool up = (lane & o) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+          const float send = up ? a[i] : a[i + h];
+          const float keep = up ? a[i + h] : a[i];
+          a[i] = keep + __shfl_xor(send, o);
+        }
+      }
+      float t = a[0];
+      t += __shfl_xor(t, 4);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 1);
+      tot[r] = t;
+    }
+
+    if (kw > 1) {
+      if ((lane & 7) == 0) {
+#pragma unroll
+        for (int r = 0; r < M; ++r) red[wave][lane >> 3][r] = tot[r];
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+          float t = red[0][lane >> 3][r];
+          for (int w = 1; w < kw; ++w) t += red[w][lane >> 3][r];
+          tot[r] = t;
+        }
+      }
+      __syncthreads();
+    }
+    if (wave != 0) continue;
+
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      if (r >= p.m) break;
+      if constexpr (NMAT == 1) {
+        const int c = lane >> 3;
+        if ((lane & 7) == 0 && c < ncols)
+          ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = (__bf16)(tot[r] * p.ts0);
+      } else {
+        const float up = __shfl_xor(tot[r], 8);  // entry 2c+1 (up) next to 2c (gate)
+        const int c = lane >> 4;
+        if ((lane & 15) == 0 && c < ncols)
+          ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = swiglu_bf16(tot[r] * p.ts0, up * p.ts1);
+      }
+    }
+  }
+}
+
+struct GemvShape {
+  int kw, g;
+};
+
+int gmax_for_rows(int m) { return m == 1 ? 3 : (m == 2 ? 2 : 1); }
+
+GemvShape gemv_shape(int m, int k) {
+  const int gran = k / 32;
+  const int gmax = gmax_for_rows(m);
+  GemvShape s;
+  s.kw = cdiv(gran, 64 * gmax);
+  s.g = cdiv(gran, 64 * s.kw);
+  return s;
+}
+
+template <int M, int NMAT, int G>
+hipError_t launch_g(const GemvArgs &p, int kw, hipStream_t st) {
+  const int grid = p.nbatch < 4096 ? p.nbatch : 4096;
+  hipLaunchKernelGGL((k_gemv<M, NMAT, G>), dim3(grid), dim3(64 * kw), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int M, int NMAT>
+hipError_t launch_m(const GemvArgs &p, const GemvShape &s, hipStream_t st) {
+  switch (s.g) {
+    case 1: return launch_g<M, NMAT, 1>(p, s.kw, st);
+    case 2: return launch_g<M, NMAT, (M <= 2 ? 2 : 1)>(p, s.kw, st);
+    default: return launch_g<M, NMAT, (M == 1 ? 3 : 1)>(p, s.kw, st);
+  }
+}
+
+template <int NMAT>
+hipError_t launch_n(const GemvArgs &p, const GemvShape &s, hipStream_t st) {
+  switch (p.m) {
+    case 1: return launch_m<1, NMAT>(p, s, st);
+    case 2: return launch_m<2, NMAT>(p, s, st);
+    case 3: return launch_m<3, NMAT>(p, s, st);
+    default: return launch_m<4, NMAT>(p, s, st);
+  }
+}
+
+}  // namespace
+
+bool gemv_eligible(int m, int k) {
+  if (m < 1 || m > 4) return false;
+  const GemvShape s = gemv_shape(m, k);
+  return s.kw <= kMaxKW && s.g <= gmax_for_rows(m);
+}
+
+hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat, const MatRef *w, void *y,
+                       hipStream_t stream) {
+  GemvArgs p{};
+  p.x = x;
+  p.m = m;
+  p.k = k;
+  p.n = n;
+  p.codes0 = w[0].codes;
+  p.scales0 = w[0].scales;
+  p.ts0 = w[0].ts;
+  p.codes1 = nmat > 1 ? w[1].codes : nullptr;
+  p.scales1 = nmat > 1 ? w[1].scales : nullptr;
+  p.ts1 = nmat > 1 ? w[1].ts : 0.f;
+  p.y = y;
+  p.nbatch = cdiv(n, kCB / nmat);
+  const GemvShape s = gemv_shape(m, k);
+  return nmat == 1 ? launch_n<1>(p, s, stream) : launch_n<2>(p, s, stream);
+}
+
+}  // namespace nvfp4

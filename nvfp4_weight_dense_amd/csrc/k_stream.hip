@@ -5,22 +5,27 @@
 // bound by streaming the 4.5-bit weights from HBM once.
 //
 // Work decomposition
-//   * A workgroup owns 16 output columns (one MFMA tile width) and a range of
-//     K; its NW waves split that range into interleaved 128-element steps.
+//   * A workgroup owns CTW column tiles of 16 output columns (for each of
+//     NMAT weight matrices: 1, or 2 for gate+up with a fused silu epilogue)
+//     and a range of K; its 4 waves split that range into interleaved
+//     128-element steps.
 //   * In one step, lane (c = lane%16, g = lane/16) loads 16 bytes of codes
-//     (32 K elements of weight row col0+c, K offset 32g) plus their 2 scale
-//     bytes with one 128-bit and one 16-bit load; a wave's load covers 16
-//     rows x 64 contiguous bytes.  The codes are dequantized in registers to
-//     four bf16 B fragments and fed to v_mfma_f32_16x16x32_bf16, whose K
-//     order inside a step is (g, element) -- the same permutation is used for
-//     the activation fragment, so the sum is unchanged.
-//   * The activation fragment of row r in a step is the 32 contiguous K
-//     values starting at the same offset (bf16, 64 bytes), or, for W4A4, the
-//     row's NVFP4 codes dequantized exactly like the weight.
-//   * Waves reduce through LDS in fixed wave order; with ksplit > 1 the
-//     workgroups write fp32 partials that a second kernel sums in split
-//     order.  The K order of every output therefore depends only on (n, k),
-//     never on m -- the property the W4A4 arm needs.
+//     (32 K elements of weight row col0+c at K offset 32g) and their 2 scale
+//     bytes with one 128-bit and one 16-bit buffer load; per column tile a
+//     wave's load covers 16 rows x 64 contiguous bytes.  Buffer loads return
+//     zero outside the resource's range, so ragged columns, rows and K need
+//     no branches.  The codes are dequantized in registers to four bf16 B
+//     fragments of v_mfma_f32_16x16x32_bf16; the MFMA's K order inside a step
+//     is (g, element), and the activation fragment uses the same order.
+//   * The activation fragment of row r is the 32 contiguous K values at the
+//     same offset (bf16, 64 bytes), or for W4A4 the row's NVFP4 codes
+//     dequantized exactly like the weight; one fragment feeds CTW*NMAT MFMAs.
+//   * Waves reduce through LDS in fixed wave order.  With ksplit > 1 each
+//     workgroup writes its fp32 partial tile; the last workgroup of a tile to
+//     finish (a self-resetting arrival counter) sums the partials in split
+//     order and runs the epilogue.  The K order of every output therefore
+//     depends only on (n, k), never on m or on arrival order -- the property
+//     the W4A4 arm needs.
 //   * Up to 64 rows (MT tiles of 16) share each dequantized weight fragment;
 //     more rows use more row blocks (grid.z).
 #include "launchers.h"
@@ -30,7 +35,7 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int kNW = 4;            // waves per workgroup (K split inside it)
+constexpr int kNW = 4;  // waves per workgroup (K split inside it)
 constexpr int kTargetBlocks = 512;
 
 struct StreamArgs {
@@ -43,102 +48,112 @@ struct StreamArgs {
   const uint8_t *codes1, *scales1;
   float ts0, ts1;
   void *y;
-  float *partial;
+  float *partial;         // [nmat][ksplit][m][n]
+  unsigned *counters;     // [gridDim.z][gridDim.x], zero between calls
   int ksplit, steps_per_split;
 };
 
-template <int MT>
-struct Batch {  // steps loaded together per wave
-  static constexpr int U = MT == 1 ? 8 : (MT == 2 ? 4 : 2);
+
+template <int MT, int NMAT, int CTW, bool AFP4>
+struct Cfg {
+  static constexpr int kRegsPerStep = NMAT * CTW * 5 + MT * (AFP4 ? 5 : 16);
+  static constexpr int U = kRegsPerStep * 8 <= 128 ? 8 : (kRegsPerStep * 4 <= 128 ? 4 : 2);
 };
 
-template <int MT, int NMAT, bool AFP4>
+template <int MT, int NMAT, int CTW, bool AFP4>
 __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
-  constexpr int U = Batch<MT>::U;
+  constexpr int U = Cfg<MT, NMAT, CTW, AFP4>::U;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int g = lane >> 4;
   const int k = p.k;
-  const int col = blockIdx.x * 16 + c16;
-  const bool col_ok = col < p.n;
+  const int col0 = blockIdx.x * (16 * CTW);
   const int row0 = blockIdx.z * 64;
   const int nsteps = (k + 127) >> 7;
   const int s_begin = blockIdx.y * p.steps_per_split;
   const int s_end = min(nsteps, s_begin + p.steps_per_split);
+  const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
 
-  const size_t wrow = (size_t)(col_ok ? col : 0);
-  const uint8_t *crow0 = p.codes0 + wrow * (size_t)(k >> 1);
-  const uint8_t *srow0 = p.scales0 + wrow * (size_t)(k >> 4);
-  const uint8_t *crow1 = NMAT > 1 ? p.codes1 + wrow * (size_t)(k >> 1) : nullptr;
-  const uint8_t *srow1 = NMAT > 1 ? p.scales1 + wrow * (size_t)(k >> 4) : nullptr;
-
-  // activation rows this lane feeds (A operand row = lane % 16)
-  bool a_ok[MT];
-  size_t arow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int r = row0 + mt * 16 + c16;
-    a_ok[mt] = r < p.m;
-    arow[mt] = (size_t)(a_ok[mt] ? r : 0);
+  // resources cover exactly this workgroup's weight rows and activation rows
+  const int ncols = min(16 * CTW, p.n - col0);
+  const int nrows = min(64, p.m - row0);
+  __amdgpu_buffer_rsrc_t wc[NMAT], ws[NMAT];
+  wc[0] = rsrc(p.codes0 + (size_t)col0 * kb2, (size_t)ncols * kb2);
+  ws[0] = rsrc(p.scales0 + (size_t)col0 * kb16, (size_t)ncols * kb16);
+  if constexpr (NMAT > 1) {
+    wc[1] = rsrc(p.codes1 + (size_t)col0 * kb2, (size_t)ncols * kb2);
+    ws[1] = rsrc(p.scales1 + (size_t)col0 * kb16, (size_t)ncols * kb16);
+  }
+  __amdgpu_buffer_rsrc_t ax, axs;
+  if constexpr (AFP4) {
+    ax = rsrc(p.xc + (size_t)row0 * kb2, (size_t)nrows * kb2);
+    axs = rsrc(p.xs + (size_t)row0 * kb16, (size_t)nrows * kb16);
+  } else {
+    ax = rsrc((const uint16_t *)p.x + (size_t)row0 * k, (size_t)nrows * k * 2);
+    axs = ax;
   }
 
-  f32x4 acc[NMAT][MT];
+  f32x4 acc[NMAT][CTW][MT];
 #pragma unroll
   for (int i = 0; i < NMAT; ++i)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
   for (int base = s_begin + wave; base < s_end; base += kNW * U) {
-    uint4 bw[U][NMAT];
-    uint32_t bsc[U][NMAT];
+    uint4 bw[U][NMAT][CTW];
+    uint32_t bsc[U][NMAT][CTW];
     uint4 aw[U][MT][AFP4 ? 1 : 4];
     uint32_t asc[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + u * kNW;
-      const int kk = t * 128 + 32 * g;
-      const bool ok = t < s_end && kk < k;
-      const bool wok = ok && col_ok;
-      bw[u][0] = wok ? *(const uint4 *)(crow0 + (kk >> 1)) : z4;
-      bsc[u][0] = wok ? (uint32_t)*(const uint16_t *)(srow0 + (kk >> 4)) : 0u;
-      if constexpr (NMAT > 1) {
-        bw[u][1] = wok ? *(const uint4 *)(crow1 + (kk >> 1)) : z4;
-        bsc[u][1] = wok ? (uint32_t)*(const uint16_t *)(srow1 + (kk >> 4)) : 0u;
-      }
+      const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
+      const bool ok = t < s_end && kk < (uint32_t)k;
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const uint32_t row = (uint32_t)(ct * 16 + c16);
+          bw[u][i][ct] = ld16(wc[i], ok ? row * kb2 + (kk >> 1) : kOOB);
+          bsc[u][i][ct] = ld2(ws[i], ok ? row * kb16 + (kk >> 4) : kOOB);
+        }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bool aok = ok && a_ok[mt];
+        const uint32_t r = (uint32_t)(mt * 16 + c16);
         if constexpr (AFP4) {
-          aw[u][mt][0] = aok ? *(const uint4 *)(p.xc + arow[mt] * (size_t)(k >> 1) + (kk >> 1)) : z4;
-          asc[u][mt] = aok ? (uint32_t)*(const uint16_t *)(p.xs + arow[mt] * (size_t)(k >> 4) + (kk >> 4)) : 0u;
+          aw[u][mt][0] = ld16(ax, ok ? r * kb2 + (kk >> 1) : kOOB);
+          asc[u][mt] = ld2(axs, ok ? r * kb16 + (kk >> 4) : kOOB);
         } else {
-          const uint4 *src = (const uint4 *)((const uint16_t *)p.x + arow[mt] * (size_t)k + kk);
+          const uint32_t off = ok ? (r * (uint32_t)k + kk) * 2u : kOOB;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) aw[u][mt][q] = aok ? src[q] : z4;
+          for (int q = 0; q < 4; ++q) aw[u][mt][q] = ld16(ax, off + 16u * q);
           asc[u][mt] = 0;
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      bf16x8 bf[NMAT][4];
+      bf16x8 bf[NMAT][CTW][4];
 #pragma unroll
-      for (int i = 0; i < NMAT; ++i) {
-        const float s0 = e4m3_to_f32(bsc[u][i] & 0xFFu);
-        const float s1 = e4m3_to_f32(bsc[u][i] >> 8);
-        bf[i][0] = dequant8(bw[u][i].x, s0);
-        bf[i][1] = dequant8(bw[u][i].y, s0);
-        bf[i][2] = dequant8(bw[u][i].z, s1);
-        bf[i][3] = dequant8(bw[u][i].w, s1);
-      }
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const float s0 = e4m3_to_f32_sel<0>(bsc[u][i][ct]);
+          const float s1 = e4m3_to_f32_sel<1>(bsc[u][i][ct]);
+          bf[i][ct][0] = dequant8(bw[u][i][ct].x, s0);
+          bf[i][ct][1] = dequant8(bw[u][i][ct].y, s0);
+          bf[i][ct][2] = dequant8(bw[u][i][ct].z, s1);
+          bf[i][ct][3] = dequant8(bw[u][i][ct].w, s1);
+        }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         bf16x8 af[4];
         if constexpr (AFP4) {
-          const float s0 = e4m3_to_f32(asc[u][mt] & 0xFFu);
-          const float s1 = e4m3_to_f32(asc[u][mt] >> 8);
+          const float s0 = e4m3_to_f32_sel<0>(asc[u][mt]);
+          const float s1 = e4m3_to_f32_sel<1>(asc[u][mt]);
           af[0] = dequant8(aw[u][mt][0].x, s0);
           af[1] = dequant8(aw[u][mt][0].y, s0);
           af[2] = dequant8(aw[u][mt][0].z, s1);
@@ -151,122 +166,157 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int i = 0; i < NMAT; ++i)
-            acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bf[i][j], acc[i][mt], 0, 0, 0);
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+              acc[i][ct][mt] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
       }
     }
   }
 
-  // fixed-order reduction over the workgroup's waves
-  __shared__ float red[kNW][NMAT][MT][4][64];
+  // fixed-order reduction over the workgroup's waves, one (matrix, tile)
+  // pair at a time to bound LDS
+  __shared__ float red[kNW - 1][MT][4][64];
 #pragma unroll
   for (int i = 0; i < NMAT; ++i)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int ct = 0; ct < CTW; ++ct) {
+      if (wave > 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][i][mt][e][lane] = acc[i][mt][e];
-  __syncthreads();
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[wave - 1][mt][e][lane] = acc[i][ct][mt][e];
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float s = acc[i][ct][mt][e];
+#pragma unroll
+            for (int w = 0; w < kNW - 1; ++w) s += red[w][mt][e][lane];
+            acc[i][ct][mt][e] = s;
+          }
+      }
+      __syncthreads();
+    }
   if (wave != 0) return;
+
+  const size_t mn = (size_t)p.m * p.n;
+  if (p.ksplit > 1) {
+    // publish this split's partial tile, then count arrivals
 #pragma unroll
-  for (int i = 0; i < NMAT; ++i)
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int col = col0 + ct * 16 + c16;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = row0 + mt * 16 + 4 * g + e;
+          if (r < p.m && col < p.n)
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i)
+              p.partial[((size_t)i * p.ksplit + blockIdx.y) * mn + (size_t)r * p.n + col] =
+                  acc[i][ct][mt][e];
+        }
+    }
+    unsigned *cnt = p.counters + (size_t)blockIdx.z * gridDim.x + blockIdx.x;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    unsigned old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old != (unsigned)(p.ksplit - 1)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // last arrival: sum the partials in split order
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      const int col = col0 + ct * 16 + c16;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = row0 + mt * 16 + 4 * g + e;
+          if (r < p.m && col < p.n)
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i) {
+              float s = 0.f;
+              for (int sp = 0; sp < p.ksplit; ++sp)
+                s += p.partial[((size_t)i * p.ksplit + sp) * mn + (size_t)r * p.n + col];
+              acc[i][ct][mt][e] = s;
+            }
+        }
+    }
+    if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // epilogue: output element (row0 + mt*16 + 4g + e, col0 + ct*16 + c16)
+#pragma unroll
+  for (int ct = 0; ct < CTW; ++ct) {
+    const int col = col0 + ct * 16 + c16;
+    if (col >= p.n) continue;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float s = red[0][i][mt][e][lane];
-#pragma unroll
-        for (int w = 1; w < kNW; ++w) s += red[w][i][mt][e][lane];
-        acc[i][mt][e] = s;
+        const int r = row0 + mt * 16 + 4 * g + e;
+        if (r >= p.m) continue;
+        float v0 = acc[0][ct][mt][e];
+        float v1 = acc[NMAT - 1][ct][mt][e];
+        if constexpr (AFP4) {
+          const float rs = p.xr[r];
+          v0 = v0 * rs;
+          v1 = v1 * rs;
+        }
+        v0 = v0 * p.ts0;
+        __bf16 out;
+        if constexpr (NMAT > 1) {
+          v1 = v1 * p.ts1;
+          out = swiglu_bf16(v0, v1);
+        } else {
+          out = (__bf16)v0;
+        }
+        ((__bf16 *)p.y)[(size_t)r * p.n + col] = out;
       }
-
-  if (!col_ok) return;
-  // output element (row0 + mt*16 + 4g + e, col) of the 16x16 tile
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = row0 + mt * 16 + 4 * g + e;
-      if (r >= p.m) continue;
-      if (p.ksplit > 1) {
-#pragma unroll
-        for (int i = 0; i < NMAT; ++i)
-          p.partial[(((size_t)i * p.ksplit + blockIdx.y) * p.m + r) * p.n + col] = acc[i][mt][e];
-        continue;
-      }
-      float v0 = acc[0][mt][e];
-      float v1 = NMAT > 1 ? acc[NMAT - 1][mt][e] : 0.f;
-      if constexpr (AFP4) {
-        const float rs = p.xr[r];
-        v0 = v0 * rs;
-        v1 = v1 * rs;
-      }
-      v0 = v0 * p.ts0;
-      __bf16 out;
-      if constexpr (NMAT > 1) {
-        v1 = v1 * p.ts1;
-        out = swiglu_bf16(v0, v1);
-      } else {
-        out = (__bf16)v0;
-      }
-      ((__bf16 *)p.y)[(size_t)r * p.n + col] = out;
-    }
-}
-
-// Sums split-K partials in split order and applies the epilogue.
-template <int NMAT, bool AFP4>
-__global__ __launch_bounds__(256) void k_splitk_reduce(StreamArgs p) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t total = (size_t)p.m * p.n;
-  if (idx >= total) return;
-  const int r = (int)(idx / p.n);
-  float v[NMAT];
-#pragma unroll
-  for (int i = 0; i < NMAT; ++i) {
-    float s = 0.f;
-    for (int sp = 0; sp < p.ksplit; ++sp) s += p.partial[((size_t)i * p.ksplit + sp) * total + idx];
-    if constexpr (AFP4) s = s * p.xr[r];
-    v[i] = s;
   }
-  __bf16 out;
-  if constexpr (NMAT > 1)
-    out = swiglu_bf16(v[0] * p.ts0, v[1] * p.ts1);
-  else
-    out = (__bf16)(v[0] * p.ts0);
-  ((__bf16 *)p.y)[idx] = out;
 }
 
-template <int MT, int NMAT, bool AFP4>
-hipError_t launch_mt(const StreamArgs &p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_stream<MT, NMAT, AFP4>), grid, dim3(kNW * 64), 0, s, p);
+template <int MT, int NMAT, int CTW, bool AFP4>
+hipError_t launch_one(const StreamArgs &p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_stream<MT, NMAT, CTW, AFP4>), grid, dim3(kNW * 64), 0, s, p);
   return hipGetLastError();
 }
 
-template <int NMAT, bool AFP4>
-hipError_t launch_cfg(const StreamArgs &p, int mt, dim3 grid, hipStream_t s) {
+template <int NMAT, int CTW, bool AFP4>
+hipError_t launch_mt(const StreamArgs &p, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_mt<1, NMAT, AFP4>(p, grid, s);
-    case 2: return launch_mt<2, NMAT, AFP4>(p, grid, s);
-    case 3: return launch_mt<3, NMAT, AFP4>(p, grid, s);
-    default: return launch_mt<4, NMAT, AFP4>(p, grid, s);
+    case 1: return launch_one<1, NMAT, CTW, AFP4>(p, grid, s);
+    case 2: return launch_one<2, NMAT, CTW, AFP4>(p, grid, s);
+    case 3: return launch_one<3, NMAT, CTW, AFP4>(p, grid, s);
+    default: return launch_one<4, NMAT, CTW, AFP4>(p, grid, s);
   }
 }
 
 }  // namespace
 
+int stream_ctw(int n) { return n >= 16 * 2 * kTargetBlocks ? 2 : 1; }
+
 StreamPlan stream_plan(int n, int k) {
-  // The split depends on (n, k) only: the same projection shape reduces in
-  // the same order at every row count.
-  const int tiles = cdiv(n, 16);
+  // The split depends on (n, k) only: one projection shape reduces in the
+  // same order at every row count.
+  const int tiles = cdiv(n, 16 * stream_ctw(n));
   const int nsteps = cdiv(k, 128);
   int ksplit = 1;
   if (tiles < kTargetBlocks) {
-    int want = cdiv(kTargetBlocks, tiles);
-    int cap = nsteps / (kNW * 2);  // at least two steps per wave
+    const int want = cdiv(kTargetBlocks, tiles);
+    const int cap = nsteps / (kNW * 2);  // at least two steps per wave
     ksplit = want < cap ? want : cap;
     if (ksplit < 1) ksplit = 1;
   }
   StreamPlan pl;
   pl.steps_per_split = cdiv(nsteps, ksplit);
   pl.ksplit = cdiv(nsteps, pl.steps_per_split);
+  pl.tiles = tiles;
   return pl;
 }
 
@@ -274,9 +324,13 @@ size_t stream_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
   return pl.ksplit > 1 ? (size_t)nmat * pl.ksplit * m * n : 0;
 }
 
-hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
-                         const MatRef *w, void *y, float *partial,
-                         const StreamPlan &pl, hipStream_t stream) {
+size_t stream_counter_words(const StreamPlan &pl, int m) {
+  return pl.ksplit > 1 ? (size_t)pl.tiles * cdiv(m, 64) : 0;
+}
+
+hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, void *y,
+                         float *partial, unsigned *counters, const StreamPlan &pl,
+                         hipStream_t stream) {
   StreamArgs p{};
   p.x = a.x_bf16;
   p.xc = a.codes;
@@ -293,31 +347,21 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
   p.ts1 = nmat > 1 ? w[1].ts : 0.f;
   p.y = y;
   p.partial = partial;
+  p.counters = counters;
   p.ksplit = pl.ksplit;
   p.steps_per_split = pl.steps_per_split;
   const bool afp4 = a.x_bf16 == nullptr;
   const int mt = m >= 64 ? 4 : cdiv(m, 16);
-  dim3 grid(cdiv(n, 16), pl.ksplit, cdiv(m, 64));
-  hipError_t e;
-  if (nmat == 1)
-    e = afp4 ? launch_cfg<1, true>(p, mt, grid, stream) : launch_cfg<1, false>(p, mt, grid, stream);
-  else
-    e = afp4 ? launch_cfg<2, true>(p, mt, grid, stream) : launch_cfg<2, false>(p, mt, grid, stream);
-  if (e != hipSuccess || pl.ksplit == 1) return e;
-  const size_t total = (size_t)m * n;
-  dim3 rgrid((unsigned)((total + 255) / 256));
-  if (nmat == 1) {
-    if (afp4)
-      hipLaunchKernelGGL((k_splitk_reduce<1, true>), rgrid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((k_splitk_reduce<1, false>), rgrid, dim3(256), 0, stream, p);
-  } else {
-    if (afp4)
-      hipLaunchKernelGGL((k_splitk_reduce<2, true>), rgrid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((k_splitk_reduce<2, false>), rgrid, dim3(256), 0, stream, p);
+  const int ctw = stream_ctw(n);
+  dim3 grid(pl.tiles, pl.ksplit, cdiv(m, 64));
+  if (ctw == 2) {
+    if (nmat == 1)
+      return afp4 ? launch_mt<1, 2, true>(p, mt, grid, stream) : launch_mt<1, 2, false>(p, mt, grid, stream);
+    return afp4 ? launch_mt<2, 2, true>(p, mt, grid, stream) : launch_mt<2, 2, false>(p, mt, grid, stream);
   }
-  return hipGetLastError();
+  if (nmat == 1)
+    return afp4 ? launch_mt<1, 1, true>(p, mt, grid, stream) : launch_mt<1, 1, false>(p, mt, grid, stream);
+  return afp4 ? launch_mt<2, 1, true>(p, mt, grid, stream) : launch_mt<2, 1, false>(p, mt, grid, stream);
 }
 
 }  // namespace nvfp4

@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void k_tiled(const uint16_t *__restrict__ x, i
     bf16x8 bf[2][4];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const float s0 = e4m3_to_f32(bs[ct] & 0xFFu);
-      const float s1 = e4m3_to_f32(bs[ct] >> 8);
+      const float s0 = e4m3_to_f32_sel<0>(bs[ct]);
+      const float s1 = e4m3_to_f32_sel<1>(bs[ct]);
       bf[ct][0] = dequant8(bw[ct].x, s0);
       bf[ct][1] = dequant8(bw[ct].y, s0);
       bf[ct][2] = dequant8(bw[ct].z, s1);

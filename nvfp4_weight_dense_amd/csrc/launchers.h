@@ -24,17 +24,28 @@ struct ActRef {
 };
 
 // Weight-streaming projection for few rows, nmat = 1 (y = x.W^T) or 2
-// (y = bf16(silu(bf16(x.W0^T)) * bf16(x.W1^T))).  `partial` must hold
-// stream_partial_floats(...) floats when that is non-zero.
+// (y = bf16(silu(bf16(x.W0^T)) * bf16(x.W1^T))).  With ksplit > 1,
+// `partial` must hold stream_partial_floats(...) floats and `counters`
+// stream_counter_words(...) words that are zero on entry (the kernel leaves
+// them zero).  The plan depends on (n, k) only.
 struct StreamPlan {
   int ksplit;           // workgroups along K
   int steps_per_split;  // 128-element K steps per split
+  int tiles;            // workgroups along N
 };
 StreamPlan stream_plan(int n, int k);
 size_t stream_partial_floats(const StreamPlan &pl, int nmat, int m, int n);
+size_t stream_counter_words(const StreamPlan &pl, int m);
 hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
                          const MatRef *w, void *y, float *partial,
-                         const StreamPlan &pl, hipStream_t stream);
+                         unsigned *counters, const StreamPlan &pl,
+                         hipStream_t stream);
+
+// Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above.
+// Eligible when K splits into at most 4 waves of register-resident granules.
+bool gemv_eligible(int m, int k);
+hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat,
+                       const MatRef *w, void *y, hipStream_t stream);
 
 // LDS-tiled MFMA projection for many rows (bf16 activations only).
 hipError_t launch_tiled(const void *x, int m, int k, int n, const MatRef &w,

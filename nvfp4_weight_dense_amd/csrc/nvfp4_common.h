@@ -24,16 +24,13 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int kWave = 64;
 
-// E4M3FN byte -> fp32.  Normal bytes move their 7 magnitude bits into the
-// fp32 exponent/mantissa fields and rebias the exponent (7 -> 127);
-// exponent-0 bytes are m * 2^-9; S.1111.111 is NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  uint32_t em = b & 0x7Fu;
-  float mag = em >= 8u ? __uint_as_float((em << 20) + (120u << 23))
-                       : (float)em * 0x1p-9f;
-  mag = em == 0x7Fu ? __builtin_nanf("") : mag;
-  return (b & 0x80u) ? -mag : mag;
+// E4M3FN byte -> fp32 with the gfx950 OCP fp8 conversion (exact for all 256
+// bytes, NaN for S.1111.111).  `sel` picks the byte of `w`.
+template <int sel>
+__device__ __forceinline__ float e4m3_to_f32_sel(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8(w, sel);
 }
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return e4m3_to_f32_sel<0>(b); }
 
 // Eight E2M1 codes (one 32-bit word, K order from the low nibble) times a
 // block scale -> the eight bf16 values of one MFMA operand fragment.  The
@@ -83,5 +80,24 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 }
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---- buffer loads -------------------------------------------------------------
+// A raw buffer resource over [base, base + bytes): loads at offsets beyond
+// the range return zero instead of touching memory, which handles ragged
+// rows, columns and K without branches.  Ranges are capped below 2^31 and
+// kOOB is an offset outside every range.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, size_t bytes) {
+  const uint32_t nrec = bytes < (size_t)0x7FFFFFFF ? (uint32_t)bytes : 0x7FFFFFFFu;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nrec,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
 
 }  // namespace nvfp4
