@@ -45,11 +45,20 @@ int fail(int code, const char *fmt, ...) {
 }
 
 enum class Force { Auto, Gemv, Stream, Tiled };
-enum class Path { Gemv, Stream, Tiled };
+enum class Path { Gemv, Stream, StreamLds, Tiled };
 
 const char *path_name(Path p) {
-  return p == Path::Gemv ? "gemv" : (p == Path::Stream ? "stream" : "tiled");
+  switch (p) {
+    case Path::Gemv: return "gemv";
+    case Path::Stream: return "stream";
+    case Path::StreamLds: return "stream-lds";
+    default: return "tiled";
+  }
 }
+
+// weight-streaming kernel for this many rows: plain up to 16, LDS-shared
+// activations from 17 to 64
+Path stream_kind(int m) { return m > 16 && m <= 64 ? Path::StreamLds : Path::Stream; }
 
 struct Config {
   int smallm_max_m = 64;
@@ -182,11 +191,11 @@ bool choose_path(int m, int k, Path *out) {
     case Force::Gemv:
       *out = Path::Gemv;
       return gemv_eligible(m, k);
-    case Force::Stream: *out = Path::Stream; return true;
+    case Force::Stream: *out = stream_kind(m); return true;
     case Force::Tiled: *out = Path::Tiled; return true;
     default:
       if (gemv_eligible(m, k)) *out = Path::Gemv;
-      else *out = m <= cfg().smallm_max_m ? Path::Stream : Path::Tiled;
+      else *out = m <= cfg().smallm_max_m ? stream_kind(m) : Path::Tiled;
       return true;
   }
 }
@@ -239,6 +248,8 @@ struct ProfileScope {
 size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
   if (path == Path::Gemv) return 0;
   if (path == Path::Stream) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+  if (path == Path::StreamLds)
+    return align256(4 * stream_lds_partial_floats(stream_lds_plan(n, k, nmat), nmat, m, n));
   return nmat == 2 ? 2 * align256((size_t)2 * m * n) : 0;
 }
 
@@ -246,6 +257,16 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
              void *scratch, Path path, hipStream_t s) {
   if (path == Path::Gemv)
     return hip_status(launch_gemv(a.x_bf16, m, k, n, nmat, w, y, s), "gemv projection launch");
+  if (path == Path::StreamLds) {
+    LdsPlan pl = stream_lds_plan(n, k, nmat);
+    unsigned *counters = nullptr;
+    if (pl.ksplit > 1) {
+      int rc = counters_get((size_t)pl.groups, &counters);
+      if (rc) return rc;
+    }
+    return hip_status(launch_stream_lds(a.x_bf16, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
+                      "weight-streaming (LDS) projection launch");
+  }
   if (path == Path::Stream) {
     StreamPlan pl = stream_plan(n, k);
     unsigned *counters = nullptr;

@@ -24,6 +24,8 @@
 //     sums; a butterfly that halves the list at each exchange leaves lane
 //     group l>>3 with column l>>3 summed over all 64 lanes (17 shuffles per
 //     batch), then the waves add their chunk sums in fixed wave order.
+#include <cstdlib>
+
 #include "launchers.h"
 #include "nvfp4_common.h"
 
@@ -32,7 +34,7 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kCB = 8;      // weight rows per batch
-constexpr int kMaxKW = 4;   // waves per workgroup
+constexpr int kMaxKW = 8;   // waves per workgroup
 
 struct GemvArgs {
   const void *x;          // bf16 [m][k]
@@ -46,8 +48,36 @@ struct GemvArgs {
 
 __device__ __forceinline__ bf16x2 u32_as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
+// value of lane (lane ^ O): ds_swizzle's xor mode within 32 lanes, a
+// bpermute across the halves
+template <int O>
+__device__ __forceinline__ float xor_shfl(float v) {
+  if constexpr (O >= 32) {
+    return __shfl_xor(v, O);
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                (O << 10) | 0x1F));
+  }
+}
+
+// One exchange of the halving butterfly over a list of 2H partial sums: a
+// lane keeps the half selected by its lane bit O and adds the partner's
+// copy of that half.  Afterwards entry i stands for entry i + H*(bit O).
+template <int H, int O>
+__device__ __forceinline__ void halve(float *a, int lane) {
+  const bool up = (lane & O) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float lo = a[i], hi = a[i + H];
+    const float send = up ? lo : hi;
+    const float keep = up ? hi : lo;
+    a[i] = keep + xor_shfl<O>(send);
+  }
+}
+
 template <int M, int NMAT, int G>
 __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
+  static_assert(G <= 3, "granules per lane");
   constexpr int NC = kCB / NMAT;  // output columns per batch
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -86,9 +116,10 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
 
   __shared__ float red[kMaxKW][kCB][M];
 
-  for (int b = blockIdx.x; b < p.nbatch; b += gridDim.x) {
+  // weight rows of batch b: 8 code granules and their scale pairs per lane
+  auto load_batch = [&](int b, uint4 (&cw)[kCB][G], uint32_t (&sw)[kCB][G]) {
     const int c0 = b * NC;
-    const int ncols = min(NC, p.n - c0);
+    const int ncols = b < p.nbatch ? min(NC, p.n - c0) : 0;
     __amdgpu_buffer_rsrc_t wres[NMAT], sres[NMAT];
     wres[0] = rsrc(p.codes0 + (size_t)c0 * kb2, (size_t)ncols * kb2);
     sres[0] = rsrc(p.scales0 + (size_t)c0 * kb16, (size_t)ncols * kb16);
@@ -96,8 +127,6 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
       wres[1] = rsrc(p.codes1 + (size_t)c0 * kb2, (size_t)ncols * kb2);
       sres[1] = rsrc(p.scales1 + (size_t)c0 * kb16, (size_t)ncols * kb16);
     }
-    uint4 cw[kCB][G];
-    uint32_t sw[kCB][G];
 #pragma unroll
     for (int i = 0; i < kCB; ++i) {
       const int mat = i % NMAT;
@@ -108,7 +137,11 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
         sw[i][g] = ld2(sres[mat], jok[g] ? col * kb16 + jg[g] * 2u : kOOB);
       }
     }
+  };
 
+  auto compute_batch = [&](int b, const uint4 (&cw)[kCB][G], const uint32_t (&sw)[kCB][G]) {
+    const int c0 = b * NC;
+    const int ncols = min(NC, p.n - c0);
     float v[kCB][M];
 #pragma unroll
     for (int i = 0; i < kCB; ++i) {
@@ -152,20 +185,14 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
       float a[kCB];
 #pragma unroll
       for (int i = 0; i < kCB; ++i) a[i] = v[i][r];
-#pragma unroll
-      for (int o = 32, h = kCB / 2; h >= 1; o >>= 1, h >>= 1) {
-        const bool up = (lane & o) != 0;
-#pragma unroll
-        for (int i = 0; i < h; ++i) {
-          const float send = up ? a[i] : a[i + h];
-          const float keep = up ? a[i + h] : a[i];
-          a[i] = keep + __shfl_xor(send, o);
-        }
-      }
+      static_assert(kCB == 8, "butterfly written for 8 entries");
+      halve<4, 32>(a, lane);
+      halve<2, 16>(a, lane);
+      halve<1, 8>(a, lane);
       float t = a[0];
-      t += __shfl_xor(t, 4);
-      t += __shfl_xor(t, 2);
-      t += __shfl_xor(t, 1);
+      t += xor_shfl<4>(t);
+      t += xor_shfl<2>(t);
+      t += xor_shfl<1>(t);
       tot[r] = t;
     }
 
@@ -185,7 +212,7 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
       }
       __syncthreads();
     }
-    if (wave != 0) continue;
+    if (wave != 0) return;
 
 #pragma unroll
     for (int r = 0; r < M; ++r) {
@@ -195,13 +222,38 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
         if ((lane & 7) == 0 && c < ncols)
           ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = (__bf16)(tot[r] * p.ts0);
       } else {
-        const float up = __shfl_xor(tot[r], 8);  // entry 2c+1 (up) next to 2c (gate)
+        const float up = xor_shfl<8>(tot[r]);  // entry 2c+1 (up) next to 2c (gate)
         const int c = lane >> 4;
         if ((lane & 15) == 0 && c < ncols)
           ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = swiglu_bf16(tot[r] * p.ts0, up * p.ts1);
       }
     }
+  };
+
+  // two register sets: the loads of the next batch are in flight while the
+  // current one is computed
+  uint4 cwA[kCB][G], cwB[kCB][G];
+  uint32_t swA[kCB][G], swB[kCB][G];
+  int b = blockIdx.x;
+  load_batch(b, cwA, swA);
+  for (; b < p.nbatch; b += 2 * gridDim.x) {
+    const int b1 = b + gridDim.x;
+    load_batch(b1, cwB, swB);
+    compute_batch(b, cwA, swA);
+    if (b1 >= p.nbatch) break;
+    const int b2 = b1 + gridDim.x;
+    load_batch(b2, cwA, swA);
+    compute_batch(b1, cwB, swB);
   }
+}
+
+int gemv_target_waves() {
+  static const int t = [] {
+    const char *v = getenv("NVFP4_GEMV_WAVES");
+    const int n = v ? atoi(v) : 0;
+    return n > 0 ? n : 4096;
+  }();
+  return t;
 }
 
 struct GemvShape {
@@ -210,18 +262,24 @@ struct GemvShape {
 
 int gmax_for_rows(int m) { return m == 1 ? 3 : (m == 2 ? 2 : 1); }
 
+// Fewest granules per lane (lightest registers, most waves in flight) that
+// keep the workgroup within kMaxKW waves.
 GemvShape gemv_shape(int m, int k) {
   const int gran = k / 32;
-  const int gmax = gmax_for_rows(m);
   GemvShape s;
-  s.kw = cdiv(gran, 64 * gmax);
-  s.g = cdiv(gran, 64 * s.kw);
+  s.g = cdiv(gran, 64 * kMaxKW);
+  if (s.g < 1) s.g = 1;
+  s.kw = cdiv(gran, 64 * s.g);
+  (void)m;
   return s;
 }
 
 template <int M, int NMAT, int G>
 hipError_t launch_g(const GemvArgs &p, int kw, hipStream_t st) {
-  const int grid = p.nbatch < 4096 ? p.nbatch : 4096;
+  // about 4096 waves in flight; every workgroup walks the same number of
+  // batches
+  const int per_wg = cdiv(p.nbatch * kw, gemv_target_waves());
+  const int grid = cdiv(p.nbatch, per_wg);
   hipLaunchKernelGGL((k_gemv<M, NMAT, G>), dim3(grid), dim3(64 * kw), 0, st, p);
   return hipGetLastError();
 }

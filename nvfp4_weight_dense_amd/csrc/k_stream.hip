@@ -148,9 +148,10 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
           bf[i][ct][2] = dequant8(bw[u][i][ct].z, s1);
           bf[i][ct][3] = dequant8(bw[u][i][ct].w, s1);
         }
+      bf16x8 afr[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        bf16x8 af[4];
+        bf16x8 (&af)[4] = afr[mt];
         if constexpr (AFP4) {
           const float s0 = e4m3_to_f32_sel<0>(asc[u][mt]);
           const float s1 = e4m3_to_f32_sel<1>(asc[u][mt]);
@@ -162,15 +163,18 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) af[q] = as_bf16x8(aw[u][mt][q]);
         }
+      }
+      // K sub-step outermost: consecutive MFMAs update different accumulators
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < NMAT; ++i)
 #pragma unroll
             for (int ct = 0; ct < CTW; ++ct)
               acc[i][ct][mt] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
-      }
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
     }
   }
 
@@ -203,49 +207,57 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
     }
   if (wave != 0) return;
 
-  const size_t mn = (size_t)p.m * p.n;
   if (p.ksplit > 1) {
-    // publish this split's partial tile, then count arrivals
+    // this workgroup's partial tiles: [NMAT][ksplit][CTW][16*MT rows][16 columns]
+    constexpr int kTile = 16 * MT * 16;
+    const size_t wg = (size_t)blockIdx.z * gridDim.x + blockIdx.x;
+    const __amdgpu_buffer_rsrc_t pres = rsrc(p.partial + wg * NMAT * p.ksplit * CTW * kTile,
+                                             (size_t)NMAT * p.ksplit * CTW * kTile * 4);
+    auto poff = [&](int i, int sp, int ct, int mt, int e) -> uint32_t {
+      const uint32_t r = mt * 16 + 4 * g + e;
+      return ((((uint32_t)(i * p.ksplit + sp) * CTW + ct) * kTile) + r * 16u + c16) * 4u;
+    };
 #pragma unroll
-    for (int ct = 0; ct < CTW; ++ct) {
-      const int col = col0 + ct * 16 + c16;
+    for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = row0 + mt * 16 + 4 * g + e;
-          if (r < p.m && col < p.n)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int i = 0; i < NMAT; ++i)
-              p.partial[((size_t)i * p.ksplit + blockIdx.y) * mn + (size_t)r * p.n + col] =
-                  acc[i][ct][mt][e];
-        }
-    }
-    unsigned *cnt = p.counters + (size_t)blockIdx.z * gridDim.x + blockIdx.x;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          for (int i = 0; i < NMAT; ++i)
+            st_coherent(pres, poff(i, blockIdx.y, ct, mt, e), acc[i][ct][mt][e]);
+    unsigned *cnt = p.counters + wg;
+    wait_all_memory();
     unsigned old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0);
     if (old != (unsigned)(p.ksplit - 1)) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // last arrival: sum the partials in split order
+    // split order outermost; all of one split's loads are in flight together
 #pragma unroll
-    for (int ct = 0; ct < CTW; ++ct) {
-      const int col = col0 + ct * 16 + c16;
+    for (int i = 0; i < NMAT; ++i)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = row0 + mt * 16 + 4 * g + e;
-          if (r < p.m && col < p.n)
+        for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < p.ksplit; ++sp) {
+      float v[NMAT][CTW][MT][4];
 #pragma unroll
-            for (int i = 0; i < NMAT; ++i) {
-              float s = 0.f;
-              for (int sp = 0; sp < p.ksplit; ++sp)
-                s += p.partial[((size_t)i * p.ksplit + sp) * mn + (size_t)r * p.n + col];
-              acc[i][ct][mt][e] = s;
-            }
-        }
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i) v[i][ct][mt][e] = ld_coherent(pres, poff(i, sp, ct, mt, e));
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i) acc[i][ct][mt][e] += v[i][ct][mt][e];
     }
     if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -321,7 +333,12 @@ StreamPlan stream_plan(int n, int k) {
 }
 
 size_t stream_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
-  return pl.ksplit > 1 ? (size_t)nmat * pl.ksplit * m * n : 0;
+  // per workgroup: [nmat][ksplit][CTW][16*MT][16]
+  const int mt = m >= 64 ? 4 : cdiv(m, 16);
+  (void)n;
+  return pl.ksplit > 1
+             ? (size_t)pl.tiles * cdiv(m, 64) * nmat * pl.ksplit * stream_ctw(n) * 16 * mt * 16
+             : 0;
 }
 
 size_t stream_counter_words(const StreamPlan &pl, int m) {

@@ -41,6 +41,22 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
                          unsigned *counters, const StreamPlan &pl,
                          hipStream_t stream);
 
+// Weight-streaming projection for 17..64 rows (bf16 activations) with the
+// activation chunk shared through LDS; partial/counter rules as above, with
+// one counter per column group (`groups` words).
+struct LdsPlan {
+  int ctw;              // 16-column tiles per wave
+  int groups;           // workgroups along N
+  int ksplit;
+  int steps_per_split;
+};
+LdsPlan stream_lds_plan(int n, int k, int nmat);
+size_t stream_lds_partial_floats(const LdsPlan &pl, int nmat, int m, int n);
+hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat,
+                             const MatRef *w, void *y, float *partial,
+                             unsigned *counters, const LdsPlan &pl,
+                             hipStream_t stream);
+
 // Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above.
 // Eligible when K splits into at most 4 waves of register-resident granules.
 bool gemv_eligible(int m, int k);

@@ -100,4 +100,26 @@ __device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
 
+// ---- split-K partials shared between workgroups on different XCDs ----------
+// Partials are written and read with the system-coherent cache policy
+// (sc0 sc1): those accesses bypass the XCDs' non-coherent L2 state, so the
+// hand-off needs no cache-wide writeback or invalidate (which an agent-scope
+// fence would emit), only the completion of the writer's stores before it
+// bumps the arrival counter.  The loads are ordinary (not atomic), so a
+// lane's loads of all splits are in flight together.
+constexpr int kCoherent = 17;  // sc0 | sc1
+
+__device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent));
+}
+// All of this wave's memory operations have completed.
+__device__ __forceinline__ void wait_all_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace nvfp4
