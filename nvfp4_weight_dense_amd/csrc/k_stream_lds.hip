@@ -10,9 +10,10 @@
 //     each activation chunk is fetched from L2 once per workgroup and read
 //     by every wave from LDS; one activation fragment feeds NMAT MFMAs.
 //
-//   * step t (64 K): the workgroup loads rows [0, 32*MT) x K [64t, 64t+64) of
-//     the activations into one of two LDS buffers (rows padded by 16 bytes);
-//     each lane prefetches its weight codes/scales two steps ahead.
+//   * step t (64 K): rows [0, 32*MT) x K [64t, 64t+64) of the activations sit
+//     in one of three LDS slots (rows padded by 16 bytes); the workgroup
+//     loads them two steps ahead, and each lane prefetches its weight
+//     codes/scales six steps ahead.
 //   * lane (c = lane%32, h = lane/32) holds, for weight row col0+c, the 32
 //     codes at K offset 32h of the step: four bf16 B fragments after
 //     in-register dequantization; MFMA j of the step sums K offsets
@@ -23,6 +24,8 @@
 //   * Workgroups that run together start their K range at different steps
 //     (a rotation by the column-group index), so they do not all read the
 //     same activation chunk at the same moment.
+#include <type_traits>
+
 #include "launchers.h"
 #include "nvfp4_common.h"
 
@@ -49,7 +52,7 @@ struct LdsArgs {
 template <int MT, int NMAT>
 __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
   constexpr int kRows = 32 * MT;
-  __shared__ __attribute__((aligned(16))) uint8_t abuf[2][kRows * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf[3][kRows * kRowBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -83,8 +86,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
   constexpr int kPieces = kRows * (kStep * 2 / 16);
   constexpr int kPerThread = kPieces / (kWaves * 64);
   static_assert(kPerThread * kWaves * 64 == kPieces, "chunk split");
-  uint4 areg[kPerThread];
-  auto load_a = [&](int tl) {
+  uint4 areg[2][kPerThread];
+  auto load_a = [&](int tl, uint4 (&a)[kPerThread]) {
     const int t = kstep(tl);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
@@ -92,14 +95,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
       const uint32_t r = (uint32_t)(piece >> 3);
       const uint32_t kk = (uint32_t)t * kStep + 8u * (uint32_t)(piece & 7);
       const bool ok = tl < len && kk < (uint32_t)k && r < (uint32_t)p.m;
-      areg[i] = ld16(xres, ok ? (r * (uint32_t)k + kk) * 2u : kOOB);
+      a[i] = ld16(xres, ok ? (r * (uint32_t)k + kk) * 2u : kOOB);
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int buf, const uint4 (&a)[kPerThread]) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int piece = tid + kWaves * 64 * i;
-      *(uint4 *)&abuf[buf][(piece >> 3) * kRowBytes + 16 * (piece & 7)] = areg[i];
+      *(uint4 *)&abuf[buf][(piece >> 3) * kRowBytes + 16 * (piece & 7)] = a[i];
     }
   };
   auto load_b = [&](int tl, uint4 (&w)[NMAT], uint32_t (&s)[NMAT]) {
@@ -121,48 +124,56 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][mt][e] = 0.f;
 
-  uint4 bw[3][NMAT];
-  uint32_t bs[3][NMAT];
-  load_a(0);
-  load_b(0, bw[0], bs[0]);
-  load_b(1, bw[1], bs[1]);
-  store_a(0);
+  // Pipeline: weight codes are prefetched kDB steps ahead into a register
+  // ring, activation chunks two steps ahead into registers and then into a
+  // three-slot LDS ring.  All slot indices are compile-time (the loop is
+  // unrolled by six), so the compiler's own load waits do the pipelining.
+  constexpr int kDB = 6;
+  uint4 bw[kDB][NMAT];
+  uint32_t bs[kDB][NMAT];
+#pragma unroll
+  for (int d = 0; d < kDB; ++d) load_b(d, bw[d], bs[d]);
+  load_a(0, areg[0]);
+  load_a(1, areg[1]);
+  store_a(0, areg[0]);
   __syncthreads();
 
-  // slot: register set of step tl's codes (mod 3)
-  auto step = [&](int tl, int slot) {
-    const int cur = tl & 1;
-    const bool more = tl + 1 < len;
-    if (more) load_a(tl + 1);
-    load_b(tl + 2, bw[(slot + 2) % 3], bs[(slot + 2) % 3]);
+  auto step = [&](int tl, auto slot_c) {
+    constexpr int sb = decltype(slot_c)::value;  // tl % 6
+    constexpr int sa = sb % 2, sl = sb % 3;
     bf16x8 bf[NMAT][4];
 #pragma unroll
     for (int i = 0; i < NMAT; ++i) {
-      const float s0 = e4m3_to_f32_sel<0>(bs[slot][i]);
-      const float s1 = e4m3_to_f32_sel<1>(bs[slot][i]);
-      bf[i][0] = dequant8(bw[slot][i].x, s0);
-      bf[i][1] = dequant8(bw[slot][i].y, s0);
-      bf[i][2] = dequant8(bw[slot][i].z, s1);
-      bf[i][3] = dequant8(bw[slot][i].w, s1);
+      const float s0 = e4m3_to_f32_sel<0>(bs[sb][i]);
+      const float s1 = e4m3_to_f32_sel<1>(bs[sb][i]);
+      bf[i][0] = dequant8(bw[sb][i].x, s0);
+      bf[i][1] = dequant8(bw[sb][i].y, s0);
+      bf[i][2] = dequant8(bw[sb][i].z, s1);
+      bf[i][3] = dequant8(bw[sb][i].w, s1);
     }
+    load_b(tl + kDB, bw[sb], bs[sb]);
+    load_a(tl + 2, areg[sa]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 af = as_bf16x8(
-            *(const uint4 *)&abuf[cur][(mt * 32 + c32) * kRowBytes + 2 * (32 * h + 8 * j)]);
+            *(const uint4 *)&abuf[sl][(mt * 32 + c32) * kRowBytes + 2 * (32 * h + 8 * j)]);
 #pragma unroll
         for (int i = 0; i < NMAT; ++i)
           acc[i][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[i][j], acc[i][mt], 0, 0, 0);
       }
     }
-    if (more) store_a(cur ^ 1);
+    if (tl + 1 < len) store_a((sl + 1) % 3, areg[sa ^ 1]);
     __syncthreads();
   };
-  for (int tl = 0; tl < len; tl += 3) {
-    step(tl, 0);
-    if (tl + 1 < len) step(tl + 1, 1);
-    if (tl + 2 < len) step(tl + 2, 2);
+  for (int tl = 0; tl < len; tl += kDB) {
+    step(tl, std::integral_constant<int, 0>{});
+    if (tl + 1 < len) step(tl + 1, std::integral_constant<int, 1>{});
+    if (tl + 2 < len) step(tl + 2, std::integral_constant<int, 2>{});
+    if (tl + 3 < len) step(tl + 3, std::integral_constant<int, 3>{});
+    if (tl + 4 < len) step(tl + 4, std::integral_constant<int, 4>{});
+    if (tl + 5 < len) step(tl + 5, std::integral_constant<int, 5>{});
   }
 
   // output element of lane, register e, row tile mt:
