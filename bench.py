@@ -14,8 +14,8 @@ Timing: hipEvents (torch.cuda.Event) recorded on the stream the library
 launches on, around exactly K back-to-back steps after W warm-up steps,
 bracketed by device synchronizations.
 
-roofline: the dominant kernel is the fused gate+up+silu weight-streaming
-kernel (two thirds of the decode FFN's bytes); its average launch duration
+roofline: the dominant kernel is the fused gate+up+silu single-row kernel
+k_gemv<1, 2, 1> (two thirds of the decode FFN's bytes); its average launch duration
 comes from K back-to-back launches of nvfp4_gate_up_silu_w4a16 (one kernel
 per call at this shape) between events on the same stream.  Algorithmic
 bytes per launch = both weight matrices (codes + E4M3 scales) + x + act.
@@ -41,8 +41,10 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 REPLICA_BYTES = 1 << 30
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-DOMINANT_KERNEL_SRC = os.path.join(ROOT, "nvfp4_weight_dense_amd", "csrc", "k_stream.hip")
-TRAFFIC_FILE = os.path.join(PROFILE_DIR, "gate_up_silu_decode_traffic.txt")
+DOMINANT_KERNEL_SRC = os.path.join(ROOT, "nvfp4_weight_dense_amd", "csrc", "k_gemv.hip")
+DOMINANT_KERNEL = "k_gemv<1, 2, 1>"
+TRAFFIC_FILE = os.path.join(PROFILE_DIR, "k_gemv_gate_up_silu_decode_traffic.txt")
+COPY_BYTES = 1 << 28
 
 
 def weight_bytes(w) -> int:
@@ -129,7 +131,7 @@ def measure_dominant_kernel(ctx, steps, warmup):
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
         "traffic": _traffic_per_launch(),
-        "kernel": "k_stream<1,2,false> (nvfp4_gate_up_silu_w4a16, decode shape)",
+        "kernel": DOMINANT_KERNEL + " (nvfp4_gate_up_silu_w4a16, m=1, k=4096, n=12288)",
         "avg_launch_us": ms * 1e3,
         "algorithmic_bytes": algo,
     }
@@ -159,6 +161,33 @@ def _traffic_per_launch():
         return float(fields["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def traffic_run(steps):
+    """Launch pattern for the rocprofv3 FETCH_SIZE / WRITE_SIZE passes: `steps`
+    launches of the dominant kernel over rotating cold replicas, then `steps`
+    plain device copies of COPY_BYTES, whose counter readings calibrate the
+    counters against a transfer of known size."""
+    import torch
+
+    import nvfp4_weight_dense_amd as nv
+
+    _, ctx = measure_ffn("decode", 1, 1)
+    xd, reps, stream = ctx["x"], ctx["weights"], ctx["stream"]
+    act = torch.empty((xd.shape[0], reps[0][0].codes.shape[0]), dtype=torch.bfloat16,
+                      device=xd.device)
+    for i in range(steps):
+        r = reps[i % len(reps)]
+        nv.nvfp4_gate_up_silu_w4a16(xd, r[0], r[1], act=act, stream=stream)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=xd.device)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_run": DOMINANT_KERNEL, "launches": steps,
+                      "copy_bytes": COPY_BYTES, "source_hash": _kernel_source_hash()}),
+          flush=True)
 
 
 def cpu_baseline(seconds=10.0, threads=16):
@@ -199,6 +228,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true",
                     help="time only the decode workload (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="only launch the dominant kernel and a calibration copy "
+                         "(for rocprofv3 --pmc passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -213,6 +245,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     nv.load_library()  # raises if the HIP library is not built
+    if args.traffic_run:
+        traffic_run(args.steps)
+        return
 
     head, ctx = measure_ffn("decode", args.steps, args.warmup)
     roof = measure_dominant_kernel(ctx, args.steps, args.warmup)
