@@ -195,7 +195,7 @@ bool choose_path(int m, int k, Path *out) {
     case Force::Tiled: *out = Path::Tiled; return true;
     default:
       if (gemv_eligible(m, k)) *out = Path::Gemv;
-      else *out = m <= cfg().smallm_max_m ? stream_kind(m) : Path::Tiled;
+      else *out = m <= cfg().smallm_max_m ? stream_kind(m) : Path::StreamLds;
       return true;
   }
 }
@@ -249,7 +249,7 @@ size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
   if (path == Path::Gemv) return 0;
   if (path == Path::Stream) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
   if (path == Path::StreamLds)
-    return align256(4 * stream_lds_partial_floats(stream_lds_plan(n, k, nmat), nmat, m, n));
+    return align256(4 * stream_lds_partial_floats(stream_lds_plan(m, n, k, nmat), nmat, m, n));
   return nmat == 2 ? 2 * align256((size_t)2 * m * n) : 0;
 }
 
@@ -258,10 +258,10 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
   if (path == Path::Gemv)
     return hip_status(launch_gemv(a.x_bf16, m, k, n, nmat, w, y, s), "gemv projection launch");
   if (path == Path::StreamLds) {
-    LdsPlan pl = stream_lds_plan(n, k, nmat);
+    LdsPlan pl = stream_lds_plan(m, n, k, nmat);
     unsigned *counters = nullptr;
     if (pl.ksplit > 1) {
-      int rc = counters_get((size_t)pl.groups, &counters);
+      int rc = counters_get(stream_lds_counter_words(pl), &counters);
       if (rc) return rc;
     }
     return hip_status(launch_stream_lds(a.x_bf16, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),

@@ -24,6 +24,7 @@
 //   * Workgroups that run together start their K range at different steps
 //     (a rotation by the column-group index), so they do not all read the
 //     same activation chunk at the same moment.
+#include <cmath>
 #include <type_traits>
 
 #include "launchers.h"
@@ -47,6 +48,8 @@ struct LdsArgs {
   float *partial;       // [nmat][ksplit][m][n]
   unsigned *counters;   // [gridDim.x], zero between calls
   int ksplit, steps_per_split;
+  int row_blocks;       // 32*MT-row blocks along m
+  int rotate;           // stagger the K start of column groups
 };
 
 template <int MT, int NMAT>
@@ -66,9 +69,17 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
   const int s_begin = blockIdx.y * p.steps_per_split;
   const int s_end = min(nsteps, s_begin + p.steps_per_split);
   const int len = s_end - s_begin;
-  const int rot = len > 0 ? (int)(blockIdx.x % (unsigned)len) : 0;
+  // blockIdx.x = row block + row_blocks * column group: consecutive
+  // workgroups (dealt round-robin to the XCDs) take different row blocks
+  // of the same columns, so with 8 row blocks each XCD's L2 keeps one
+  // activation row block for the whole launch.
+  const int rb = (int)(blockIdx.x % (unsigned)p.row_blocks);
+  const int cg = (int)(blockIdx.x / (unsigned)p.row_blocks);
+  const int row0 = rb * kRows;
+  const int rows = min(kRows, p.m - row0);
+  const int rot = (p.rotate && len > 0) ? cg % len : 0;
   auto kstep = [&](int tl) { int q = tl + rot; return s_begin + (q >= len ? q - len : q); };
-  const int col0 = (blockIdx.x * kWaves + wave) * 32;  // this wave's columns
+  const int col0 = (cg * kWaves + wave) * 32;  // this wave's columns
 
   const int ncols = max(0, min(32, p.n - col0));
   const size_t cbase = (size_t)min(col0, p.n);
@@ -79,7 +90,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
     wc[1] = rsrc(p.codes1 + cbase * kb2, (size_t)ncols * kb2);
     ws[1] = rsrc(p.scales1 + cbase * kb16, (size_t)ncols * kb16);
   }
-  const __amdgpu_buffer_rsrc_t xres = rsrc(p.x, (size_t)p.m * k * 2);
+  const __amdgpu_buffer_rsrc_t xres =
+      rsrc((const uint8_t *)p.x + (size_t)row0 * k * 2, (size_t)rows * k * 2);
 
   // cooperative activation chunk: 16-byte pieces (row = piece / 8, byte
   // offset 16 * (piece % 8)); thread tid moves pieces tid + 256 i
@@ -94,7 +106,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
       const int piece = tid + kWaves * 64 * i;
       const uint32_t r = (uint32_t)(piece >> 3);
       const uint32_t kk = (uint32_t)t * kStep + 8u * (uint32_t)(piece & 7);
-      const bool ok = tl < len && kk < (uint32_t)k && r < (uint32_t)p.m;
+      const bool ok = tl < len && kk < (uint32_t)k && r < (uint32_t)rows;
       a[i] = ld16(xres, ok ? (r * (uint32_t)k + kk) * 2u : kOOB);
     }
   };
@@ -128,7 +140,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
   // ring, activation chunks two steps ahead into registers and then into a
   // three-slot LDS ring.  All slot indices are compile-time (the loop is
   // unrolled by six), so the compiler's own load waits do the pipelining.
-  constexpr int kDB = 6;
+  // (six steps cover HBM latency for few rows; with many rows a step is long
+  // and the weights mostly come from L2, so three are enough)
+  constexpr int kDB = MT >= 4 ? 3 : 6;
+  static_assert(6 % kDB == 0, "ring slots must divide the unroll");
   uint4 bw[kDB][NMAT];
   uint32_t bs[kDB][NMAT];
 #pragma unroll
@@ -139,8 +154,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
   __syncthreads();
 
   auto step = [&](int tl, auto slot_c) {
-    constexpr int sb = decltype(slot_c)::value;  // tl % 6
-    constexpr int sa = sb % 2, sl = sb % 3;
+    constexpr int s6 = decltype(slot_c)::value;  // tl % 6
+    constexpr int sb = s6 % kDB, sa = s6 % 2, sl = s6 % 3;
     bf16x8 bf[NMAT][4];
 #pragma unroll
     for (int i = 0; i < NMAT; ++i) {
@@ -167,7 +182,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
     if (tl + 1 < len) store_a((sl + 1) % 3, areg[sa ^ 1]);
     __syncthreads();
   };
-  for (int tl = 0; tl < len; tl += kDB) {
+  for (int tl = 0; tl < len; tl += 6) {
     step(tl, std::integral_constant<int, 0>{});
     if (tl + 1 < len) step(tl + 1, std::integral_constant<int, 1>{});
     if (tl + 2 < len) step(tl + 2, std::integral_constant<int, 2>{});
@@ -212,23 +227,28 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][mt][e] = 0.f;
+    // the loads of one split (up to four tiles at a time) are in flight together
+    constexpr int kChunk = NMAT * MT <= 4 ? NMAT * MT : 4;
     for (int sp = 0; sp < p.ksplit; ++sp) {
-      float v[NMAT][MT][16];
 #pragma unroll
-      for (int i = 0; i < NMAT; ++i)
+      for (int c0 = 0; c0 < NMAT * MT; c0 += kChunk) {
+        float v[kChunk][16];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int c = 0; c < kChunk; ++c) {
+          const int i = (c0 + c) / MT, mt = (c0 + c) % MT;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const uint32_t r = mt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-            v[i][mt][e] = ld_coherent(pres, (((uint32_t)(i * p.ksplit + sp) * kTile) + r * 32u + c32) * 4u);
+            v[c][e] = ld_coherent(pres, (((uint32_t)(i * p.ksplit + sp) * kTile) + r * 32u + c32) * 4u);
           }
+        }
 #pragma unroll
-      for (int i = 0; i < NMAT; ++i)
+        for (int c = 0; c < kChunk; ++c) {
+          const int i = (c0 + c) / MT, mt = (c0 + c) % MT;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][mt][e] += v[i][mt][e];
+          for (int e = 0; e < 16; ++e) acc[i][mt][e] += v[c][e];
+        }
+      }
     }
     if (tid == 0) __hip_atomic_store(&p.counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -239,13 +259,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_stream_lds(LdsArgs p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = mt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (r >= p.m) continue;
+      if (r >= rows) continue;
       __bf16 out;
       if constexpr (NMAT > 1)
         out = swiglu_bf16(acc[0][mt][e] * p.ts0, acc[1][mt][e] * p.ts1);
       else
         out = (__bf16)(acc[0][mt][e] * p.ts0);
-      ((__bf16 *)p.y)[(size_t)r * p.n + col] = out;
+      ((__bf16 *)p.y)[(size_t)(row0 + r) * p.n + col] = out;
     }
 }
 
@@ -257,28 +277,50 @@ hipError_t launch2(const LdsArgs &p, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-LdsPlan stream_lds_plan(int n, int k, int nmat) {
+int lds_row_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : 8; }
+
+LdsPlan stream_lds_plan(int m, int n, int k, int nmat) {
   LdsPlan pl;
-  pl.ctw = 2;  // 32-column tile per wave
+  pl.mt = lds_row_tiles(m);
+  pl.row_blocks = cdiv(m, 32 * pl.mt);
   pl.groups = cdiv(n, kWaves * 32);
   const int nsteps = cdiv(k, kStep);
-  // enough workgroups to cover the chip twice; the split depends on (n, k)
-  int ksplit = cdiv(512, pl.groups);
+  const int tiles = pl.groups * pl.row_blocks;
+  int ksplit = 1;
+  if (pl.row_blocks == 1) {
+    // few rows: enough workgroups to cover the chip twice; the split then
+    // depends on (n, k) only
+    ksplit = cdiv(512, pl.groups);
+  } else if (nmat == 1) {
+    // many rows: one workgroup per CU; split K only to even out the last
+    // round (partials cost 4 bytes per output and split)
+    const int slots = 256;
+    double best = 0;
+    for (int ks = 1; ks <= 4; ++ks) {
+      const double rounds = (double)tiles * ks / slots;
+      const double eff = rounds / std::ceil(rounds);
+      if (eff > best + 0.05) { best = eff; ksplit = ks; }
+    }
+  }
   const int cap = nsteps / 4 > 0 ? nsteps / 4 : 1;  // at least four steps per split
   if (ksplit > cap) ksplit = cap;
   if (ksplit < 1) ksplit = 1;
-  (void)nmat;
   pl.steps_per_split = cdiv(nsteps, ksplit);
   pl.ksplit = cdiv(nsteps, pl.steps_per_split);
+  pl.rotate = pl.row_blocks == 1;
   return pl;
 }
 
 size_t stream_lds_partial_floats(const LdsPlan &pl, int nmat, int m, int n) {
-  // per wave: [nmat][ksplit][32*MT][32]
-  const int mt = m > 32 ? 2 : 1;
+  // per wave: [nmat][ksplit][32*mt][32]
+  (void)m;
   (void)n;
-  return pl.ksplit > 1 ? (size_t)pl.groups * kWaves * nmat * pl.ksplit * 32 * mt * 32 : 0;
+  return pl.ksplit > 1
+             ? (size_t)pl.groups * pl.row_blocks * kWaves * nmat * pl.ksplit * 32 * pl.mt * 32
+             : 0;
 }
+
+size_t stream_lds_counter_words(const LdsPlan &pl) { return (size_t)pl.groups * pl.row_blocks; }
 
 hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat, const MatRef *w,
                              void *y, float *partial, unsigned *counters, const LdsPlan &pl,
@@ -299,10 +341,23 @@ hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat, const
   p.counters = counters;
   p.ksplit = pl.ksplit;
   p.steps_per_split = pl.steps_per_split;
-  dim3 grid(pl.groups, pl.ksplit);
-  const bool two = m > 32;
-  if (nmat == 2) return two ? launch2<2, 2>(p, grid, stream) : launch2<1, 2>(p, grid, stream);
-  return two ? launch2<2, 1>(p, grid, stream) : launch2<1, 1>(p, grid, stream);
+  p.row_blocks = pl.row_blocks;
+  p.rotate = pl.rotate;
+  dim3 grid(pl.groups * pl.row_blocks, pl.ksplit);
+  if (nmat == 2) {
+    switch (pl.mt) {
+      case 1: return launch2<1, 2>(p, grid, stream);
+      case 2: return launch2<2, 2>(p, grid, stream);
+      case 4: return launch2<4, 2>(p, grid, stream);
+      default: return launch2<8, 2>(p, grid, stream);
+    }
+  }
+  switch (pl.mt) {
+    case 1: return launch2<1, 1>(p, grid, stream);
+    case 2: return launch2<2, 1>(p, grid, stream);
+    case 4: return launch2<4, 1>(p, grid, stream);
+    default: return launch2<8, 1>(p, grid, stream);
+  }
 }
 
 }  // namespace nvfp4

@@ -41,17 +41,23 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
                          unsigned *counters, const StreamPlan &pl,
                          hipStream_t stream);
 
-// Weight-streaming projection for 17..64 rows (bf16 activations) with the
-// activation chunk shared through LDS; partial/counter rules as above, with
-// one counter per column group (`groups` words).
+// LDS-shared projection (bf16 activations): a workgroup owns 32*mt rows
+// and 128 columns; its four waves share each 64-element activation chunk
+// through LDS.  Serves 17..64 rows (mt 1 or 2, one row block) and the
+// many-row regime (mt 8).  Partial/counter rules as above, with
+// stream_lds_counter_words(...) counters.
 struct LdsPlan {
-  int ctw;              // 16-column tiles per wave
+  int mt;               // 32-row tiles per workgroup
+  int row_blocks;       // workgroups along m
   int groups;           // workgroups along N
   int ksplit;
   int steps_per_split;
+  int rotate;           // stagger K start per column group (one row block)
 };
-LdsPlan stream_lds_plan(int n, int k, int nmat);
+int lds_row_tiles(int m);
+LdsPlan stream_lds_plan(int m, int n, int k, int nmat);
 size_t stream_lds_partial_floats(const LdsPlan &pl, int nmat, int m, int n);
+size_t stream_lds_counter_words(const LdsPlan &pl);
 hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat,
                              const MatRef *w, void *y, float *partial,
                              unsigned *counters, const LdsPlan &pl,
