@@ -52,7 +52,7 @@ extern "C" {
 /* status codes */
 #define NVFP4_OK 0
 #define NVFP4_EINVAL (-1) /* null/misaligned pointer, negative m, bad count */
-#define NVFP4_ESHAPE (-2) /* n or k <= 0, k % 32 != 0, inconsistent shapes */
+#define NVFP4_ESHAPE (-2) /* n or k <= 0 or > 2^21, k % 32 != 0, m > 4194240, inconsistent shapes */
 #define NVFP4_ENOMEM (-3) /* the scratch arena could not grow */
 #define NVFP4_EHIP (-4)   /* a HIP launch or runtime call failed */
 

@@ -44,14 +44,15 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
-enum class Force { Auto, Gemv, Stream, Tiled };
-enum class Path { Gemv, Stream, StreamLds, Tiled };
+enum class Force { Auto, Gemv, Stream, Tiled, Prefill };
+enum class Path { Gemv, Stream, StreamLds, Tiled, Prefill };
 
 const char *path_name(Path p) {
   switch (p) {
     case Path::Gemv: return "gemv";
     case Path::Stream: return "stream";
     case Path::StreamLds: return "stream-lds";
+    case Path::Prefill: return "prefill";
     default: return "tiled";
   }
 }
@@ -76,6 +77,7 @@ const Config &cfg() {
       if (!strcmp(v, "gemv")) c.force = Force::Gemv;
       if (!strcmp(v, "stream")) c.force = Force::Stream;
       if (!strcmp(v, "tiled")) c.force = Force::Tiled;
+      if (!strcmp(v, "prefill")) c.force = Force::Prefill;
     }
     if (const char *v = getenv("NVFP4_PROFILE")) c.profile = !strcmp(v, "1");
     if (const char *v = getenv("NVFP4_LOG")) c.log = !strcmp(v, "1");
@@ -163,12 +165,16 @@ int counters_get(size_t words, unsigned **out) {
 
 bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 
+constexpr int kMaxDim = 1 << 21;
+
 int check_weight(const nvfp4_weight *w, const char *name) {
   if (!w) return fail(NVFP4_EINVAL, "%s: null weight descriptor", name);
   if (!w->codes || !w->scales) return fail(NVFP4_EINVAL, "%s: null codes or scales pointer", name);
   if (w->n <= 0 || w->k <= 0) return fail(NVFP4_ESHAPE, "%s: n=%d k=%d must be positive", name, w->n, w->k);
   if (w->k % 32 != 0) return fail(NVFP4_ESHAPE, "%s: k=%d is not a multiple of 32", name, w->k);
-  if (w->k > 4194304) return fail(NVFP4_ESHAPE, "%s: k=%d exceeds 4194304", name, w->k);
+  // (keeps every buffer range and 32-bit offset of the kernels below 2^31)
+  if (w->k > kMaxDim || w->n > kMaxDim)
+    return fail(NVFP4_ESHAPE, "%s: n=%d k=%d exceed %d", name, w->n, w->k, kMaxDim);
   if (misaligned(w->codes) || misaligned(w->scales))
     return fail(NVFP4_EINVAL, "%s: codes/scales must be 16-byte aligned", name);
   return NVFP4_OK;
@@ -193,9 +199,10 @@ bool choose_path(int m, int k, Path *out) {
       return gemv_eligible(m, k);
     case Force::Stream: *out = stream_kind(m); return true;
     case Force::Tiled: *out = Path::Tiled; return true;
+    case Force::Prefill: *out = Path::Prefill; return true;
     default:
       if (gemv_eligible(m, k)) *out = Path::Gemv;
-      else *out = m <= cfg().smallm_max_m ? stream_kind(m) : Path::StreamLds;
+      else *out = m <= cfg().smallm_max_m ? stream_kind(m) : Path::Prefill;
       return true;
   }
 }
@@ -248,6 +255,7 @@ struct ProfileScope {
 size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
   if (path == Path::Gemv) return 0;
   if (path == Path::Stream) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+  if (path == Path::Prefill) return align256(4 * prefill_partial_floats(prefill_plan(m, n, k, nmat)));
   if (path == Path::StreamLds)
     return align256(4 * stream_lds_partial_floats(stream_lds_plan(m, n, k, nmat), nmat, m, n));
   return nmat == 2 ? 2 * align256((size_t)2 * m * n) : 0;
@@ -257,6 +265,16 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
              void *scratch, Path path, hipStream_t s) {
   if (path == Path::Gemv)
     return hip_status(launch_gemv(a.x_bf16, m, k, n, nmat, w, y, s), "gemv projection launch");
+  if (path == Path::Prefill) {
+    PrefillPlan pl = prefill_plan(m, n, k, nmat);
+    unsigned *counters = nullptr;
+    if (pl.ksplit > 1) {
+      int rc = counters_get(prefill_counter_words(pl), &counters);
+      if (rc) return rc;
+    }
+    return hip_status(launch_prefill(a.x_bf16, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
+                      "many-row projection launch");
+  }
   if (path == Path::StreamLds) {
     LdsPlan pl = stream_lds_plan(m, n, k, nmat);
     unsigned *counters = nullptr;

@@ -48,6 +48,7 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
 // stream_lds_counter_words(...) counters.
 struct LdsPlan {
   int mt;               // 32-row tiles per workgroup
+  int wpe;              // waves per SIMD the kernel is built for
   int row_blocks;       // workgroups along m
   int groups;           // workgroups along N
   int ksplit;
@@ -62,6 +63,26 @@ hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat,
                              const MatRef *w, void *y, float *partial,
                              unsigned *counters, const LdsPlan &pl,
                              hipStream_t stream);
+
+// Many-row projection (bf16 activations): workgroups of 256 rows x 128
+// (nmat 2, gate+up+silu fused) or 256 (nmat 1) columns; K split across
+// workgroups only when the tiles leave CUs idle.  Partial/counter rules as
+// above.
+struct PrefillPlan {
+  int mt;               // 32-row tiles per workgroup
+  int nbc;              // 32-column tiles per wave and matrix
+  int row_blocks;
+  int groups;
+  int ksplit;
+  int steps_per_split;
+};
+PrefillPlan prefill_plan(int m, int n, int k, int nmat);
+size_t prefill_partial_floats(const PrefillPlan &pl);
+size_t prefill_counter_words(const PrefillPlan &pl);
+hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat,
+                          const MatRef *w, void *y, float *partial,
+                          unsigned *counters, const PrefillPlan &pl,
+                          hipStream_t stream);
 
 // Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above.
 // Eligible when K splits into at most 4 waves of register-resident granules.

@@ -62,9 +62,16 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 // nothing overflows, so for very negative t the result stays the tiny (but
 // representable) t*e^t instead of t divided by an overflowed exp(-t).
 __device__ __forceinline__ float silu_f32(float t) {
-  const float e = expf(-fabsf(t));
-  const float sig = t >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
-  return t * sig;
+  // sigma(t) from e = exp(-|t|) <= 1, so nothing overflows for large |t|.
+  // e = 2^(64 - |t| log2 e) * 2^-64: v_exp_f32 (about 1 ulp) only ever sees
+  // normal results, and the exact power-of-two multiply rounds e into the
+  // fp32 subnormal range once (silu(t) for t < -87 is a bf16 subnormal).
+  // v_rcp_f32 on [1, 2] is within about 1 ulp; both errors sit far below the
+  // resolution of the bf16 result.
+  const float e = __builtin_amdgcn_exp2f(64.0f - fabsf(t) * 1.44269504088896341f) *
+                  5.42101086242752217e-20f;  // log2(e); 2^-64
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  return t * (t >= 0.0f ? r : e * r);
 }
 
 // bf16(silu(bf16(g)) * bf16(u)): gate and up are rounded to bf16 first,
@@ -98,6 +105,12 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+// A 16-bit store through a buffer resource: offsets beyond its range are
+// dropped, so rows past the end need no branch.
+__device__ __forceinline__ void st2(__amdgpu_buffer_rsrc_t r, uint32_t off, __bf16 v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, 0);
 }
 
 // ---- split-K partials shared between workgroups on different XCDs ----------
