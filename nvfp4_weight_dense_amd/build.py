@@ -68,6 +68,15 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A kernel template whose host-side instantiation failed leaves its launch
+    # stub undefined without any compile error; binding every symbol now (in
+    # a child process, so this one keeps no handle) turns that into a build
+    # failure instead of a load failure later.
+    chk = subprocess.run(
+        [sys.executable, "-c", "import ctypes, os, sys; ctypes.CDLL(sys.argv[1], os.RTLD_NOW)", tmp],
+        capture_output=True, text=True)
+    if chk.returncode != 0:
+        raise RuntimeError(f"built library does not load:\n{chk.stderr}")
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

@@ -6,8 +6,9 @@
 // layers/dense_ffn_prefill.rs, `forward_prefill` / `w4a16_prefill_gemm`):
 //   W4A16: gate+up(+silu) -> act, then down -> out.  Up to NVFP4_SMALLM_MAX_M
 //          rows (default 64, the pages' small-m edge) take the weight-streaming
-//          kernel with gate, up and silu_mul fused; more rows take the tiled
-//          kernel, then silu_mul.
+//          kernel with gate, up and silu_mul fused; more rows take the
+//          many-row kernel (also gate+up+silu fused) when k % 256 == 0, else
+//          the LDS-shared streaming kernel with 256-row blocks.
 //   W4A4:  quantize x -> gate+up(+silu) -> act -> quantize act -> down.  One
 //          kernel and one K order for every m, so row bits do not depend on m.
 // Every check runs before the first launch; a forced path that cannot serve a
@@ -44,16 +45,15 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
-enum class Force { Auto, Gemv, Stream, Tiled, Prefill };
-enum class Path { Gemv, Stream, StreamLds, Tiled, Prefill };
+enum class Force { Auto, Gemv, Stream, Prefill };
+enum class Path { Gemv, Stream, StreamLds, Prefill };
 
 const char *path_name(Path p) {
   switch (p) {
     case Path::Gemv: return "gemv";
     case Path::Stream: return "stream";
     case Path::StreamLds: return "stream-lds";
-    case Path::Prefill: return "prefill";
-    default: return "tiled";
+    default: return "prefill";
   }
 }
 
@@ -76,7 +76,6 @@ const Config &cfg() {
     if (const char *v = getenv("NVFP4_FORCE_PATH")) {
       if (!strcmp(v, "gemv")) c.force = Force::Gemv;
       if (!strcmp(v, "stream")) c.force = Force::Stream;
-      if (!strcmp(v, "tiled")) c.force = Force::Tiled;
       if (!strcmp(v, "prefill")) c.force = Force::Prefill;
     }
     if (const char *v = getenv("NVFP4_PROFILE")) c.profile = !strcmp(v, "1");
@@ -198,19 +197,20 @@ bool choose_path(int m, int k, Path *out) {
       *out = Path::Gemv;
       return gemv_eligible(m, k);
     case Force::Stream: *out = stream_kind(m); return true;
-    case Force::Tiled: *out = Path::Tiled; return true;
-    case Force::Prefill: *out = Path::Prefill; return true;
+    case Force::Prefill: *out = Path::Prefill; return k % 256 == 0;
     default:
       if (gemv_eligible(m, k)) *out = Path::Gemv;
-      else *out = m <= cfg().smallm_max_m ? stream_kind(m) : Path::Prefill;
+      else if (m <= cfg().smallm_max_m) *out = stream_kind(m);
+      else *out = k % 256 == 0 ? Path::Prefill : Path::StreamLds;
       return true;
   }
 }
 
 int path_or_fail(int m, int k, Path *out) {
   if (!choose_path(m, k, out))
-    return fail(NVFP4_ESHAPE, "NVFP4_FORCE_PATH=gemv cannot serve m=%d k=%d (needs m<=4 and a K "
-                "that fits four waves of register-resident activations)", m, k);
+    return fail(NVFP4_ESHAPE, "NVFP4_FORCE_PATH=%s cannot serve m=%d k=%d (gemv needs m<=4 and a K "
+                "that fits four waves of register-resident activations; prefill needs k %% 256 == 0)",
+                cfg().force == Force::Gemv ? "gemv" : "prefill", m, k);
   return NVFP4_OK;
 }
 
@@ -255,26 +255,18 @@ struct ProfileScope {
 size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
   if (path == Path::Gemv) return 0;
   if (path == Path::Stream) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
-  if (path == Path::Prefill) return align256(4 * prefill_partial_floats(prefill_plan(m, n, k, nmat)));
   if (path == Path::StreamLds)
     return align256(4 * stream_lds_partial_floats(stream_lds_plan(m, n, k, nmat), nmat, m, n));
-  return nmat == 2 ? 2 * align256((size_t)2 * m * n) : 0;
+  return 0;  // many-row kernel: no scratch
 }
 
 int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, void *y,
              void *scratch, Path path, hipStream_t s) {
   if (path == Path::Gemv)
     return hip_status(launch_gemv(a.x_bf16, m, k, n, nmat, w, y, s), "gemv projection launch");
-  if (path == Path::Prefill) {
-    PrefillPlan pl = prefill_plan(m, n, k, nmat);
-    unsigned *counters = nullptr;
-    if (pl.ksplit > 1) {
-      int rc = counters_get(prefill_counter_words(pl), &counters);
-      if (rc) return rc;
-    }
-    return hip_status(launch_prefill(a.x_bf16, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
+  if (path == Path::Prefill)
+    return hip_status(launch_prefill(a.x_bf16, m, k, n, nmat, w, y, prefill_plan(m, n, k, nmat), s),
                       "many-row projection launch");
-  }
   if (path == Path::StreamLds) {
     LdsPlan pl = stream_lds_plan(m, n, k, nmat);
     unsigned *counters = nullptr;
@@ -293,14 +285,7 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
     return hip_status(launch_stream(a, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
                       "weight-streaming projection launch");
   }
-  if (nmat == 1) return hip_status(launch_tiled(a.x_bf16, m, k, n, w[0], y, s), "tiled projection launch");
-  char *g = (char *)scratch;
-  char *u = g + align256((size_t)2 * m * n);
-  int rc = hip_status(launch_tiled(a.x_bf16, m, k, n, w[0], g, s), "tiled gate launch");
-  if (rc) return rc;
-  rc = hip_status(launch_tiled(a.x_bf16, m, k, n, w[1], u, s), "tiled up launch");
-  if (rc) return rc;
-  return hip_status(launch_silu_mul(g, u, y, (int64_t)m * n, s), "silu_mul launch");
+  return fail(NVFP4_EINVAL, "internal: no kernel for path %s", path_name(path));
 }
 
 int check_ffn(const void *x, int m, int hidden, int inter, const nvfp4_weight *wg,

@@ -25,8 +25,6 @@
 //     (a rotation by the column-group index), so they do not all read the
 //     same activation chunk at the same moment.
 #include <cmath>
-#include <cstdio>
-#include <cstdlib>
 #include <type_traits>
 
 #include "launchers.h"
@@ -54,10 +52,8 @@ struct LdsArgs {
   int rotate;           // stagger the K start of column groups
 };
 
-// WPE: waves per SIMD the register budget is sized for (1: up to 512
-// registers per lane, 2: up to 256, so two workgroups share a CU).
-template <int MT, int NMAT, int WPE>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+template <int MT, int NMAT>
+__global__ __launch_bounds__(kWaves * 64)
 void k_stream_lds(LdsArgs p) {
   constexpr int kRows = 32 * MT;
   __shared__ __attribute__((aligned(16))) uint8_t abuf[3][kRows * kRowBytes];
@@ -147,7 +143,7 @@ void k_stream_lds(LdsArgs p) {
   // unrolled by six), so the compiler's own load waits do the pipelining.
   // (six steps cover HBM latency for few rows; with many rows a step is long
   // and the weights mostly come from L2, so three are enough)
-  constexpr int kDB = MT >= 4 ? (WPE > 1 ? 2 : 3) : 6;
+  constexpr int kDB = MT >= 4 ? 3 : 6;
   static_assert(6 % kDB == 0, "ring slots must divide the unroll");
   uint4 bw[kDB][NMAT];
   uint32_t bs[kDB][NMAT];
@@ -274,9 +270,9 @@ void k_stream_lds(LdsArgs p) {
     }
 }
 
-template <int MT, int NMAT, int WPE = 1>
+template <int MT, int NMAT>
 hipError_t launch2(const LdsArgs &p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_stream_lds<MT, NMAT, WPE>), grid, dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((k_stream_lds<MT, NMAT>), grid, dim3(kWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -284,26 +280,9 @@ hipError_t launch2(const LdsArgs &p, dim3 grid, hipStream_t s) {
 
 int lds_row_tiles(int m) { return m <= 32 ? 1 : m <= 64 ? 2 : 8; }
 
-// many-row shape (row tiles, waves per SIMD); NVFP4_LDS_CFG=<mt>x<wpe>
-// overrides it for measurements
-static void many_row_shape(int *mt, int *wpe) {
-  *mt = 8;
-  *wpe = 1;
-  if (const char *v = getenv("NVFP4_LDS_CFG")) {
-    int a = 0, b = 0;
-    if (sscanf(v, "%dx%d", &a, &b) == 2 && (a == 2 || a == 4 || a == 8) && (b == 1 || b == 2) &&
-        !(a == 8 && b == 2)) {
-      *mt = a;
-      *wpe = b;
-    }
-  }
-}
-
 LdsPlan stream_lds_plan(int m, int n, int k, int nmat) {
   LdsPlan pl;
   pl.mt = lds_row_tiles(m);
-  pl.wpe = 1;
-  if (m > 64) many_row_shape(&pl.mt, &pl.wpe);
   pl.row_blocks = cdiv(m, 32 * pl.mt);
   pl.groups = cdiv(n, kWaves * 32);
   const int nsteps = cdiv(k, kStep);
@@ -317,7 +296,7 @@ LdsPlan stream_lds_plan(int m, int n, int k, int nmat) {
   } else if (nmat == 1) {
     // many rows: one workgroup per CU; split K only to even out the last
     // round (partials cost 4 bytes per output and split)
-    const int slots = 256 * pl.wpe;
+    const int slots = 256;
     double best = 0;
     for (int ks = 1; ks <= 4; ++ks) {
       const double rounds = (double)tiles * ks / slots;
@@ -367,22 +346,16 @@ hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat, const
   p.row_blocks = pl.row_blocks;
   p.rotate = pl.rotate;
   dim3 grid(pl.groups * pl.row_blocks, pl.ksplit);
-  if (pl.wpe == 2) {
-    if (nmat == 2) return pl.mt == 2 ? launch2<2, 2, 2>(p, grid, stream) : launch2<4, 2, 2>(p, grid, stream);
-    return pl.mt == 2 ? launch2<2, 1, 2>(p, grid, stream) : launch2<4, 1, 2>(p, grid, stream);
-  }
   if (nmat == 2) {
     switch (pl.mt) {
       case 1: return launch2<1, 2>(p, grid, stream);
       case 2: return launch2<2, 2>(p, grid, stream);
-      case 4: return launch2<4, 2>(p, grid, stream);
       default: return launch2<8, 2>(p, grid, stream);
     }
   }
   switch (pl.mt) {
     case 1: return launch2<1, 1>(p, grid, stream);
     case 2: return launch2<2, 1>(p, grid, stream);
-    case 4: return launch2<4, 1>(p, grid, stream);
     default: return launch2<8, 1>(p, grid, stream);
   }
 }

@@ -48,7 +48,6 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
 // stream_lds_counter_words(...) counters.
 struct LdsPlan {
   int mt;               // 32-row tiles per workgroup
-  int wpe;              // waves per SIMD the kernel is built for
   int row_blocks;       // workgroups along m
   int groups;           // workgroups along N
   int ksplit;
@@ -64,24 +63,19 @@ hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat,
                              unsigned *counters, const LdsPlan &pl,
                              hipStream_t stream);
 
-// Many-row projection (bf16 activations): workgroups of 256 rows x 128
-// (nmat 2, gate+up+silu fused) or 256 (nmat 1) columns; K split across
-// workgroups only when the tiles leave CUs idle.  Partial/counter rules as
-// above.
+// Many-row projection (bf16 activations, k % 256 == 0): tiles of 256 rows x
+// 128 (nmat 2, gate+up+silu fused) or 256 (nmat 1) columns over the whole
+// K, walked by one persistent workgroup per CU.  Needs no scratch.
 struct PrefillPlan {
-  int mt;               // 32-row tiles per workgroup
-  int nbc;              // 32-column tiles per wave and matrix
+  int mt;    // 32-row tiles per tile
+  int nbc;   // 32-column tiles per wave and matrix
   int row_blocks;
-  int groups;
-  int ksplit;
-  int steps_per_split;
+  int groups;  // column groups
+  int nwg;     // persistent workgroups
 };
 PrefillPlan prefill_plan(int m, int n, int k, int nmat);
-size_t prefill_partial_floats(const PrefillPlan &pl);
-size_t prefill_counter_words(const PrefillPlan &pl);
 hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat,
-                          const MatRef *w, void *y, float *partial,
-                          unsigned *counters, const PrefillPlan &pl,
+                          const MatRef *w, void *y, const PrefillPlan &pl,
                           hipStream_t stream);
 
 // Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above.
@@ -89,10 +83,6 @@ hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat,
 bool gemv_eligible(int m, int k);
 hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat,
                        const MatRef *w, void *y, hipStream_t stream);
-
-// LDS-tiled MFMA projection for many rows (bf16 activations only).
-hipError_t launch_tiled(const void *x, int m, int k, int n, const MatRef &w,
-                        void *y, hipStream_t stream);
 
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out,
                            int64_t count, hipStream_t stream);

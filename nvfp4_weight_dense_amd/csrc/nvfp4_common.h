@@ -100,8 +100,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, size_t 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nrec,
                                            0x00020000);
 }
+// The same, for a base and size the caller knows to be wave-uniform: the
+// pieces go through readfirstlane, so the descriptor stays in scalar
+// registers (instructions that need it there, such as LDS-DMA loads, are
+// otherwise wrapped in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_uniform(const void *base, size_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t nrec = __builtin_amdgcn_readfirstlane(
+      bytes < (size_t)0x7FFFFFFF ? (uint32_t)bytes : 0x7FFFFFFFu);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, (int)nrec,
+                                           0x00020000);
+}
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// The same with a wave-uniform part of the offset in the instruction's
+// scalar offset register (keeps per-lane offset arrays out of VGPRs).
+__device__ __forceinline__ uint4 ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 __device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
@@ -111,6 +129,9 @@ __device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // dropped, so rows past the end need no branch.
 __device__ __forceinline__ void st2(__amdgpu_buffer_rsrc_t r, uint32_t off, __bf16 v) {
   __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void st2s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, __bf16 v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, voff, soff, 0);
 }
 
 // ---- split-K partials shared between workgroups on different XCDs ----------
@@ -132,6 +153,25 @@ __device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t 
 __device__ __forceinline__ void wait_all_memory() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// 16 bytes per lane from a buffer straight into LDS (gfx950 LDS-DMA): lane l
+// writes lds + 16 l (lds must be wave-uniform).  Completion is tracked by
+// the wave's vector-memory counter, like any load.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off,
+                                           0, 0, 0);
+}
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS operations
+// complete (lgkmcnt 0), then s_barrier.  Unlike __syncthreads it does not
+// wait for outstanding global loads, so prefetches stay in flight.  The
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 

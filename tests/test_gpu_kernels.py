@@ -34,7 +34,7 @@ def _all_bytes_weight():
     return si.NvWeight(torch.from_numpy(codes), torch.from_numpy(scales), 1.0)
 
 
-@pytest.mark.parametrize("m", [32, 96])  # 32: streaming kernel, 96: tiled kernel
+@pytest.mark.parametrize("m", [32, 96])  # 32: streaming kernel, 96: many-row kernel
 def test_dequant_every_code_and_scale_exact(m):
     _say(f"dequant identity m={m}")
     w = _all_bytes_weight()
@@ -57,6 +57,8 @@ SHAPES = [
     (1, 16, 32), (1, 50, 96), (2, 200, 160), (4, 64, 4096), (15, 33, 128), (16, 64, 256),
     (17, 80, 384), (33, 33, 512), (48, 100, 640), (64, 130, 1024),
     (65, 130, 1024), (130, 300, 416), (257, 129, 96), (200, 64, 2048),
+    # many-row kernel with tiles split over workgroups by K steps (stream-K)
+    (600, 520, 2048), (300, 1000, 1024),
 ]
 
 
@@ -204,6 +206,30 @@ def test_gate_up_silu_matches_oracle(m):
     sync()
     assert_close(bits(g), oracle.gemm_w4a16(bits(x), o_weight(wg))[1], f"gate m={m}")
     assert_close(bits(u), oracle.gemm_w4a16(bits(x), o_weight(wu))[1], f"up m={m}")
+    ref = oracle.silu_mul(bits(g), bits(u))
+    got = bits(act)
+    d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    same_sign = (got & 0x8000) == (ref & 0x8000)
+    zero_pair = ((got & 0x7FFF) == 0) & ((ref & 0x7FFF) <= 1)
+    assert np.all((same_sign & (d <= 1)) | zero_pair)
+
+
+def test_gate_up_silu_many_rows_split_tiles():
+    """300 rows, hidden 2048, inter 640: two row blocks x five column groups,
+    each split over several workgroups by K steps; act must still equal
+    silu_mul of the separately computed gate and up within one bf16 ulp."""
+    m, hidden, inter = 300, 2048, 640
+    _say(f"gate_up_silu split tiles m={m} hidden={hidden} inter={inter}")
+    x = si.activations(m, hidden, seed=11)
+    wg = si.weight(inter, hidden, seed=12, code_stream=1, scale_stream=2)
+    wu = si.weight(inter, hidden, seed=13, code_stream=3, scale_stream=4)
+    xd = x.cuda()
+    act = nv.nvfp4_gate_up_silu_w4a16(xd, g_weight(wg), g_weight(wu))
+    g = nv.nvfp4_gemm_w4a16(xd, g_weight(wg))
+    u = nv.nvfp4_gemm_w4a16(xd, g_weight(wu))
+    sync()
+    assert_close(bits(g), oracle.gemm_w4a16(bits(x), o_weight(wg))[1], "gate")
+    assert_close(bits(u), oracle.gemm_w4a16(bits(x), o_weight(wu))[1], "up")
     ref = oracle.silu_mul(bits(g), bits(u))
     got = bits(act)
     d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
