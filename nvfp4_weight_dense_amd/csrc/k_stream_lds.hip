@@ -152,7 +152,7 @@ void k_stream_lds(LdsArgs p) {
   load_a(0, areg[0]);
   load_a(1, areg[1]);
   store_a(0, areg[0]);
-  __syncthreads();
+  lds_barrier();
 
   auto step = [&](int tl, auto slot_c) {
     constexpr int s6 = decltype(slot_c)::value;  // tl % 6
@@ -181,7 +181,8 @@ void k_stream_lds(LdsArgs p) {
       }
     }
     if (tl + 1 < len) store_a((sl + 1) % 3, areg[sa ^ 1]);
-    __syncthreads();
+    // LDS hand-off only: the weight prefetch ring stays in flight
+    lds_barrier();
   };
   for (int tl = 0; tl < len; tl += 6) {
     step(tl, std::integral_constant<int, 0>{});
