@@ -256,6 +256,8 @@ def main():
     if not args.only_headline:
         for name, steps, w4a4, m in (("smallm", max(20, args.steps // 2), False, None),
                                      ("prefill", max(5, args.steps // 20), False, None),
+                                     ("w4a4", max(20, args.steps // 2), True, 1),
+                                     ("w4a4", max(20, args.steps // 2), True, 8),
                                      ("w4a4", max(20, args.steps // 2), True, 64),
                                      ("w4a4", max(5, args.steps // 20), True, 512)):
             r, c = measure_ffn(name, steps, max(3, args.warmup // 2), w4a4=w4a4, m=m)
