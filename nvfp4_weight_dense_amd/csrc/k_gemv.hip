@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
       const uint32_t col = (uint32_t)(i / NMAT);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        cw[i][g] = ld16(wres[mat], jok[g] ? col * kb2 + jg[g] * 16u : kOOB);
-        sw[i][g] = ld2(sres[mat], jok[g] ? col * kb16 + jg[g] * 2u : kOOB);
+        cw[i][g] = ld16_nt(wres[mat], jok[g] ? col * kb2 + jg[g] * 16u : kOOB);
+        sw[i][g] = ld2_nt(sres[mat], jok[g] ? col * kb16 + jg[g] * 2u : kOOB);
       }
     }
   };
@@ -251,7 +251,7 @@ int gemv_target_waves() {
   static const int t = [] {
     const char *v = getenv("NVFP4_GEMV_WAVES");
     const int n = v ? atoi(v) : 0;
-    return n > 0 ? n : 4096;
+    return n > 0 ? n : 2048;
   }();
   return t;
 }
@@ -276,7 +276,7 @@ GemvShape gemv_shape(int m, int k) {
 
 template <int M, int NMAT, int G>
 hipError_t launch_g(const GemvArgs &p, int kw, hipStream_t st) {
-  // about 4096 waves in flight; every workgroup walks the same number of
+  // about 2048 waves in flight; every workgroup walks the same number of
   // batches
   const int per_wg = cdiv(p.nbatch * kw, gemv_target_waves());
   const int grid = cdiv(p.nbatch, per_wg);

@@ -121,6 +121,16 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint4 ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// Streaming variants for data read once per call (weights): the
+// non-temporal policy keeps them from displacing reused lines in the caches.
+constexpr int kStreamPolicy = 2;  // nt
+__device__ __forceinline__ uint4 ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamPolicy));
+}
+__device__ __forceinline__ uint32_t ld2_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_bit_cast(uint16_t,
+                                      __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kStreamPolicy));
+}
 __device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
