@@ -46,20 +46,24 @@ int fail(int code, const char *fmt, ...) {
 }
 
 enum class Force { Auto, Gemv, Stream, Prefill };
-enum class Path { Gemv, Stream, StreamLds, Prefill };
+enum class Path { Gemv, Stream, StreamLds, Small, Prefill };
 
 const char *path_name(Path p) {
   switch (p) {
     case Path::Gemv: return "gemv";
     case Path::Stream: return "stream";
     case Path::StreamLds: return "stream-lds";
+    case Path::Small: return "small-m";
     default: return "prefill";
   }
 }
 
-// weight-streaming kernel for this many rows: plain up to 16, LDS-shared
-// activations from 17 to 64
-Path stream_kind(int m) { return m > 16 && m <= 64 ? Path::StreamLds : Path::Stream; }
+// weight-streaming kernel for this many rows: plain up to 16; from 17 to 64
+// the LDS-DMA weight ring when k % 256 == 0, else LDS-shared activations
+Path stream_kind(int m, int k) {
+  if (m <= 16) return Path::Stream;
+  return smallm_eligible(m, k) ? Path::Small : Path::StreamLds;
+}
 
 struct Config {
   int smallm_max_m = 64;
@@ -196,11 +200,11 @@ bool choose_path(int m, int k, Path *out) {
     case Force::Gemv:
       *out = Path::Gemv;
       return gemv_eligible(m, k);
-    case Force::Stream: *out = stream_kind(m); return true;
+    case Force::Stream: *out = stream_kind(m, k); return true;
     case Force::Prefill: *out = Path::Prefill; return k % 256 == 0;
     default:
       if (gemv_eligible(m, k)) *out = Path::Gemv;
-      else if (m <= cfg().smallm_max_m) *out = stream_kind(m);
+      else if (m <= cfg().smallm_max_m) *out = stream_kind(m, k);
       else *out = k % 256 == 0 ? Path::Prefill : Path::StreamLds;
       return true;
   }
@@ -255,6 +259,7 @@ struct ProfileScope {
 size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
   if (path == Path::Gemv) return 0;
   if (path == Path::Stream) return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+  if (path == Path::Small) return align256(4 * smallm_partial_floats(smallm_plan(m, n, k, nmat)));
   if (path == Path::StreamLds)
     return align256(4 * stream_lds_partial_floats(stream_lds_plan(m, n, k, nmat), nmat, m, n));
   return 0;  // many-row kernel: no scratch
@@ -267,6 +272,16 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
   if (path == Path::Prefill)
     return hip_status(launch_prefill(a.x_bf16, m, k, n, nmat, w, y, prefill_plan(m, n, k, nmat), s),
                       "many-row projection launch");
+  if (path == Path::Small) {
+    SmallPlan pl = smallm_plan(m, n, k, nmat);
+    unsigned *counters = nullptr;
+    if (pl.ksplit > 1) {
+      int rc = counters_get((size_t)pl.tiles, &counters);
+      if (rc) return rc;
+    }
+    return hip_status(launch_smallm(a.x_bf16, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
+                      "small-m projection launch");
+  }
   if (path == Path::StreamLds) {
     LdsPlan pl = stream_lds_plan(m, n, k, nmat);
     unsigned *counters = nullptr;

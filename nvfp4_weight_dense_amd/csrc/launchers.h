@@ -63,6 +63,25 @@ hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat,
                              unsigned *counters, const LdsPlan &pl,
                              hipStream_t stream);
 
+// Weight-streaming projection for 17..64 rows (bf16 activations, k % 256
+// == 0): two-wave workgroups of 64 (nmat 2, gate+up+silu fused) or 128
+// (nmat 1) columns, K split over blockIdx.y with the in-kernel fixup;
+// `partial` holds smallm_partial_floats(...) floats and `counters` tiles
+// words that are zero on entry (the kernel leaves them zero).
+struct SmallPlan {
+  int mt;     // 32-row tiles (1 or 2)
+  int tiles;  // workgroups along N
+  int ksplit;
+  int steps_per_split;
+};
+bool smallm_eligible(int m, int k);
+SmallPlan smallm_plan(int m, int n, int k, int nmat);
+size_t smallm_partial_floats(const SmallPlan &pl);
+hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat,
+                         const MatRef *w, void *y, float *partial,
+                         unsigned *counters, const SmallPlan &pl,
+                         hipStream_t stream);
+
 // Many-row projection (bf16 activations, k % 256 == 0): tiles of 256 rows x
 // 128 (nmat 2, gate+up+silu fused) or 256 (nmat 1) columns over the whole
 // K, walked by one persistent workgroup per CU.  Needs no scratch.
