@@ -1,5 +1,7 @@
 // k_elementwise.hip -- silu_mul and the per-row NVFP4 activation quantizer
 // (gfx950).  Both are HBM-bound passes over bf16 rows.
+#include <algorithm>
+
 #include "launchers.h"
 #include "nvfp4_common.h"
 
@@ -78,38 +80,59 @@ __device__ __forceinline__ uint32_t e2m1_encode_sat(float q) {
   return sign | mag;
 }
 
-// One workgroup per row; k % 32 == 0.
-__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restrict__ x, int k,
-                                                      uint8_t *__restrict__ codes,
-                                                      uint8_t *__restrict__ scales,
-                                                      float *__restrict__ row_scale) {
-  const int r = blockIdx.x;
-  const uint16_t *xr = x + (size_t)r * k;
-  const uint4 *xv4 = (const uint4 *)xr;
+// One workgroup per row, one thread per 16-element block (k % 32 == 0): the
+// workgroup size follows the row length up to 1024 threads, and each thread
+// keeps up to kKeep of its blocks in registers between the row-amax pass and
+// the encode pass (longer rows re-read the rest).  The row amax is a plain
+// maximum, so the thread count does not change any result.
+constexpr int kQuantMaxThreads = 1024;
+constexpr int kKeep = 4;
 
-  float amax = 0.0f;
-  for (int c = threadIdx.x; c < (k >> 3); c += 256) {
-    const uint4 v = xv4[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16_t *__restrict__ x, int k,
+                                                                   uint8_t *__restrict__ codes,
+                                                                   uint8_t *__restrict__ scales,
+                                                                   float *__restrict__ row_scale) {
+  const int r = blockIdx.x;
+  const int nt = blockDim.x;
+  const int t = threadIdx.x;
+  const int nblk = k >> 4;
+  const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
+
+  auto block_amax = [](const uint4 &v0, const uint4 &v1, float amax) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)));
       amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
     }
+    return amax;
+  };
+
+  uint4 keep[kKeep][2];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    const int b = t + i * nt;
+    if (b < nblk) {
+      keep[i][0] = xv4[2 * b];
+      keep[i][1] = xv4[2 * b + 1];
+      amax = block_amax(keep[i][0], keep[i][1], amax);
+    }
   }
+  for (int b = t + kKeep * nt; b < nblk; b += nt) amax = block_amax(xv4[2 * b], xv4[2 * b + 1], amax);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  __shared__ float wmax[4];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __shared__ float wmax[kQuantMaxThreads / 64];
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  amax = wmax[0];
+  for (int w = 1; w < (nt >> 6); ++w) amax = fmaxf(amax, wmax[w]);
 
   float s_row = amax / 2688.0f;
   if (amax == 0.0f) s_row = 1.0f;
-  if (threadIdx.x == 0) row_scale[r] = s_row;
+  if (t == 0) row_scale[r] = s_row;
 
-  for (int b = threadIdx.x; b < (k >> 4); b += 256) {
-    const uint4 v0 = xv4[2 * b], v1 = xv4[2 * b + 1];
+  auto encode_block = [&](int b, const uint4 &v0, const uint4 &v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     float xv[16];
     float amax_b = 0.0f;
@@ -121,8 +144,8 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
       amax_b = fmaxf(amax_b, fabsf(xv[2 * q + 1]));
     }
     const float d = 6.0f * s_row;
-    const float t = amax_b / d;
-    const uint32_t sb = e4m3_encode_sat(t);
+    const float tb = amax_b / d;
+    const uint32_t sb = e4m3_encode_sat(tb);
     const float v = e4m3_to_f32(sb);
     const float den = v * s_row;
     uint32_t packed[2] = {0u, 0u};
@@ -136,8 +159,14 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
       packed[i >> 3] |= code << (4 * (i & 7));
     }
     *(uint2 *)(codes + (size_t)r * (k >> 1) + 8 * b) = make_uint2(packed[0], packed[1]);
-    scales[(size_t)r * (k >> 4) + b] = (uint8_t)sb;
+    scales[(size_t)r * nblk + b] = (uint8_t)sb;
+  };
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    const int b = t + i * nt;
+    if (b < nblk) encode_block(b, keep[i][0], keep[i][1]);
   }
+  for (int b = t + kKeep * nt; b < nblk; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
 }
 
 }  // namespace
@@ -155,7 +184,9 @@ hipError_t launch_silu_mul(const void *gate, const void *up, void *out, int64_t 
 
 hipError_t launch_quantize_rows(const void *x, int m, int k, uint8_t *codes, uint8_t *scales,
                                 float *row_scale, hipStream_t stream) {
-  hipLaunchKernelGGL(k_quantize_rows, dim3(m), dim3(256), 0, stream, (const uint16_t *)x, k,
+  const int nblk = k >> 4;
+  const int threads = std::min(kQuantMaxThreads, (nblk + 63) / 64 * 64);
+  hipLaunchKernelGGL(k_quantize_rows, dim3(m), dim3(threads), 0, stream, (const uint16_t *)x, k,
                      codes, scales, row_scale);
   return hipGetLastError();
 }
