@@ -75,7 +75,7 @@ def _time_loop(fn, reps, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
-def measure_ffn(name, steps, warmup, w4a4=False, m=None):
+def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False):
     import torch
 
     import nvfp4_weight_dense_amd as nv
@@ -87,15 +87,23 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None):
     inter = wg.n
     wbytes = weight_bytes(wg) + weight_bytes(wu) + weight_bytes(wd)
     nrep = max(1, math.ceil(REPLICA_BYTES / wbytes))
-    reps = _replicas((wg, wu, wd), nrep, dev)
     xd = x.to(dev)
     out = torch.empty((m, hidden), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    fn = nv.dense_ffn_forward_w4a4 if w4a4 else nv.dense_ffn_forward
+    if fused:
+        # one [2*inter, hidden] buffer holding gate then up (same bytes)
+        assert wg.ts == wu.ts and not w4a4
+        wgu = si.NvWeight(torch.cat([wg.codes, wu.codes]), torch.cat([wg.scales, wu.scales]), wg.ts)
+        reps = _replicas((wgu, wd), nrep, dev)
+        fn = nv.dense_ffn_forward_fused
+    else:
+        reps = _replicas((wg, wu, wd), nrep, dev)
+        fn = nv.dense_ffn_forward_w4a4 if w4a4 else nv.dense_ffn_forward
     ms = _time_loop(lambda r: fn(xd, *r, out=out, stream=stream), reps, steps, warmup, stream)
     flops = 6.0 * m * hidden * inter
     res = {
-        "workload": f"{name} m={m} hidden={hidden} inter={inter}" + (" w4a4" if w4a4 else ""),
+        "workload": f"{name} m={m} hidden={hidden} inter={inter}" + (" w4a4" if w4a4 else "")
+                    + (" fused gate+up weight" if fused else ""),
         "m": m, "hidden": hidden, "inter": inter,
         "ms_per_step": ms,
         "tflops": flops / (ms * 1e-3) / 1e12,
@@ -254,13 +262,15 @@ def main():
     del ctx
     workloads = []
     if not args.only_headline:
-        for name, steps, w4a4, m in (("smallm", max(20, args.steps // 2), False, None),
-                                     ("prefill", max(5, args.steps // 20), False, None),
-                                     ("w4a4", max(20, args.steps // 2), True, 1),
-                                     ("w4a4", max(20, args.steps // 2), True, 8),
-                                     ("w4a4", max(20, args.steps // 2), True, 64),
-                                     ("w4a4", max(5, args.steps // 20), True, 512)):
-            r, c = measure_ffn(name, steps, max(3, args.warmup // 2), w4a4=w4a4, m=m)
+        for name, steps, w4a4, m, fused in (
+                ("decode", args.steps, False, None, True),
+                ("smallm", max(20, args.steps // 2), False, None, False),
+                ("prefill", max(5, args.steps // 20), False, None, False),
+                ("w4a4", max(20, args.steps // 2), True, 1, False),
+                ("w4a4", max(20, args.steps // 2), True, 8, False),
+                ("w4a4", max(20, args.steps // 2), True, 64, False),
+                ("w4a4", max(5, args.steps // 20), True, 512, False)):
+            r, c = measure_ffn(name, steps, max(3, args.warmup // 2), w4a4=w4a4, m=m, fused=fused)
             del c
             torch.cuda.empty_cache()
             workloads.append(r)

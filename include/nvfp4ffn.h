@@ -127,6 +127,33 @@ int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden,
                            const nvfp4_weight *wu, const nvfp4_weight *wd,
                            void *out, void *stream);
 
+/* Views into one fused gate+up weight [2*inter][hidden]: rows 0..inter-1 are
+ * gate and rows inter..2*inter-1 are up, and the E4M3 scale grid is split
+ * the same way.  On success *gate and *up point into fused's buffers:
+ *   gate->codes  == fused->codes,
+ *   up->codes    == fused->codes  + inter * hidden/2,
+ *   gate->scales == fused->scales,
+ *   up->scales   == fused->scales + inter * hidden/16,
+ * both [inter][hidden] with fused's tensor scale.  Host-side pointer
+ * arithmetic only: no device access, no allocation, the outputs borrow
+ * fused's memory.  NVFP4_EINVAL for a null or misaligned descriptor
+ * (a view must stay 16-byte aligned), NVFP4_ESHAPE when fused->n is odd.
+ * (page layers/dense_ffn_overlays.rs, `set_fp8_gate_up_fused`: there the
+ * FP8 gate and up weights are views into one [2*inter, hidden] buffer at
+ * offsets 0 and inter*hidden, scale grid alike; here the same contract for
+ * NVFP4.) */
+int nvfp4_gate_up_views(const nvfp4_weight *fused, nvfp4_weight *gate,
+                        nvfp4_weight *up);
+
+/* Dense SwiGLU FFN, W4A16, on a fused gate+up weight wgu [2*inter][hidden]
+ * (layout as in nvfp4_gate_up_views) and wd [hidden][inter].  Runs exactly
+ * what dense_ffn_forward runs on the two views (one launch streams both
+ * halves and applies silu), so the two give identical bits.  Errors as
+ * dense_ffn_forward, plus NVFP4_ESHAPE when wgu is not [2*inter][hidden]. */
+int dense_ffn_forward_fused(const void *x, int32_t m, int32_t hidden,
+                            int32_t inter, const nvfp4_weight *wgu,
+                            const nvfp4_weight *wd, void *out, void *stream);
+
 /* The calling thread's last error message ("" if none). */
 const char *nvfp4_last_error(void);
 

@@ -33,6 +33,7 @@ __all__ = [
     "NVFP4Weight", "Nvfp4Error", "Nvfp4LibraryMissing",
     "nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "nvfp4_quantize_rows", "silu_mul",
     "nvfp4_gate_up_silu_w4a16", "dense_ffn_forward", "dense_ffn_forward_w4a4",
+    "nvfp4_gate_up_views", "dense_ffn_forward_fused",
     "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
 ]
 
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH):
         "nvfp4_gate_up_silu_w4a16": [vp, i32, wp, wp, vp, vp],
         "dense_ffn_forward": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
         "dense_ffn_forward_w4a4": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
+        "nvfp4_gate_up_views": [wp, wp, wp],
+        "dense_ffn_forward_fused": [vp, i32, i32, i32, wp, wp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -237,3 +240,35 @@ def dense_ffn_forward_w4a4(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None
                            stream=None):
     """Fixed-format W4A4 FFN (activations quantized per row before each projection)."""
     return _ffn(load_library().dense_ffn_forward_w4a4, x, wg, wu, wd, out, stream)
+
+
+def nvfp4_gate_up_views(fused) -> tuple[NVFP4Weight, NVFP4Weight]:
+    """(gate, up) views into a fused gate+up weight [2*inter, hidden]: row
+    slices of the same codes/scales storage, at the offsets the C-ABI call
+    reports (checked here)."""
+    L = load_library()
+    cf = _cweight(fused)
+    cg, cu = _CWeight(), _CWeight()
+    _check(L.nvfp4_gate_up_views(ctypes.byref(cf), ctypes.byref(cg), ctypes.byref(cu)))
+    inter = cg.n
+    ts = float(cf.tensor_scale)
+    gate = NVFP4Weight(fused.codes[:inter], fused.scales[:inter], ts)
+    up = NVFP4Weight(fused.codes[inter:], fused.scales[inter:], ts)
+    for view, c in ((gate, cg), (up, cu)):
+        assert view.codes.data_ptr() == c.codes and view.scales.data_ptr() == c.scales
+    return gate, up
+
+
+def dense_ffn_forward_fused(x: torch.Tensor, wgu, wd, out: torch.Tensor | None = None,
+                            stream=None):
+    """W4A16 dense SwiGLU FFN on a fused gate+up weight [2*inter, hidden]."""
+    L = load_library()
+    x = _act(x, "x")
+    cgu, cd = _cweight(wgu), _cweight(wd)
+    m, hidden = x.shape
+    inter = cgu.n // 2
+    if out is None:
+        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
+    _check(L.dense_ffn_forward_fused(_ptr(x), m, hidden, inter, ctypes.byref(cgu), ctypes.byref(cd),
+                                     _ptr(out), _stream(stream)))
+    return out

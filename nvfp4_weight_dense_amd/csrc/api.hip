@@ -455,6 +455,38 @@ int dense_ffn_forward(const void *x, int32_t m, int32_t hidden, int32_t inter,
   return run_proj(ActRef{act, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &wdm, out, scr, p_down, s);
 }
 
+int nvfp4_gate_up_views(const nvfp4_weight *fused, nvfp4_weight *gate, nvfp4_weight *up) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_weight(fused, "fused"))) return rc;
+  if (!gate || !up) return fail(NVFP4_EINVAL, "gate_up_views: null output descriptor");
+  if (fused->n % 2 != 0)
+    return fail(NVFP4_ESHAPE, "gate_up_views: fused n=%d is not 2*inter", fused->n);
+  const int inter = fused->n / 2;
+  const size_t off_codes = (size_t)inter * (size_t)(fused->k / 2);
+  const size_t off_scales = (size_t)inter * (size_t)(fused->k / 16);
+  nvfp4_weight g = {fused->codes, fused->scales, fused->tensor_scale, inter, fused->k};
+  nvfp4_weight u = {fused->codes + off_codes, fused->scales + off_scales, fused->tensor_scale, inter,
+                    fused->k};
+  if ((rc = check_weight(&u, "up view"))) return rc;
+  *gate = g;
+  *up = u;
+  return NVFP4_OK;
+}
+
+int dense_ffn_forward_fused(const void *x, int32_t m, int32_t hidden, int32_t inter,
+                            const nvfp4_weight *wgu, const nvfp4_weight *wd, void *out,
+                            void *stream) {
+  g_err.clear();
+  int rc;
+  nvfp4_weight wg, wu;
+  if ((rc = nvfp4_gate_up_views(wgu, &wg, &wu))) return rc;
+  if ((int64_t)wgu->n != 2 * (int64_t)inter || wgu->k != hidden)
+    return fail(NVFP4_ESHAPE, "wgu must be [2*inter=%lld][hidden=%d], got [%d][%d]",
+                2 * (long long)inter, hidden, wgu->n, wgu->k);
+  return dense_ffn_forward(x, m, hidden, inter, &wg, &wu, wd, out, stream);
+}
+
 int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, void *stream) {
   g_err.clear();
   int rc;

@@ -34,6 +34,7 @@ def test_header_declares_the_abi():
     names = _declared_functions()
     for want in ["nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "silu_mul", "dense_ffn_forward",
                  "dense_ffn_forward_w4a4", "nvfp4_quantize_rows", "nvfp4_gate_up_silu_w4a16",
+                 "nvfp4_gate_up_views", "dense_ffn_forward_fused",
                  "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version"]:
         assert want in names
 
@@ -100,6 +101,37 @@ def test_ffn_shape_consistency_checks():
         assert fn(x, 2, 0, inter, ctypes.byref(wg), ctypes.byref(wu), ctypes.byref(wd),
                   out, s) == nv.NVFP4_ESHAPE
     assert L.nvfp4_gate_up_silu_w4a16(x, 2, ctypes.byref(wg), ctypes.byref(_w(inter, 32)), out, s) \
+        == nv.NVFP4_ESHAPE
+
+
+def test_gate_up_views_are_offsets_into_the_fused_buffer():
+    """Host-only pointer arithmetic: no device memory is touched."""
+    L = _lib()
+    inter, hidden = 96, 64
+    fused = _w(2 * inter, hidden)
+    g, u = nv._CWeight(), nv._CWeight()
+    assert L.nvfp4_gate_up_views(ctypes.byref(fused), ctypes.byref(g), ctypes.byref(u)) == nv.NVFP4_OK
+    assert (g.codes, g.scales, g.n, g.k) == (0x10000, 0x20000, inter, hidden)
+    assert (u.codes, u.scales, u.n, u.k) == (0x10000 + inter * hidden // 2,
+                                             0x20000 + inter * hidden // 16, inter, hidden)
+    assert g.tensor_scale == u.tensor_scale == 1.0
+    # odd row count
+    assert L.nvfp4_gate_up_views(ctypes.byref(_w(2 * inter + 1, hidden)), ctypes.byref(g),
+                                 ctypes.byref(u)) == nv.NVFP4_ESHAPE
+    # up's scale view would start 6 bytes in: not 16-byte aligned
+    assert L.nvfp4_gate_up_views(ctypes.byref(_w(6, 32)), ctypes.byref(g),
+                                 ctypes.byref(u)) == nv.NVFP4_EINVAL
+    assert "up view" in nv.nvfp4_last_error()
+    assert L.nvfp4_gate_up_views(ctypes.byref(fused), None, ctypes.byref(u)) == nv.NVFP4_EINVAL
+    # fused FFN: shape checks, m == 0 succeeds without a launch
+    x, out, s = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x80000), ctypes.c_void_p(None)
+    wd = _w(hidden, inter)
+    fn = L.dense_ffn_forward_fused
+    assert fn(x, 0, hidden, inter, ctypes.byref(fused), ctypes.byref(wd), out, s) == nv.NVFP4_OK
+    assert fn(x, 2, hidden, inter + 16, ctypes.byref(fused), ctypes.byref(wd), out, s) \
+        == nv.NVFP4_ESHAPE
+    assert "wgu must be" in nv.nvfp4_last_error()
+    assert fn(x, 2, hidden, inter, ctypes.byref(fused), ctypes.byref(_w(inter, hidden)), out, s) \
         == nv.NVFP4_ESHAPE
 
 

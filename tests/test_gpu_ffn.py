@@ -92,3 +92,25 @@ def test_w4a4_activation_codes_match_oracle_on_gpu_activations():
     assert np.array_equal(c.cpu().numpy(), co)
     assert np.array_equal(s.cpu().numpy(), so)
     assert np.array_equal(r.cpu().numpy(), ro)
+
+
+@pytest.mark.parametrize("m", [1, 40, 200])
+def test_dense_ffn_fused_gate_up_weight(m):
+    """A [2*inter, hidden] buffer holding gate then up gives the same bits
+    as the separate weights (GEMV, small-m and many-row paths), and the
+    oracle's result within tolerance."""
+    _say(f"ffn fused gate+up weight m={m}")
+    x, wg, wu, wd = si.workload("tiny", m=m)
+    assert wg.ts == wu.ts
+    wgu = nv.NVFP4Weight(torch.cat([wg.codes, wu.codes]).cuda(),
+                         torch.cat([wg.scales, wu.scales]).cuda(), wg.ts)
+    gv, uv = nv.nvfp4_gate_up_views(wgu)
+    assert gv.codes.data_ptr() == wgu.codes.data_ptr()
+    assert uv.scales.data_ptr() == wgu.scales.data_ptr() + wg.n * wg.k // 16
+    xd, gd = x.cuda(), g_weight(wd)
+    y_fused = nv.dense_ffn_forward_fused(xd, wgu, gd)
+    y_sep = nv.dense_ffn_forward(xd, g_weight(wg), g_weight(wu), gd)
+    sync()
+    assert torch.equal(y_fused.view(torch.int16), y_sep.view(torch.int16))
+    _, ye = oracle.dense_ffn(bits(x), o_weight(wg), o_weight(wu), o_weight(wd))
+    assert_close(bits(y_fused), ye, f"ffn fused m={m}")
