@@ -14,12 +14,16 @@
 //     bytes with one 128-bit and one 16-bit buffer load; per column tile a
 //     wave's load covers 16 rows x 64 contiguous bytes.  Buffer loads return
 //     zero outside the resource's range, so ragged columns, rows and K need
-//     no branches.  The codes are dequantized in registers to four bf16 B
-//     fragments of v_mfma_f32_16x16x32_bf16; the MFMA's K order inside a step
-//     is (g, element), and the activation fragment uses the same order.
+//     no branches.  The codes are dequantized in registers to four B
+//     fragments of v_mfma_f32_16x16x32_bf16 (bf16 activations), or of
+//     v_mfma_f32_16x16x32_f16 for W4A4, where both operands are NVFP4 and
+//     exact in fp16 (one conversion and one packed multiply per pair instead
+//     of four operations); the MFMA's K order inside a step is (g, element),
+//     and the activation fragment uses the same order.
 //   * The activation fragment of row r is the 32 contiguous K values at the
 //     same offset (bf16, 64 bytes), or for W4A4 the row's NVFP4 codes
-//     dequantized exactly like the weight; one fragment feeds CTW*NMAT MFMAs.
+//     dequantized exactly like the weight (fp16); one fragment feeds
+//     CTW*NMAT MFMAs.
 //   * Waves reduce through LDS in fixed wave order.  With ksplit > 1 each
 //     workgroup writes its fp32 partial tile; the last workgroup of a tile to
 //     finish (a self-resetting arrival counter) sums the partials in split
@@ -28,6 +32,8 @@
 //     the W4A4 arm needs.
 //   * Up to 64 rows (MT tiles of 16) share each dequantized weight fragment;
 //     more rows use more row blocks (grid.z).
+#include <type_traits>
+
 #include "launchers.h"
 #include "nvfp4_common.h"
 
@@ -63,6 +69,9 @@ struct Cfg {
 template <int MT, int NMAT, int CTW, bool AFP4>
 __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
   constexpr int U = Cfg<MT, NMAT, CTW, AFP4>::U;
+  // MFMA operand type: fp16 when both operands are NVFP4 (exact either way,
+  // half the conversion work), bf16 for bf16 activations
+  using Frag = std::conditional_t<AFP4, f16x8, bf16x8>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
@@ -136,29 +145,39 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      bf16x8 bf[NMAT][CTW][4];
+      Frag bf[NMAT][CTW][4];
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
+          const uint4 w = bw[u][i][ct];
           const float s0 = e4m3_to_f32_sel<0>(bsc[u][i][ct]);
           const float s1 = e4m3_to_f32_sel<1>(bsc[u][i][ct]);
-          bf[i][ct][0] = dequant8(bw[u][i][ct].x, s0);
-          bf[i][ct][1] = dequant8(bw[u][i][ct].y, s0);
-          bf[i][ct][2] = dequant8(bw[u][i][ct].z, s1);
-          bf[i][ct][3] = dequant8(bw[u][i][ct].w, s1);
+          if constexpr (AFP4) {
+            const f16x2 m0 = scale_mantissa_f16x2(s0), m1 = scale_mantissa_f16x2(s1);
+            bf[i][ct][0] = dequant8_f16(w.x, s0, m0);
+            bf[i][ct][1] = dequant8_f16(w.y, s0, m0);
+            bf[i][ct][2] = dequant8_f16(w.z, s1, m1);
+            bf[i][ct][3] = dequant8_f16(w.w, s1, m1);
+          } else {
+            bf[i][ct][0] = dequant8(w.x, s0);
+            bf[i][ct][1] = dequant8(w.y, s0);
+            bf[i][ct][2] = dequant8(w.z, s1);
+            bf[i][ct][3] = dequant8(w.w, s1);
+          }
         }
-      bf16x8 afr[MT][4];
+      Frag afr[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        bf16x8 (&af)[4] = afr[mt];
+        Frag (&af)[4] = afr[mt];
         if constexpr (AFP4) {
           const float s0 = e4m3_to_f32_sel<0>(asc[u][mt]);
           const float s1 = e4m3_to_f32_sel<1>(asc[u][mt]);
-          af[0] = dequant8(aw[u][mt][0].x, s0);
-          af[1] = dequant8(aw[u][mt][0].y, s0);
-          af[2] = dequant8(aw[u][mt][0].z, s1);
-          af[3] = dequant8(aw[u][mt][0].w, s1);
+          const f16x2 m0 = scale_mantissa_f16x2(s0), m1 = scale_mantissa_f16x2(s1);
+          af[0] = dequant8_f16(aw[u][mt][0].x, s0, m0);
+          af[1] = dequant8_f16(aw[u][mt][0].y, s0, m0);
+          af[2] = dequant8_f16(aw[u][mt][0].z, s1, m1);
+          af[3] = dequant8_f16(aw[u][mt][0].w, s1, m1);
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) af[q] = as_bf16x8(aw[u][mt][q]);
@@ -172,9 +191,14 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
 #pragma unroll
           for (int i = 0; i < NMAT; ++i)
 #pragma unroll
-            for (int ct = 0; ct < CTW; ++ct)
-              acc[i][ct][mt] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
+            for (int ct = 0; ct < CTW; ++ct) {
+              if constexpr (AFP4)
+                acc[i][ct][mt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[mt][j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
+              else
+                acc[i][ct][mt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
+            }
     }
   }
 

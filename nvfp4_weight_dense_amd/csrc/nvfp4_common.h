@@ -21,6 +21,8 @@ typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
@@ -52,6 +54,27 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
   r[6] = (__bf16)(p3[0] * s);
   r[7] = (__bf16)(p3[1] * s);
   return r;
+}
+
+// The same eight values as fp16, for operands that are NVFP4 on both sides.
+// An E2M1 value (at most 2 significant bits) times an E4M3 scale (at most
+// 4) needs at most 6 significant bits and lies in [2^-10, 2688], so it is
+// exact in fp16.  The hardware conversion applies the power-of-two part of
+// its scale operand (the scale itself is passed); the mantissa factor of
+// the scale, in [1, 2), follows as one packed fp16 multiply per pair.  A
+// zero scale gives zeros.
+__device__ __forceinline__ f16x2 scale_mantissa_f16x2(float s) {
+  const float mf =
+      __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, s) & 0x007FFFFFu) | 0x3F800000u);
+  const _Float16 h = (_Float16)mf;
+  return f16x2{h, h};
+}
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float s, f16x2 mf) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0) * mf;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1) * mf;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * mf;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * mf;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
