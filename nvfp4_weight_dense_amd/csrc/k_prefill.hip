@@ -7,11 +7,12 @@
 // cost that matters besides the MFMAs is the in-register dequantization
 // (about two VALU instructions per weight element).
 //
-// Workgroup: four waves, 256 rows.  Each wave owns 256 rows x two 32-column
-// B tiles -- gate and up at the same columns (SWIGLU), or two adjacent
-// column tiles of one matrix -- so a dequantized B fragment feeds eight
-// v_mfma_f32_32x32x16_bf16 and an activation fragment read from LDS feeds
-// two.  Accumulators: 2 x 8 x 16 fp32 per lane (the AGPR file).
+// Workgroup: four waves, 32*MT rows (MT = 8, 6, 5 or 4, chosen per shape so
+// that the tiles fill the CUs' rounds best).  Each wave owns those rows x
+// two 32-column B tiles -- gate and up at the same columns (SWIGLU), or two
+// adjacent column tiles of one matrix -- so a dequantized B fragment feeds
+// MT v_mfma_f32_32x32x16_bf16 and an activation fragment read from LDS
+// feeds two.  Accumulators: 2 x MT x 16 fp32 per lane (the AGPR file).
 //
 // Step (64 K): rows x 64 K of bf16 activations sit in one of two LDS slots
 // (row pitch 144 bytes: conflict-free 16-byte fragment reads); the chunk of
@@ -48,6 +49,7 @@
 //
 // Requires k % 256 == 0 (16-byte aligned scale groups).
 #include <algorithm>
+#include <cstdint>
 #include <cmath>
 #include <type_traits>
 
@@ -134,9 +136,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
 
   // activation chunk: 16-byte pieces, row = piece / 8, byte 16 * (piece % 8);
   // thread tid moves pieces tid + 256 i, i.e. row tid/8 + 32 i at K offset
-  // 8 (tid % 8) of the step.  The per-lane part of the address is one VGPR,
-  // the 32 i rows go in the scalar offset; rows past m fall outside xres.
+  // 8 (tid % 8) of the step (MT pieces per thread).  The per-lane part of
+  // the address is one VGPR, the 32 i rows go in the scalar offset; rows
+  // past m fall outside xres.
   constexpr int kPerThread = kRows * 8 / (kWaves * 64);
+  static_assert(kPerThread * kWaves * 64 == kRows * 8, "activation pieces per thread");
   const uint32_t kin = 8u * (uint32_t)(tid & 7);
   const uint32_t avoff = ((uint32_t)(tid >> 3) * (uint32_t)k + kin) * 2u;
   uint4 areg[kPerThread];
@@ -347,15 +351,31 @@ static int device_cus() {
 }
 
 PrefillPlan prefill_plan(int m, int n, int k, int nmat) {
-  PrefillPlan pl;
-  pl.mt = 8;
-  pl.nbc = nmat == 2 ? 1 : 2;
-  pl.row_blocks = cdiv(m, 32 * pl.mt);
-  pl.groups = cdiv(n, kWaves * 32 * pl.nbc);
   (void)k;
-  // one persistent workgroup per CU (fewer if there are fewer tiles)
-  pl.nwg = std::max(1, std::min(device_cus(), pl.row_blocks * pl.groups));
-  return pl;
+  // Tile height: 32 * MT rows, MT in {8, 6, 5, 4}.  A workgroup's time per
+  // K step grows with MT plus a part that does not (weight groups, B
+  // dequantization, the step barrier): measured about 6 MT-units of fixed
+  // cost per step.  Persistent workgroups walk the tiles in rounds of one
+  // per CU, so a shape is charged rounds x (6 + MT) and the cheapest height
+  // wins (ties to the taller tile, which reuses each weight fragment most).
+  const int cus = device_cus();
+  PrefillPlan best{};
+  long best_cost = -1;
+  for (int mt : {8, 6, 5, 4}) {
+    PrefillPlan pl;
+    pl.mt = mt;
+    pl.nbc = nmat == 2 ? 1 : 2;
+    pl.row_blocks = cdiv(m, 32 * mt);
+    pl.groups = cdiv(n, kWaves * 32 * pl.nbc);
+    const long tiles = (long)pl.row_blocks * pl.groups;
+    pl.nwg = (int)std::max(1L, std::min((long)cus, tiles));
+    const long cost = cdiv((int)std::min(tiles, (long)INT32_MAX), cus) * (long)(6 + mt);
+    if (best_cost < 0 || cost < best_cost) {
+      best = pl;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat, const MatRef *w, void *y,
@@ -376,10 +396,17 @@ hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat, const Ma
   p.groups = pl.groups;
   p.nwg = pl.nwg;
   dim3 grid(pl.nwg), block(kWaves * 64);
-  if (nmat == 2)
-    hipLaunchKernelGGL((k_prefill<8, 1, true>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((k_prefill<8, 2, false>), grid, block, 0, stream, p);
+  switch ((nmat == 2 ? 100 : 0) + pl.mt) {
+    case 108: hipLaunchKernelGGL((k_prefill<8, 1, true>), grid, block, 0, stream, p); break;
+    case 106: hipLaunchKernelGGL((k_prefill<6, 1, true>), grid, block, 0, stream, p); break;
+    case 105: hipLaunchKernelGGL((k_prefill<5, 1, true>), grid, block, 0, stream, p); break;
+    case 104: hipLaunchKernelGGL((k_prefill<4, 1, true>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((k_prefill<8, 2, false>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((k_prefill<6, 2, false>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((k_prefill<5, 2, false>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_prefill<4, 2, false>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
