@@ -50,6 +50,7 @@
 // Requires k % 256 == 0 (16-byte aligned scale groups).
 #include <algorithm>
 #include <cstdint>
+#include <initializer_list>
 #include <cmath>
 #include <type_traits>
 
@@ -71,6 +72,7 @@ struct PrefillArgs {
   const uint8_t *codes1, *scales1;  // up (SWIGLU) or unused
   float ts0, ts1;
   void *y;
+  int ldy;                 // row stride of y in elements (>= n)
   int row_blocks, groups;  // tile = column group * row_blocks + row block
   int nwg;                 // persistent workgroups (gridDim.x)
 };
@@ -298,10 +300,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
   // lane's element e of row tile mt: row 32mt + 8(e/4) + 4h + e%4, column col[i] + c32
   // rows past m fall outside the output resource and are dropped
   const __amdgpu_buffer_rsrc_t yres =
-      rsrc_uniform((uint8_t *)p.y + (size_t)row0 * p.n * 2, (size_t)max(rows, 0) * p.n * 2);
+      rsrc_uniform((uint8_t *)p.y + (size_t)row0 * p.ldy * 2, (size_t)max(rows, 0) * p.ldy * 2);
   // element (mt, e): row 32mt + 8(e/4) + 4h + e%4 -- the 4h row and the
   // column are the per-lane part, the rest is uniform (scalar offset)
-  const uint32_t n2 = (uint32_t)p.n * 2u;
+  const uint32_t n2 = (uint32_t)p.ldy * 2u;
   if constexpr (SWIGLU) {
 #pragma unroll
     for (int i = 0; i < NBC; ++i) {
@@ -350,33 +352,93 @@ static int device_cus() {
   return cached[dev];
 }
 
-PrefillPlan prefill_plan(int m, int n, int k, int nmat) {
-  (void)k;
-  // Tile height: 32 * MT rows, MT in {8, 6, 5, 4}.  A workgroup's time per
-  // K step grows with MT plus a part that does not (weight groups, B
-  // dequantization, the step barrier): measured about 6 MT-units of fixed
-  // cost per step.  Persistent workgroups walk the tiles in rounds of one
-  // per CU, so a shape is charged rounds x (6 + MT) and the cheapest height
-  // wins (ties to the taller tile, which reuses each weight fragment most).
-  const int cus = device_cus();
-  PrefillPlan best{};
-  long best_cost = -1;
-  for (int mt : {8, 6, 5, 4}) {
-    PrefillPlan pl;
-    pl.mt = mt;
-    pl.nbc = nmat == 2 ? 1 : 2;
-    pl.row_blocks = cdiv(m, 32 * mt);
-    pl.groups = cdiv(n, kWaves * 32 * pl.nbc);
-    const long tiles = (long)pl.row_blocks * pl.groups;
-    pl.nwg = (int)std::max(1L, std::min((long)cus, tiles));
-    const long cost = cdiv((int)std::min(tiles, (long)INT32_MAX), cus) * (long)(6 + mt);
-    if (best_cost < 0 || cost < best_cost) {
-      best = pl;
-      best_cost = cost;
-    }
+namespace {
+
+struct PartCost {
+  int mt, row_blocks, groups;
+  long cost;
+};
+
+// tile height for a column range of `cols` columns, charged rounds x (6 + MT)
+PartCost best_part(int m, int cols, int cw, int cus, std::initializer_list<int> mts) {
+  PartCost best{0, 0, 0, -1};
+  for (int mt : mts) {
+    const int rb = cdiv(m, 32 * mt), g = cdiv(cols, cw);
+    const long cost = (long)cdiv(rb * g, cus) * (6 + mt);
+    if (best.cost < 0 || cost < best.cost) best = {mt, rb, g, cost};
   }
   return best;
 }
+
+}  // namespace
+
+PrefillPlan prefill_plan(int m, int n, int k, int nmat) {
+  (void)k;
+  // Tile height: 32 * MT rows.  A workgroup's time per K step grows with MT
+  // plus a part that does not (weight groups, B dequantization, the step
+  // barrier): measured about 6 MT-units of fixed cost per step.  Persistent
+  // workgroups walk the tiles in rounds of one per CU, so a column range is
+  // charged rounds x (6 + MT) and the cheapest height wins (ties to the
+  // taller tile, which reuses each weight fragment most).  When the tiles
+  // overflow their last round, the columns may instead be split: a first
+  // launch over whole rounds of tall tiles, a second over the remaining
+  // column groups with short tiles that fill one round.
+  const int cus = device_cus();
+  const int nbc = nmat == 2 ? 1 : 2;
+  const int cw = kWaves * 32 * nbc;  // columns per column group
+  PrefillPlan pl{};
+  pl.nbc = nbc;
+  const PartCost one = best_part(m, n, cw, cus, {8, 6, 5, 4, 2});
+  pl.mt = one.mt;
+  pl.row_blocks = one.row_blocks;
+  pl.groups = one.groups;
+  pl.n_bulk = n;
+  long best_cost = one.cost;
+  for (int mt : {8, 6, 5, 4}) {
+    const int rb = cdiv(m, 32 * mt), g = cdiv(n, cw);
+    const long tiles = (long)rb * g;
+    if (tiles <= cus) continue;
+    const int gb = (int)((tiles / cus) * cus / rb);  // column groups in whole rounds
+    if (gb <= 0 || gb >= g) continue;
+    const PartCost rest = best_part(m, n - gb * cw, cw, cus, {8, 6, 5, 4, 2});
+    const long cost = (long)cdiv(gb * rb, cus) * (6 + mt) + rest.cost;
+    if (cost < best_cost) {
+      best_cost = cost;
+      pl.mt = mt;
+      pl.row_blocks = rb;
+      pl.groups = gb;
+      pl.n_bulk = gb * cw;
+      pl.mt2 = rest.mt;
+      pl.row_blocks2 = rest.row_blocks;
+      pl.groups2 = rest.groups;
+    }
+  }
+  pl.nwg = std::max(1, std::min(cus, pl.row_blocks * pl.groups));
+  pl.nwg2 = pl.n_bulk < n ? std::max(1, std::min(cus, pl.row_blocks2 * pl.groups2)) : 0;
+  return pl;
+}
+
+namespace {
+
+hipError_t launch_part(PrefillArgs p, int nmat, int mt, hipStream_t stream) {
+  dim3 grid(p.nwg), block(kWaves * 64);
+  switch ((nmat == 2 ? 100 : 0) + mt) {
+    case 108: hipLaunchKernelGGL((k_prefill<8, 1, true>), grid, block, 0, stream, p); break;
+    case 106: hipLaunchKernelGGL((k_prefill<6, 1, true>), grid, block, 0, stream, p); break;
+    case 105: hipLaunchKernelGGL((k_prefill<5, 1, true>), grid, block, 0, stream, p); break;
+    case 104: hipLaunchKernelGGL((k_prefill<4, 1, true>), grid, block, 0, stream, p); break;
+    case 102: hipLaunchKernelGGL((k_prefill<2, 1, true>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((k_prefill<8, 2, false>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((k_prefill<6, 2, false>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((k_prefill<5, 2, false>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_prefill<4, 2, false>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_prefill<2, 2, false>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat, const MatRef *w, void *y,
                           const PrefillPlan &pl, hipStream_t stream) {
@@ -384,30 +446,26 @@ hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat, const Ma
   p.x = x;
   p.m = m;
   p.k = k;
-  p.n = n;
-  p.codes0 = w[0].codes;
-  p.scales0 = w[0].scales;
+  p.ldy = n;
   p.ts0 = w[0].ts;
-  p.codes1 = nmat > 1 ? w[1].codes : nullptr;
-  p.scales1 = nmat > 1 ? w[1].scales : nullptr;
   p.ts1 = nmat > 1 ? w[1].ts : 0.f;
-  p.y = y;
-  p.row_blocks = pl.row_blocks;
-  p.groups = pl.groups;
-  p.nwg = pl.nwg;
-  dim3 grid(pl.nwg), block(kWaves * 64);
-  switch ((nmat == 2 ? 100 : 0) + pl.mt) {
-    case 108: hipLaunchKernelGGL((k_prefill<8, 1, true>), grid, block, 0, stream, p); break;
-    case 106: hipLaunchKernelGGL((k_prefill<6, 1, true>), grid, block, 0, stream, p); break;
-    case 105: hipLaunchKernelGGL((k_prefill<5, 1, true>), grid, block, 0, stream, p); break;
-    case 104: hipLaunchKernelGGL((k_prefill<4, 1, true>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((k_prefill<8, 2, false>), grid, block, 0, stream, p); break;
-    case 6: hipLaunchKernelGGL((k_prefill<6, 2, false>), grid, block, 0, stream, p); break;
-    case 5: hipLaunchKernelGGL((k_prefill<5, 2, false>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((k_prefill<4, 2, false>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  // columns [c0, c0 + cols) of every matrix and of y
+  auto part = [&](int c0, int cols, int mt, int rb, int groups, int nwg) {
+    const size_t cb = (size_t)c0 * (size_t)(k / 2), sb = (size_t)c0 * (size_t)(k / 16);
+    p.n = cols;
+    p.codes0 = w[0].codes + cb;
+    p.scales0 = w[0].scales + sb;
+    p.codes1 = nmat > 1 ? w[1].codes + cb : nullptr;
+    p.scales1 = nmat > 1 ? w[1].scales + sb : nullptr;
+    p.y = (uint8_t *)y + (size_t)c0 * 2;
+    p.row_blocks = rb;
+    p.groups = groups;
+    p.nwg = nwg;
+    return launch_part(p, nmat, mt, stream);
+  };
+  hipError_t e = part(0, pl.n_bulk, pl.mt, pl.row_blocks, pl.groups, pl.nwg);
+  if (e != hipSuccess || pl.n_bulk >= n) return e;
+  return part(pl.n_bulk, n - pl.n_bulk, pl.mt2, pl.row_blocks2, pl.groups2, pl.nwg2);
 }
 
 }  // namespace nvfp4

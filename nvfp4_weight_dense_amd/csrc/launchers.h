@@ -83,15 +83,19 @@ hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat,
                          hipStream_t stream);
 
 // Many-row projection (bf16 activations, k % 256 == 0): tiles of 32*mt rows
-// (mt in {8, 6, 5, 4}, chosen per shape) x 128 (nmat 2, gate+up+silu fused)
-// or 256 (nmat 1) columns over the whole K, walked by one persistent
-// workgroup per CU.  Needs no scratch.
+// (mt in {8, 6, 5, 4, 2}, chosen per shape) x 128 (nmat 2, gate+up+silu
+// fused) or 256 (nmat 1) columns over the whole K, walked by one persistent
+// workgroup per CU.  Columns [0, n_bulk) take one launch; when n_bulk < n
+// the rest take a second launch with tiles of 32*mt2 rows.  Needs no
+// scratch.
 struct PrefillPlan {
   int mt;    // 32-row tiles per tile
   int nbc;   // 32-column tiles per wave and matrix
   int row_blocks;
   int groups;  // column groups
   int nwg;     // persistent workgroups
+  int n_bulk;  // columns of the first launch
+  int mt2, row_blocks2, groups2, nwg2;  // second launch (n_bulk < n)
 };
 PrefillPlan prefill_plan(int m, int n, int k, int nmat);
 hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat,
