@@ -231,7 +231,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed calls before the timed ones (about 10 ms of decode work: "
+                         "kernels in the first ~40 ms of a process run slower)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true",
                     help="time only the decode workload (for profiling runs)")
