@@ -86,6 +86,10 @@ def lib():
         for f in ("nvo_dense_ffn", "nvo_dense_ffn_w4a4"):
             getattr(L, f).argtypes = [vp, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp, ip]
             getattr(L, f).restype = ip
+        L.nvo_lora_delta.argtypes = [vp, ip, ip, vp, ip, vp, vp]
+        L.nvo_lora_delta.restype = ip
+        L.nvo_dense_ffn_lora.argtypes = [vp, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip]
+        L.nvo_dense_ffn_lora.restype = ip
         _lib = L
     return _lib
 
@@ -252,3 +256,65 @@ def dense_ffn(x: np.ndarray, wg: Weight, wu: Weight, wd: Weight, w4a4: bool = Fa
     if intermediates:
         return y, ye, g, u, a
     return y, ye
+
+
+class _Lora(ctypes.Structure):
+    _fields_ = [
+        ("a", ctypes.c_void_p),
+        ("b", ctypes.c_void_p),
+        ("r", ctypes.c_int),
+        ("scale", ctypes.c_float),
+    ]
+
+
+@dataclass
+class Lora:
+    """One LoRA pair: ``a`` bf16 bits [r, k], ``b`` bf16 bits [n, r]; dW = scale * B . A."""
+    a: np.ndarray
+    b: np.ndarray
+    scale: float = 1.0
+
+    def _struct(self) -> "_Lora":
+        self.a = _u16(self.a)
+        self.b = _u16(self.b)
+        return _Lora(self.a.ctypes.data, self.b.ctypes.data, int(self.a.shape[0]), float(self.scale))
+
+
+def _lora_ref(l):
+    return None if l is None else ctypes.byref(l._struct())
+
+
+def lora_delta(x: np.ndarray, l: Lora, base: np.ndarray):
+    """Returns (bf16(base + dW . x) bits, the double value before rounding)."""
+    x = _u16(x)
+    out = _u16(base).copy()
+    m, k = x.shape
+    n = out.shape[1]
+    ex = np.empty(out.shape, dtype=np.float64)
+    s = l._struct()
+    rc = lib().nvo_lora_delta(x.ctypes.data, m, k, ctypes.byref(s), n, out.ctypes.data,
+                              ex.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle lora_delta: bad shape")
+    return out, ex
+
+
+def dense_ffn_lora(x: np.ndarray, wg: Weight, wu: Weight, wd: Weight, lg: Lora | None,
+                   lu: Lora | None, ld: Lora | None, nthreads: int = 0,
+                   intermediates: bool = False):
+    """W4A16 FFN with LoRA pairs (None = absent).  Returns (y, y_exact[, a])."""
+    x = _u16(x)
+    m, hidden = x.shape
+    inter = wg.n
+    y = np.empty((m, hidden), dtype=np.uint16)
+    ye = np.empty((m, hidden), dtype=np.float64)
+    a = np.empty((m, inter), dtype=np.uint16)
+    structs = [None if l is None else l._struct() for l in (lg, lu, ld)]
+    refs = [None if s is None else ctypes.byref(s) for s in structs]
+    sg, su, sd = wg._struct(), wu._struct(), wd._struct()
+    rc = lib().nvo_dense_ffn_lora(x.ctypes.data, m, hidden, inter, ctypes.byref(sg),
+                                  ctypes.byref(su), ctypes.byref(sd), refs[0], refs[1], refs[2],
+                                  y.ctypes.data, ye.ctypes.data, a.ctypes.data, nthreads)
+    if rc != 0:
+        raise ValueError("oracle dense_ffn_lora: bad shapes")
+    return (y, ye, a) if intermediates else (y, ye)

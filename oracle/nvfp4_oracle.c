@@ -393,3 +393,67 @@ int nvo_dense_ffn_w4a4(const uint16_t *x, int m, int hidden, int inter,
   return dense_ffn(1, x, m, hidden, inter, wg, wu, wd, y, y_exact, g, u, a,
                    nthreads);
 }
+
+/* ---- LoRA overlay (page layers/dense_ffn_overlays.rs) -----------------------
+ * The delta of one pair is dW . input with dW = scale * B . A, taken in two
+ * products as the overlay does (first xa = input . A^T, then xa . B^T), in
+ * double; it is added to the bf16 base and rounded once. */
+
+static int lora_present(const nvo_lora *l) { return l && l->r > 0 && l->a && l->b; }
+
+int nvo_lora_delta(const uint16_t *x, int m, int k, const nvo_lora *l, int n,
+                   uint16_t *base, double *base_exact) {
+  if (m < 0 || k <= 0 || n <= 0 || !base) return -1;
+  if (!lora_present(l)) {
+    if (base_exact)
+      for (size_t i = 0; i < (size_t)m * n; i++) base_exact[i] = nvo_bf16_value(base[i]);
+    return 0;
+  }
+  const int r = l->r;
+  double *xa = (double *)malloc(sizeof(double) * (size_t)r);
+  for (int i = 0; i < m; i++) {
+    const uint16_t *xi = x + (size_t)i * k;
+    for (int j = 0; j < r; j++) {
+      const uint16_t *aj = l->a + (size_t)j * k;
+      double s = 0.0;
+      for (int kk = 0; kk < k; kk++) s += nvo_bf16_value(xi[kk]) * nvo_bf16_value(aj[kk]);
+      xa[j] = s;
+    }
+    for (int c = 0; c < n; c++) {
+      const uint16_t *bc = l->b + (size_t)c * r;
+      double d = 0.0;
+      for (int j = 0; j < r; j++) d += xa[j] * nvo_bf16_value(bc[j]);
+      const double v = nvo_bf16_value(base[(size_t)i * n + c]) + (double)l->scale * d;
+      if (base_exact) base_exact[(size_t)i * n + c] = v;
+      base[(size_t)i * n + c] = nvo_bf16_from_double(v);
+    }
+  }
+  free(xa);
+  return 0;
+}
+
+int nvo_dense_ffn_lora(const uint16_t *x, int m, int hidden, int inter,
+                       const nvo_weight *wg, const nvo_weight *wu,
+                       const nvo_weight *wd, const nvo_lora *lg,
+                       const nvo_lora *lu, const nvo_lora *ld, uint16_t *y,
+                       double *y_exact, uint16_t *a, int nthreads) {
+  if (m < 0 || !ffn_shapes_ok(hidden, inter, wg, wu, wd)) return -1;
+  if (m == 0) return 0;
+  size_t mi = (size_t)m * inter;
+  uint16_t *gb = (uint16_t *)malloc(2 * mi);
+  uint16_t *ub = (uint16_t *)malloc(2 * mi);
+  uint16_t *ab = a ? a : (uint16_t *)malloc(2 * mi);
+  nvo_gemm_w4a16(x, m, wg, gb, NULL, nthreads);
+  nvo_gemm_w4a16(x, m, wu, ub, NULL, nthreads);
+  int rc = nvo_lora_delta(x, m, hidden, lg, inter, gb, NULL);
+  if (!rc) rc = nvo_lora_delta(x, m, hidden, lu, inter, ub, NULL);
+  if (!rc) {
+    nvo_silu_mul(gb, ub, ab, (int64_t)mi);
+    nvo_gemm_w4a16(ab, m, wd, y, y_exact, nthreads);
+    if (lora_present(ld)) rc = nvo_lora_delta(ab, m, inter, ld, hidden, y, y_exact);
+  }
+  free(gb);
+  free(ub);
+  if (!a) free(ab);
+  return rc;
+}

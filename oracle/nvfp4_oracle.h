@@ -21,6 +21,11 @@
  *   - the dense FFN: gate, up, silu_mul, down (page
  *     layers/dense_ffn_fixed.rs, `forward_fixed`; page
  *     layers/dense_ffn_prefill.rs, `forward_prefill_inner`).
+ *   - the LoRA overlay on it (page layers/dense_ffn_overlays.rs,
+ *     `apply_lora_gate_up` and `apply_lora_down`): base += dW . input for
+ *     m rows, with dW = scale * B . A a low-rank pair; gate and up get their
+ *     deltas after the projections and before silu_mul, the output its
+ *     delta after the down projection, with silu(gate)*up as input.
  *
  * Layout (host memory, row-major):
  *   x, g, u, a, y : bf16 bit patterns (uint16_t) [rows][cols]
@@ -89,6 +94,31 @@ int nvo_dense_ffn_w4a4(const uint16_t *x, int m, int hidden, int inter,
                        const nvo_weight *wg, const nvo_weight *wu,
                        const nvo_weight *wd, uint16_t *y, double *y_exact,
                        uint16_t *g, uint16_t *u, uint16_t *a, int nthreads);
+
+/* One LoRA pair: a bf16 [r][k], b bf16 [n][r], dW = scale * B . A; r == 0
+ * (or a null pointer) means no pair. */
+typedef struct {
+  const uint16_t *a; /* [r][k] */
+  const uint16_t *b; /* [n][r] */
+  int r;
+  float scale;
+} nvo_lora;
+
+/* base[m][n] = bf16(base + scale * sum_j (sum_k x[i][k] A[j][k]) B[c][j]),
+ * in place; base_exact (optional) receives the double before rounding.
+ * Returns 0, or -1 on a shape error. */
+int nvo_lora_delta(const uint16_t *x, int m, int k, const nvo_lora *l, int n,
+                   uint16_t *base, double *base_exact);
+
+/* Dense SwiGLU FFN (W4A16) with LoRA pairs on gate, up and down (any may
+ * be absent): g = bf16(x.Wg^T) then g += dWg . x; u likewise; a =
+ * silu_mul(g, u); y = bf16(a.Wd^T) then y += dWd . a.  y_exact is the
+ * double value of the last step before its rounding. */
+int nvo_dense_ffn_lora(const uint16_t *x, int m, int hidden, int inter,
+                       const nvo_weight *wg, const nvo_weight *wu,
+                       const nvo_weight *wd, const nvo_lora *lg,
+                       const nvo_lora *lu, const nvo_lora *ld, uint16_t *y,
+                       double *y_exact, uint16_t *a, int nthreads);
 
 #ifdef __cplusplus
 }
