@@ -75,7 +75,7 @@ def _time_loop(fn, reps, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
-def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False):
+def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=0):
     import torch
 
     import nvfp4_weight_dense_amd as nv
@@ -90,7 +90,16 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False):
     xd = x.to(dev)
     out = torch.empty((m, hidden), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    if fused:
+    if lora_rank:
+        # rank-r pairs on gate, up and down (small: shared by every replica)
+        def pair(n, k, which, scale):
+            a, b = si.lora_pair(n, k, lora_rank, which=which)
+            return nv.LoraPair(a.to(dev), b.to(dev), scale)
+        lp = (pair(inter, hidden, 0, 2.0), pair(inter, hidden, 1, -1.5), pair(hidden, inter, 2, 0.5))
+        reps = _replicas((wg, wu, wd), nrep, dev)
+        fn = lambda xx, g, u, d, out, stream: nv.dense_ffn_forward_lora(xx, g, u, d, *lp, out=out,
+                                                                         stream=stream)
+    elif fused:
         # one [2*inter, hidden] buffer holding gate then up (same bytes)
         assert wg.ts == wu.ts and not w4a4
         wgu = si.NvWeight(torch.cat([wg.codes, wu.codes]), torch.cat([wg.scales, wu.scales]), wg.ts)
@@ -103,7 +112,8 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False):
     flops = 6.0 * m * hidden * inter
     res = {
         "workload": f"{name} m={m} hidden={hidden} inter={inter}" + (" w4a4" if w4a4 else "")
-                    + (" fused gate+up weight" if fused else ""),
+                    + (" fused gate+up weight" if fused else "")
+                    + (f" + LoRA rank {lora_rank} on gate, up, down" if lora_rank else ""),
         "m": m, "hidden": hidden, "inter": inter,
         "ms_per_step": ms,
         "tflops": flops / (ms * 1e-3) / 1e12,
@@ -264,15 +274,17 @@ def main():
     del ctx
     workloads = []
     if not args.only_headline:
-        for name, steps, w4a4, m, fused in (
-                ("decode", args.steps, False, None, True),
-                ("smallm", max(20, args.steps // 2), False, None, False),
-                ("prefill", max(5, args.steps // 20), False, None, False),
-                ("w4a4", max(20, args.steps // 2), True, 1, False),
-                ("w4a4", max(20, args.steps // 2), True, 8, False),
-                ("w4a4", max(20, args.steps // 2), True, 64, False),
-                ("w4a4", max(5, args.steps // 20), True, 512, False)):
-            r, c = measure_ffn(name, steps, max(3, args.warmup // 2), w4a4=w4a4, m=m, fused=fused)
+        for name, steps, w4a4, m, fused, rank in (
+                ("decode", args.steps, False, None, True, 0),
+                ("decode", args.steps, False, None, False, 16),
+                ("smallm", max(20, args.steps // 2), False, None, False, 0),
+                ("prefill", max(5, args.steps // 20), False, None, False, 0),
+                ("w4a4", max(20, args.steps // 2), True, 1, False, 0),
+                ("w4a4", max(20, args.steps // 2), True, 8, False, 0),
+                ("w4a4", max(20, args.steps // 2), True, 64, False, 0),
+                ("w4a4", max(5, args.steps // 20), True, 512, False, 0)):
+            r, c = measure_ffn(name, steps, max(3, args.warmup // 2), w4a4=w4a4, m=m, fused=fused,
+                               lora_rank=rank)
             del c
             torch.cuda.empty_cache()
             workloads.append(r)

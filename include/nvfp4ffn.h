@@ -154,6 +154,47 @@ int dense_ffn_forward_fused(const void *x, int32_t m, int32_t hidden,
                             int32_t inter, const nvfp4_weight *wgu,
                             const nvfp4_weight *wd, void *out, void *stream);
 
+/* One LoRA pair: dW = scale * B . A, with
+ *   a: device bf16 [rank][k] (row-major, K contiguous),
+ *   b: device bf16 [n][rank],
+ * rank a multiple of 8 and at most 256 (0: no pair; a and b may then be
+ * null).  Both buffers 16-byte aligned and owned by the caller. */
+typedef struct nvfp4_lora_pair {
+  const void *a;
+  const void *b;
+  int32_t rank;
+  float scale;
+} nvfp4_lora_pair;
+
+/* The LoRA overlay of one FFN: gate and up pairs act on x ([inter][hidden]
+ * deltas), the down pair on act ([hidden][inter]). */
+typedef struct nvfp4_lora {
+  nvfp4_lora_pair gate, up, down;
+} nvfp4_lora;
+
+/* base[m][n] = bf16(base + scale * sum_j (sum_k x[i][k] a[j][k]) b[c][j]),
+ * in place: x bf16 [m][k] (k % 8 == 0), base bf16 [m][n].  x . A^T is
+ * formed in fp32 first, then its product with B^T (page
+ * layers/dense_ffn_overlays.rs, `apply_lora_gate_up`: the overlay keeps
+ * an x.A^T buffer and a delta buffer).  rank 0 is a no-op.  NVFP4_EINVAL
+ * for null or misaligned pointers, NVFP4_ESHAPE for a rank that is not a
+ * multiple of 8 or above 256, or k % 8 != 0. */
+int nvfp4_lora_delta(const void *x, int32_t m, int32_t k,
+                     const nvfp4_lora_pair *pair, int32_t n, void *base,
+                     void *stream);
+
+/* Dense SwiGLU FFN, W4A16, with a LoRA overlay (page
+ * layers/dense_ffn_overlays.rs, `set_lora_weights`, `apply_lora_gate_up`,
+ * `apply_lora_down`; the overlay needs gate and up materialized, so this
+ * takes the split path): gate = bf16(x.Wg^T) then gate += dWg . x; up
+ * likewise; act = bf16(silu(gate) * up); out = bf16(act.Wd^T) then out +=
+ * dWd . act.  lora == NULL or every rank 0 runs dense_ffn_forward.  Errors
+ * as dense_ffn_forward and nvfp4_lora_delta. */
+int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden,
+                           int32_t inter, const nvfp4_weight *wg,
+                           const nvfp4_weight *wu, const nvfp4_weight *wd,
+                           const nvfp4_lora *lora, void *out, void *stream);
+
 /* The calling thread's last error message ("" if none). */
 const char *nvfp4_last_error(void);
 

@@ -33,7 +33,8 @@ __all__ = [
     "NVFP4Weight", "Nvfp4Error", "Nvfp4LibraryMissing",
     "nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "nvfp4_quantize_rows", "silu_mul",
     "nvfp4_gate_up_silu_w4a16", "dense_ffn_forward", "dense_ffn_forward_w4a4",
-    "nvfp4_gate_up_views", "dense_ffn_forward_fused",
+    "nvfp4_gate_up_views", "dense_ffn_forward_fused", "LoraPair", "nvfp4_lora_delta",
+    "dense_ffn_forward_lora",
     "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
 ]
 
@@ -56,6 +57,27 @@ class _CWeight(ctypes.Structure):
         ("n", ctypes.c_int32),
         ("k", ctypes.c_int32),
     ]
+
+
+class _CLoraPair(ctypes.Structure):
+    _fields_ = [
+        ("a", ctypes.c_void_p),
+        ("b", ctypes.c_void_p),
+        ("rank", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class _CLora(ctypes.Structure):
+    _fields_ = [("gate", _CLoraPair), ("up", _CLoraPair), ("down", _CLoraPair)]
+
+
+@dataclass
+class LoraPair:
+    """One LoRA pair on the GPU: dW = scale * b . a, a bf16 [rank, k], b bf16 [n, rank]."""
+    a: torch.Tensor
+    b: torch.Tensor
+    scale: float = 1.0
 
 
 @dataclass
@@ -90,6 +112,8 @@ def load_library(path: str = LIB_PATH):
         "dense_ffn_forward_w4a4": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
         "nvfp4_gate_up_views": [wp, wp, wp],
         "dense_ffn_forward_fused": [vp, i32, i32, i32, wp, wp, vp, vp],
+        "nvfp4_lora_delta": [vp, i32, i32, ctypes.POINTER(_CLoraPair), i32, vp, vp],
+        "dense_ffn_forward_lora": [vp, i32, i32, i32, wp, wp, wp, ctypes.POINTER(_CLora), vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -271,4 +295,42 @@ def dense_ffn_forward_fused(x: torch.Tensor, wgu, wd, out: torch.Tensor | None =
         out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
     _check(L.dense_ffn_forward_fused(_ptr(x), m, hidden, inter, ctypes.byref(cgu), ctypes.byref(cd),
                                      _ptr(out), _stream(stream)))
+    return out
+
+
+def _clora_pair(p: LoraPair | None) -> _CLoraPair:
+    if p is None:
+        return _CLoraPair(None, None, 0, 0.0)
+    for t, nm in ((p.a, "a"), (p.b, "b")):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"lora {nm}: expected a contiguous 2-D bfloat16 GPU tensor")
+    if p.a.shape[0] != p.b.shape[1]:
+        raise ValueError("lora: a is [rank, k] and b is [n, rank]")
+    return _CLoraPair(p.a.data_ptr(), p.b.data_ptr(), int(p.a.shape[0]), float(p.scale))
+
+
+def nvfp4_lora_delta(x: torch.Tensor, pair: LoraPair, base: torch.Tensor, stream=None):
+    """base += pair.scale * (x . a^T) . b^T in place (bf16 base [m, n])."""
+    L = load_library()
+    x = _act(x, "x")
+    base = _act(base, "base")
+    cp = _clora_pair(pair)
+    _check(L.nvfp4_lora_delta(_ptr(x), x.shape[0], x.shape[1], ctypes.byref(cp), base.shape[1],
+                              _ptr(base), _stream(stream)))
+    return base
+
+
+def dense_ffn_forward_lora(x: torch.Tensor, wg, wu, wd, gate: LoraPair | None = None,
+                           up: LoraPair | None = None, down: LoraPair | None = None,
+                           out: torch.Tensor | None = None, stream=None):
+    """W4A16 dense SwiGLU FFN with a LoRA overlay on gate, up and down."""
+    L = load_library()
+    x = _act(x, "x")
+    cg, cu, cd = _cweight(wg), _cweight(wu), _cweight(wd)
+    m, hidden = x.shape
+    if out is None:
+        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
+    cl = _CLora(_clora_pair(gate), _clora_pair(up), _clora_pair(down))
+    _check(L.dense_ffn_forward_lora(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
+                                    ctypes.byref(cd), ctypes.byref(cl), _ptr(out), _stream(stream)))
     return out

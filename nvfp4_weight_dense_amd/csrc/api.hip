@@ -487,6 +487,85 @@ int dense_ffn_forward_fused(const void *x, int32_t m, int32_t hidden, int32_t in
   return dense_ffn_forward(x, m, hidden, inter, &wg, &wu, wd, out, stream);
 }
 
+int check_lora(const nvfp4_lora_pair *l, int k, int n, const char *name) {
+  if (!l || l->rank == 0) return NVFP4_OK;
+  if (l->rank < 0 || l->rank % 8 != 0 || l->rank > kMaxRank)
+    return fail(NVFP4_ESHAPE, "%s: rank=%d must be a multiple of 8 in 8..%d", name, l->rank, kMaxRank);
+  if (!l->a || !l->b) return fail(NVFP4_EINVAL, "%s: null a or b", name);
+  if (misaligned(l->a) || misaligned(l->b))
+    return fail(NVFP4_EINVAL, "%s: a and b must be 16-byte aligned", name);
+  if (k % 8 != 0) return fail(NVFP4_ESHAPE, "%s: k=%d is not a multiple of 8", name, k);
+  (void)n;
+  return NVFP4_OK;
+}
+
+bool lora_on(const nvfp4_lora_pair &l) { return l.rank > 0; }
+
+int nvfp4_lora_delta(const void *x, int32_t m, int32_t k, const nvfp4_lora_pair *pair, int32_t n,
+                     void *base, void *stream) {
+  g_err.clear();
+  int rc;
+  if (!pair) return fail(NVFP4_EINVAL, "lora_delta: null pair");
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(base, m, "base"))) return rc;
+  if (k <= 0 || n <= 0 || k > kMaxDim || n > kMaxDim)
+    return fail(NVFP4_ESHAPE, "lora_delta: k=%d n=%d out of range", k, n);
+  if ((rc = check_lora(pair, k, n, "lora_delta"))) return rc;
+  if (m == 0 || pair->rank == 0) return NVFP4_OK;
+  void *xa = nullptr;
+  if ((rc = arena_get(align256(4 * lora_xa_floats(m, pair->rank)), &xa))) return rc;
+  return hip_status(launch_lora_delta(x, m, k, pair->a, pair->b, pair->rank, n, pair->scale,
+                                      base, (float *)xa, (hipStream_t)stream),
+                    "lora delta launch");
+}
+
+int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden, int32_t inter,
+                           const nvfp4_weight *wg, const nvfp4_weight *wu, const nvfp4_weight *wd,
+                           const nvfp4_lora *lora, void *out, void *stream) {
+  g_err.clear();
+  int rc;
+  if (!lora || (!lora_on(lora->gate) && !lora_on(lora->up) && !lora_on(lora->down)))
+    return dense_ffn_forward(x, m, hidden, inter, wg, wu, wd, out, stream);
+  if ((rc = check_ffn(x, m, hidden, inter, wg, wu, wd, out))) return rc;
+  if ((rc = check_lora(&lora->gate, hidden, inter, "lora.gate")) ||
+      (rc = check_lora(&lora->up, hidden, inter, "lora.up")) ||
+      (rc = check_lora(&lora->down, inter, hidden, "lora.down")))
+    return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Path p_up, p_down;
+  if ((rc = path_or_fail(m, hidden, &p_up)) || (rc = path_or_fail(m, inter, &p_down))) return rc;
+  log_path("dense_ffn_forward_lora gate/up", path_name(p_up), m, inter, hidden);
+  log_path("dense_ffn_forward_lora down", path_name(p_down), m, hidden, inter);
+  // arena: gate (then act), up, xa, projection scratch
+  const size_t gu_b = align256((size_t)2 * m * inter);
+  const size_t xa_b = align256(4 * lora_xa_floats(m, kMaxRank));
+  size_t scr_b = proj_scratch_bytes(m, inter, hidden, 1, p_up);
+  const size_t down_b = proj_scratch_bytes(m, hidden, inter, 1, p_down);
+  if (down_b > scr_b) scr_b = down_b;
+  void *base = nullptr;
+  if ((rc = arena_get(2 * gu_b + xa_b + scr_b, &base))) return rc;
+  char *g = (char *)base, *u = g + gu_b;
+  float *xa = (float *)(u + gu_b);
+  char *scr = (char *)xa + xa_b;
+  ProfileScope ps("dense_total lora", m, s);
+  MatRef mg = mat(wg), mu = mat(wu), md = mat(wd);
+  const ActRef ax{x, nullptr, nullptr, nullptr};
+  if ((rc = run_proj(ax, m, hidden, inter, 1, &mg, g, scr, p_up, s)) ||
+      (rc = run_proj(ax, m, hidden, inter, 1, &mu, u, scr, p_up, s)))
+    return rc;
+  auto delta = [&](const void *in, int k, const nvfp4_lora_pair &l, int n, void *b) {
+    if (!lora_on(l)) return NVFP4_OK;
+    return hip_status(launch_lora_delta(in, m, k, l.a, l.b, l.rank, n, l.scale, b, xa, s),
+                      "lora delta launch");
+  };
+  if ((rc = delta(x, hidden, lora->gate, inter, g)) || (rc = delta(x, hidden, lora->up, inter, u)))
+    return rc;
+  if ((rc = hip_status(launch_silu_mul(g, u, g, (int64_t)m * inter, s), "silu_mul launch"))) return rc;
+  if ((rc = run_proj(ActRef{g, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &md, out, scr, p_down, s)))
+    return rc;
+  return delta(g, inter, lora->down, hidden, out);
+}
+
 int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, void *stream) {
   g_err.clear();
   int rc;

@@ -37,6 +37,7 @@ W4A4_ROW_COUNTS = (1, 8, 64, 512)
 
 # stream ids under one seed
 _X, _WG_C, _WG_S, _WU_C, _WU_S, _WD_C, _WD_S, _OUTLIER = range(8)
+_LORA = 8  # LoRA pairs: streams 8..13
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -83,6 +84,16 @@ def weight(n: int, k: int, seed: int, code_stream: int, scale_stream: int,
                    dtype=torch.float32) * -4.0
     scales = torch.exp2(u).to(torch.float8_e4m3fn).view(torch.uint8)
     return NvWeight(codes, scales.contiguous(), ts)
+
+
+def lora_pair(n: int, k: int, rank: int, seed: int = 0, which: int = 0):
+    """One LoRA pair (a bf16 [rank, k] ~ N(0, 1/k), b bf16 [n, rank] ~ N(0, 1)),
+    so that x . a^T has about the scale of x; ``which`` (0 gate, 1 up, 2 down)
+    picks the generator streams."""
+    sa, sb = _LORA + 2 * which, _LORA + 2 * which + 1
+    a = torch.randn((rank, k), generator=_gen(seed, sa), dtype=torch.float32) / (k ** 0.5)
+    b = torch.randn((n, rank), generator=_gen(seed, sb), dtype=torch.float32)
+    return a.to(torch.bfloat16), b.to(torch.bfloat16)
 
 
 def ffn_weights(hidden: int, inter: int, seed: int = 0):

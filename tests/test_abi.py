@@ -34,7 +34,8 @@ def test_header_declares_the_abi():
     names = _declared_functions()
     for want in ["nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "silu_mul", "dense_ffn_forward",
                  "dense_ffn_forward_w4a4", "nvfp4_quantize_rows", "nvfp4_gate_up_silu_w4a16",
-                 "nvfp4_gate_up_views", "dense_ffn_forward_fused",
+                 "nvfp4_gate_up_views", "dense_ffn_forward_fused", "nvfp4_lora_delta",
+                 "dense_ffn_forward_lora",
                  "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version"]:
         assert want in names
 
@@ -133,6 +134,33 @@ def test_gate_up_views_are_offsets_into_the_fused_buffer():
     assert "wgu must be" in nv.nvfp4_last_error()
     assert fn(x, 2, hidden, inter, ctypes.byref(fused), ctypes.byref(_w(inter, hidden)), out, s) \
         == nv.NVFP4_ESHAPE
+
+
+def test_lora_argument_checks():
+    L = _lib()
+    x, base, s = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x80000), ctypes.c_void_p(None)
+    P = nv._CLoraPair
+    assert L.nvfp4_lora_delta(x, 2, 64, None, 32, base, s) == nv.NVFP4_EINVAL
+    assert L.nvfp4_lora_delta(x, 2, 64, ctypes.byref(P(0x10000, 0x20000, 12, 1.0)), 32, base, s) \
+        == nv.NVFP4_ESHAPE
+    assert "multiple of 8" in nv.nvfp4_last_error()
+    assert L.nvfp4_lora_delta(x, 2, 64, ctypes.byref(P(0x10000, 0x20000, 264, 1.0)), 32, base, s) \
+        == nv.NVFP4_ESHAPE
+    assert L.nvfp4_lora_delta(x, 2, 64, ctypes.byref(P(None, 0x20000, 16, 1.0)), 32, base, s) \
+        == nv.NVFP4_EINVAL
+    assert L.nvfp4_lora_delta(x, 2, 60, ctypes.byref(P(0x10000, 0x20000, 16, 1.0)), 32, base, s) \
+        == nv.NVFP4_ESHAPE
+    # rank 0 and m == 0 are no-ops
+    assert L.nvfp4_lora_delta(x, 2, 64, ctypes.byref(P(None, None, 0, 1.0)), 32, base, s) == nv.NVFP4_OK
+    assert L.nvfp4_lora_delta(x, 0, 64, ctypes.byref(P(0x10000, 0x20000, 16, 1.0)), 32, base, s) \
+        == nv.NVFP4_OK
+    # the FFN checks every pair before any launch
+    hidden, inter = 64, 96
+    wg, wu, wd = _w(inter, hidden), _w(inter, hidden), _w(hidden, inter)
+    bad = nv._CLora(P(None, None, 0, 0.0), P(0x10000, 0x20000, 7, 1.0), P(None, None, 0, 0.0))
+    assert L.dense_ffn_forward_lora(x, 2, hidden, inter, ctypes.byref(wg), ctypes.byref(wu),
+                                    ctypes.byref(wd), ctypes.byref(bad), base, s) == nv.NVFP4_ESHAPE
+    assert "lora.up" in nv.nvfp4_last_error()
 
 
 def test_binding_refuses_cpu_tensors():

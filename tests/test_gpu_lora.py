@@ -1,0 +1,81 @@
+"""GPU parity of the LoRA overlay (nvfp4_lora_delta, dense_ffn_forward_lora)
+against the oracle, on seeded inputs.
+
+The delta alone has the usual bound (max|err| <= 2e-2 * rms of the oracle's
+value before its last rounding).  The FFN with the overlay rounds twice
+more than the plain FFN: gate/up and the output are rounded to bf16 before
+their deltas are added (the overlay updates bf16 buffers in place), and the
+GPU's and the oracle's first roundings may differ by one ulp.  Its bound
+adds that one rounding at the element's own magnitude:
+|err_i| <= 2e-2 * rms(ref) + 2^-7 * |ref_i| (one bf16 ulp is at most
+2^-7 of the value)."""
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_weight_dense_amd as nv
+import oracle
+import synthetic_inputs as si
+from gpu_helpers import assert_close, bf16_f64, bits, g_weight, o_weight, sync
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _pair(n, k, rank, which, scale, seed=0):
+    a, b = si.lora_pair(n, k, rank, seed=seed, which=which)
+    return (nv.LoraPair(a.cuda(), b.cuda(), scale),
+            oracle.Lora(bits(a), bits(b), scale))
+
+
+@pytest.mark.parametrize("m,k,n,rank", [(1, 4096, 3000, 16), (5, 512, 777, 8), (3, 12288, 4096, 64),
+                                        (70, 256, 768, 256)])
+def test_lora_delta_matches_oracle(m, k, n, rank):
+    _say(f"lora delta m={m} k={k} n={n} rank={rank}")
+    x = si.activations(m, k, seed=5)
+    base = si.activations(m, n, seed=6)
+    gp, op = _pair(n, k, rank, 0, 0.75)
+    got = nv.nvfp4_lora_delta(x.cuda(), gp, base.cuda().clone())
+    sync()
+    _, exact = oracle.lora_delta(bits(x), op, bits(base))
+    assert_close(bits(got), exact, "lora delta")
+    # the delta part alone, against the delta the oracle adds
+    d_gpu = got.cpu().double().numpy() - base.double().numpy()
+    d_ref = exact - base.double().numpy()
+    err = np.max(np.abs(d_gpu - d_ref)) / np.sqrt(np.mean(d_ref ** 2))
+    assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("name,m", [("tiny", 1), ("tiny", 4), ("tiny", 40), ("tiny", 70), ("decode", 1)])
+def test_dense_ffn_lora_matches_oracle(name, m):
+    _say(f"ffn lora {name} m={m}")
+    x, wg, wu, wd = si.workload(name, m=m)
+    hidden, inter = x.shape[1], wg.n
+    pg, og = _pair(inter, hidden, 16, 0, 2.0)
+    pu, ou = _pair(inter, hidden, 16, 1, -1.5)
+    pd, od = _pair(hidden, inter, 16, 2, 0.5)
+    y = nv.dense_ffn_forward_lora(x.cuda(), g_weight(wg), g_weight(wu), g_weight(wd), pg, pu, pd)
+    sync()
+    _, ye = oracle.dense_ffn_lora(bits(x), o_weight(wg), o_weight(wu), o_weight(wd), og, ou, od)
+    got = bf16_f64(bits(y))
+    assert np.all(np.isfinite(got))
+    bound = 2e-2 * np.sqrt(np.mean(ye ** 2)) + 2.0 ** -7 * np.abs(ye)
+    worst = np.max(np.abs(got - ye) / bound)
+    assert worst <= 1.0, f"ffn lora {name} m={m}: max err/bound = {worst:.3f}"
+    # the overlay changes the result by much more than the tolerance
+    _, ye0 = oracle.dense_ffn(bits(x), o_weight(wg), o_weight(wu), o_weight(wd))
+    assert np.max(np.abs(ye - ye0)) > 0.2 * np.sqrt(np.mean(ye0 ** 2))
+
+
+def test_dense_ffn_lora_without_pairs_is_dense_ffn():
+    _say("ffn lora, no pairs")
+    x, wg, wu, wd = si.workload("tiny", m=6)
+    W = [g_weight(w) for w in (wg, wu, wd)]
+    y0 = nv.dense_ffn_forward(x.cuda(), *W)
+    y1 = nv.dense_ffn_forward_lora(x.cuda(), *W)
+    sync()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
