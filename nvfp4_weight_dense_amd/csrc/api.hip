@@ -14,6 +14,7 @@
 // Every check runs before the first launch; a forced path that cannot serve a
 // shape is an error, never a silent fallback (the pages refuse to start with
 // a requested but missing variant: page layers/mod.rs, `w4a16_v2_kernel`).
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -512,7 +513,7 @@ int nvfp4_lora_delta(const void *x, int32_t m, int32_t k, const nvfp4_lora_pair 
   if ((rc = check_lora(pair, k, n, "lora_delta"))) return rc;
   if (m == 0 || pair->rank == 0) return NVFP4_OK;
   void *xa = nullptr;
-  if ((rc = arena_get(align256(4 * lora_xa_floats(m, pair->rank)), &xa))) return rc;
+  if ((rc = arena_get(align256(4 * lora_xa_floats(m, k, 1)), &xa))) return rc;
   return hip_status(launch_lora_delta(x, m, k, pair->a, pair->b, pair->rank, n, pair->scale,
                                       base, (float *)xa, (hipStream_t)stream),
                     "lora delta launch");
@@ -538,7 +539,7 @@ int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden, int32_t int
   log_path("dense_ffn_forward_lora down", path_name(p_down), m, hidden, inter);
   // arena: gate (then act), up, xa, projection scratch
   const size_t gu_b = align256((size_t)2 * m * inter);
-  const size_t xa_b = align256(4 * lora_xa_floats(m, kMaxRank));
+  const size_t xa_b = align256(4 * std::max(lora_xa_floats(m, hidden, 2), lora_xa_floats(m, inter, 1)));
   size_t scr_b = proj_scratch_bytes(m, inter, hidden, 1, p_up);
   const size_t down_b = proj_scratch_bytes(m, hidden, inter, 1, p_down);
   if (down_b > scr_b) scr_b = down_b;
@@ -553,17 +554,20 @@ int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden, int32_t int
   if ((rc = run_proj(ax, m, hidden, inter, 1, &mg, g, scr, p_up, s)) ||
       (rc = run_proj(ax, m, hidden, inter, 1, &mu, u, scr, p_up, s)))
     return rc;
-  auto delta = [&](const void *in, int k, const nvfp4_lora_pair &l, int n, void *b) {
-    if (!lora_on(l)) return NVFP4_OK;
-    return hip_status(launch_lora_delta(in, m, k, l.a, l.b, l.rank, n, l.scale, b, xa, s),
-                      "lora delta launch");
+  auto ref = [](const nvfp4_lora_pair &l) {
+    return lora_on(l) ? LoraRef{l.a, l.b, l.rank, l.scale} : LoraRef{nullptr, nullptr, 0, 0.f};
   };
-  if ((rc = delta(x, hidden, lora->gate, inter, g)) || (rc = delta(x, hidden, lora->up, inter, u)))
+  // gate and up deltas, then silu_mul, in one pass over gate/up (act over gate)
+  if ((rc = hip_status(launch_lora_gate_up_silu(x, m, hidden, ref(lora->gate), ref(lora->up), inter, g,
+                                                u, xa, s),
+                       "lora gate/up + silu launch")))
     return rc;
-  if ((rc = hip_status(launch_silu_mul(g, u, g, (int64_t)m * inter, s), "silu_mul launch"))) return rc;
   if ((rc = run_proj(ActRef{g, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &md, out, scr, p_down, s)))
     return rc;
-  return delta(g, inter, lora->down, hidden, out);
+  if (!lora_on(lora->down)) return NVFP4_OK;
+  return hip_status(launch_lora_delta(g, m, inter, lora->down.a, lora->down.b, lora->down.rank, hidden,
+                                      lora->down.scale, out, xa, s),
+                    "lora delta launch");
 }
 
 int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, void *stream) {

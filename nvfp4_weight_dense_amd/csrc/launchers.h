@@ -105,12 +105,21 @@ hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat,
 // Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above.
 // Eligible when K splits into at most 4 waves of register-resident granules.
 // LoRA delta: base[m][n] (bf16, in place) += scale * (x . A^T) . B^T with
-// A bf16 [r][k], B bf16 [n][r]; xa is fp32 [m][r] scratch.  r % 8 == 0,
-// r <= kMaxRank, k % 8 == 0.
+// A bf16 [r][k], B bf16 [n][r]; xa is fp32 scratch of lora_xa_floats(m, k,
+// pairs) floats.  r % 8 == 0, r <= kMaxRank, k % 8 == 0.
 constexpr int kMaxRank = 256;
-size_t lora_xa_floats(int m, int r);
+struct LoraRef {
+  const void *a, *b;
+  int r;  // 0: no pair
+  float scale;
+};
+size_t lora_xa_floats(int m, int k, int npairs);
 hipError_t launch_lora_delta(const void *x, int m, int k, const void *a, const void *b, int r, int n,
                              float scale, void *base, float *xa, hipStream_t stream);
+// gate and up deltas (from x) and silu_mul in one pass: g (bf16 [m][n])
+// receives act = bf16(silu(bf16(g + dg)) * bf16(u + du)).
+hipError_t launch_lora_gate_up_silu(const void *x, int m, int k, const LoraRef &lg, const LoraRef &lu,
+                                    int n, void *g, const void *u, float *xa, hipStream_t stream);
 
 bool gemv_eligible(int m, int k);
 hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat,

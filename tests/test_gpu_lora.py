@@ -71,6 +71,27 @@ def test_dense_ffn_lora_matches_oracle(name, m):
     assert np.max(np.abs(ye - ye0)) > 0.2 * np.sqrt(np.mean(ye0 ** 2))
 
 
+@pytest.mark.parametrize("which", ["gate", "up", "down"])
+def test_dense_ffn_lora_single_pair(which):
+    """Only one of the three pairs present (the others rank 0)."""
+    _say(f"ffn lora, {which} only")
+    x, wg, wu, wd = si.workload("tiny", m=3)
+    hidden, inter = x.shape[1], wg.n
+    shapes = {"gate": (inter, hidden, 0), "up": (inter, hidden, 1), "down": (hidden, inter, 2)}
+    n, k, w = shapes[which]
+    gp, op = _pair(n, k, 8, w, 1.25)
+    gpu = {which: gp}
+    orc = {which: op}
+    y = nv.dense_ffn_forward_lora(x.cuda(), g_weight(wg), g_weight(wu), g_weight(wd),
+                                  gpu.get("gate"), gpu.get("up"), gpu.get("down"))
+    sync()
+    _, ye = oracle.dense_ffn_lora(bits(x), o_weight(wg), o_weight(wu), o_weight(wd),
+                                  orc.get("gate"), orc.get("up"), orc.get("down"))
+    got = bf16_f64(bits(y))
+    bound = 2e-2 * np.sqrt(np.mean(ye ** 2)) + 2.0 ** -7 * np.abs(ye)
+    assert np.max(np.abs(got - ye) / bound) <= 1.0
+
+
 def test_dense_ffn_lora_without_pairs_is_dense_ffn():
     _say("ffn lora, no pairs")
     x, wg, wu, wd = si.workload("tiny", m=6)
