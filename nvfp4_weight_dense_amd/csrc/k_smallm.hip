@@ -23,8 +23,10 @@
 //     step ahead; the step barrier waits for LDS operations only, so weight
 //     and activation requests stay in flight.
 //   * deep K is split over workgroups (blockIdx.y) by whole weight groups;
-//     each split writes fp32 partial tiles and the last to arrive sums them
-//     in split order (deterministic), then runs the epilogue.
+//     each split writes fp32 partial tiles.  For gate+up (two splits at
+//     most on these shapes) the last split to arrive sums them in split
+//     order and runs the silu epilogue; for one matrix a second launch sums
+//     them in split order over the whole output in parallel.
 //
 // Lane (c = lane%32, h = lane/32) holds for weight row col+c the 32 codes at
 // K offset 32h of a step; MFMA j sums K offsets {8j..8j+7} U
@@ -273,6 +275,7 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
             st16_coherent(pres, pvoff, (uint32_t)((i * MT + mt) * 4 + e4) * 1024u, v);
           }
     }
+    if (!SWIGLU) return;  // k_smallm_reduce sums the splits
     wait_all_memory();
     __syncthreads();
     if (tid == 0) {
@@ -325,6 +328,45 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
   }
 }
 
+// The split sum of a one-matrix launch, in parallel over the whole output:
+// one thread per 16-byte partial chunk (four rows of one column), summing
+// the splits in split order -- the order the in-kernel sum of the fused
+// gate+up launch uses -- then the epilogue.  With one workgroup per tile
+// doing the sum, a deep K split left one CU per tile reading every split's
+// partials at the end of the launch.
+template <int MT>
+__global__ __launch_bounds__(256) void k_smallm_reduce(const float *__restrict__ partial, int tiles,
+                                                       int ksplit, int m, int n, float ts, void *y) {
+  constexpr int kRows = 32 * MT;
+  constexpr int kWaveFloats = kNB * kRows * 32;
+  constexpr int kChunks = kNB * MT * 4 * 64;  // 16-byte chunks per wave
+  const int gid = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (gid >= tiles * kNW * kChunks) return;
+  const int tile = gid / (kNW * kChunks);
+  const int rem = gid - tile * (kNW * kChunks);
+  const int wave = rem / kChunks;
+  const int q = (rem - wave * kChunks) >> 6, lane = rem & 63;
+  const int i = q / (4 * MT), mt = (q >> 2) % MT, e4 = q & 3;
+  const float4 *src = (const float4 *)(partial + ((size_t)tile * ksplit * kNW + wave) * kWaveFloats) +
+                      (size_t)q * 64 + lane;
+  const size_t split_stride = (size_t)kNW * kWaveFloats / 4;  // in float4
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < ksplit; ++sp) {
+    const float4 v = src[sp * split_stride];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const int col = (tile * kNW + wave) * 64 + 32 * i + (lane & 31);
+  if (col >= n) return;
+  const int row0 = 32 * mt + 8 * e4 + 4 * (lane >> 5);
+  const float v[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (row0 + t < m) ((__bf16 *)y)[(size_t)(row0 + t) * n + col] = (__bf16)(v[t] * ts);
+}
+
 }  // namespace
 
 bool smallm_eligible(int m, int k) { return m >= 17 && m <= 64 && k % 256 == 0; }
@@ -374,9 +416,21 @@ hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat, const Mat
   if (nmat == 2) {
     if (pl.mt == 1) hipLaunchKernelGGL((k_smallm<1, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((k_smallm<2, true>), grid, block, 0, stream, p);
-  } else {
-    if (pl.mt == 1) hipLaunchKernelGGL((k_smallm<1, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((k_smallm<2, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  if (pl.mt == 1) hipLaunchKernelGGL((k_smallm<1, false>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((k_smallm<2, false>), grid, block, 0, stream, p);
+  if (pl.ksplit > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int threads = pl.tiles * kNW * kNB * pl.mt * 4 * 64;
+    const dim3 rgrid((threads + 255) / 256);
+    if (pl.mt == 1)
+      hipLaunchKernelGGL((k_smallm_reduce<1>), rgrid, dim3(256), 0, stream, partial, pl.tiles, pl.ksplit, m,
+                         n, p.ts0, y);
+    else
+      hipLaunchKernelGGL((k_smallm_reduce<2>), rgrid, dim3(256), 0, stream, partial, pl.tiles, pl.ksplit, m,
+                         n, p.ts0, y);
   }
   return hipGetLastError();
 }
