@@ -90,6 +90,13 @@ def lib():
         L.nvo_lora_delta.restype = ip
         L.nvo_dense_ffn_lora.argtypes = [vp, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp, vp, ip]
         L.nvo_dense_ffn_lora.restype = ip
+        L.nvo_dequant_fp8.argtypes, L.nvo_dequant_fp8.restype = [vp, vp], None
+        L.nvo_quantize_rows_fp8.argtypes = [vp, ip, ip, vp, vp]
+        L.nvo_quantize_rows_fp8.restype = ip
+        L.nvo_gemm_w8a8.argtypes = [vp, ip, vp, vp, vp, ip]
+        L.nvo_gemm_w8a8.restype = ip
+        L.nvo_dense_ffn_w8a8.argtypes = [vp, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp, ip]
+        L.nvo_dense_ffn_w8a8.restype = ip
         _lib = L
     return _lib
 
@@ -318,3 +325,90 @@ def dense_ffn_lora(x: np.ndarray, wg: Weight, wu: Weight, wd: Weight, lg: Lora |
     if rc != 0:
         raise ValueError("oracle dense_ffn_lora: bad shapes")
     return (y, ye, a) if intermediates else (y, ye)
+
+
+# ---- W8A8 fixed format --------------------------------------------------------
+
+class _Fp8Weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("n", ctypes.c_int),
+        ("k", ctypes.c_int),
+    ]
+
+
+@dataclass
+class Fp8Weight:
+    """Block-scaled FP8 weight: ``codes`` uint8 E4M3 ``[n, k]``, ``scales``
+    float32 ``[ceil(n/128), ceil(k/128)]`` (one per 128 x 128 block)."""
+    codes: np.ndarray
+    scales: np.ndarray
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.codes.shape[1])
+
+    def _struct(self):
+        self.codes = np.ascontiguousarray(self.codes, dtype=np.uint8)
+        self.scales = np.ascontiguousarray(self.scales, dtype=np.float32)
+        assert self.scales.shape == ((self.n + 127) // 128, (self.k + 127) // 128)
+        return _Fp8Weight(self.codes.ctypes.data, self.scales.ctypes.data, self.n, self.k)
+
+
+def dequant_fp8(w: Fp8Weight) -> np.ndarray:
+    out = np.empty((w.n, w.k), dtype=np.float64)
+    s = w._struct()
+    lib().nvo_dequant_fp8(ctypes.byref(s), out.ctypes.data)
+    return out
+
+
+def quantize_rows_fp8(x: np.ndarray):
+    """Returns (codes uint8 [m, k] E4M3, row_scale f32 [m])."""
+    x = _u16(x)
+    m, k = x.shape
+    codes = np.zeros((m, k), dtype=np.uint8)
+    rs = np.zeros((m,), dtype=np.float32)
+    rc = lib().nvo_quantize_rows_fp8(x.ctypes.data, m, k, codes.ctypes.data, rs.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle quantize_rows_fp8: bad shape")
+    return codes, rs
+
+
+def gemm_w8a8(x: np.ndarray, w: Fp8Weight, nthreads: int = 0):
+    """Returns (y bf16 bits [m, n], y_exact float64 [m, n])."""
+    x = _u16(x)
+    m = x.shape[0]
+    y = np.empty((m, w.n), dtype=np.uint16)
+    ye = np.empty((m, w.n), dtype=np.float64)
+    s = w._struct()
+    rc = lib().nvo_gemm_w8a8(x.ctypes.data, m, ctypes.byref(s), y.ctypes.data,
+                             ye.ctypes.data, nthreads)
+    if rc != 0:
+        raise ValueError("oracle gemm_w8a8: bad shape")
+    return y, ye
+
+
+def dense_ffn_w8a8(x: np.ndarray, wg: Fp8Weight, wu: Fp8Weight, wd: Fp8Weight,
+                   nthreads: int = 0, intermediates: bool = False):
+    """W8A8 FFN.  Returns (y bf16 [m, hidden], y_exact f64[, g, u, a])."""
+    x = _u16(x)
+    m, hidden = x.shape
+    inter = wg.n
+    y = np.empty((m, hidden), dtype=np.uint16)
+    ye = np.empty((m, hidden), dtype=np.float64)
+    g = np.empty((m, inter), dtype=np.uint16)
+    u = np.empty((m, inter), dtype=np.uint16)
+    a = np.empty((m, inter), dtype=np.uint16)
+    sg, su, sd = wg._struct(), wu._struct(), wd._struct()
+    rc = lib().nvo_dense_ffn_w8a8(x.ctypes.data, m, hidden, inter, ctypes.byref(sg),
+                                  ctypes.byref(su), ctypes.byref(sd), y.ctypes.data,
+                                  ye.ctypes.data, g.ctypes.data, u.ctypes.data,
+                                  a.ctypes.data, nthreads)
+    if rc != 0:
+        raise ValueError("oracle dense_ffn_w8a8: bad shapes")
+    return (y, ye, g, u, a) if intermediates else (y, ye)

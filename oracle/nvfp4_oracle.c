@@ -168,10 +168,13 @@ void nvo_dequant(const nvo_weight *w, double *out) {
 
 /* ---- projection: y = x . W^T, double sums in ascending k ------------------ */
 
+typedef void (*row_decoder)(const void *w, int c, double *row);
+
 typedef struct {
   const double *xd; /* [m][k] activations as doubles */
-  int m;
-  const nvo_weight *w;
+  int m, n, k;
+  const void *w;
+  row_decoder decode; /* writes weight row c (k doubles) */
   uint16_t *y;
   double *y_exact;
   int c0, c1;
@@ -179,10 +182,10 @@ typedef struct {
 
 static void *proj_worker(void *arg) {
   proj_job *j = (proj_job *)arg;
-  int k = j->w->k, n = j->w->n;
+  int k = j->k, n = j->n;
   double *row = (double *)malloc(sizeof(double) * (size_t)k);
   for (int c = j->c0; c < j->c1; c++) {
-    dequant_row(j->w, c, row);
+    j->decode(j->w, c, row);
     for (int r = 0; r < j->m; r++) {
       const double *xr = j->xd + (size_t)r * k;
       double s = 0.0;
@@ -205,20 +208,25 @@ static int thread_count(int nthreads, int work) {
   return nthreads < 1 ? 1 : nthreads;
 }
 
-/* Projection of m rows whose activations are already doubles. */
-static void project(const double *xd, int m, const nvo_weight *w, uint16_t *y,
-                    double *y_exact, int nthreads) {
-  int nt = thread_count(nthreads, w->n);
+/* Projection of m rows whose activations are already doubles, against an
+ * [n][k] weight whose rows `decode` produces. */
+static void project_rows(const double *xd, int m, int n, int k, const void *w,
+                         row_decoder decode, uint16_t *y, double *y_exact,
+                         int nthreads) {
+  int nt = thread_count(nthreads, n);
   pthread_t th[256];
   proj_job jobs[256];
   for (int t = 0; t < nt; t++) {
     jobs[t].xd = xd;
     jobs[t].m = m;
+    jobs[t].n = n;
+    jobs[t].k = k;
     jobs[t].w = w;
+    jobs[t].decode = decode;
     jobs[t].y = y;
     jobs[t].y_exact = y_exact;
-    jobs[t].c0 = (int)((long long)w->n * t / nt);
-    jobs[t].c1 = (int)((long long)w->n * (t + 1) / nt);
+    jobs[t].c0 = (int)((long long)n * t / nt);
+    jobs[t].c1 = (int)((long long)n * (t + 1) / nt);
   }
   if (nt == 1) {
     proj_worker(&jobs[0]);
@@ -226,6 +234,15 @@ static void project(const double *xd, int m, const nvo_weight *w, uint16_t *y,
   }
   for (int t = 0; t < nt; t++) pthread_create(&th[t], NULL, proj_worker, &jobs[t]);
   for (int t = 0; t < nt; t++) pthread_join(th[t], NULL);
+}
+
+static void nvfp4_row(const void *w, int c, double *row) {
+  dequant_row((const nvo_weight *)w, c, row);
+}
+
+static void project(const double *xd, int m, const nvo_weight *w, uint16_t *y,
+                    double *y_exact, int nthreads) {
+  project_rows(xd, m, w->n, w->k, w, nvfp4_row, y, y_exact, nthreads);
 }
 
 int nvo_gemm_w4a16(const uint16_t *x, int m, const nvo_weight *w, uint16_t *y,
@@ -456,4 +473,109 @@ int nvo_dense_ffn_lora(const uint16_t *x, int m, int hidden, int inter,
   free(ub);
   if (!a) free(ab);
   return rc;
+}
+
+/* ---- W8A8 fixed format -----------------------------------------------------
+ * Page layers/dense_ffn_fixed.rs, `Fixed::W8a8` (the declared W8A8 layer:
+ * per-row FP8 activations at every row count, so a row's bits do not depend
+ * on the row count) and page layers/dense_ffn_overlays.rs, `set_fp8_weights`
+ * and `set_fp8_gate_up_fused` (block-scaled FP8 weights with a scale grid).
+ * The pages define neither grid nor activation recipe; the readings:
+ *   weight value W[c][kk] = e4m3(codes[c][kk]) * scales[c/128][kk/128],
+ *     one fp32 scale per 128 x 128 block, grid [ceil(n/128)][ceil(k/128)];
+ *   activation quantizer, per row, fp32 steps in this order:
+ *     1. amax = max |x| over the row;
+ *     2. s_row = amax / 448 (the largest E4M3 magnitude), or 1 for an
+ *        all-zero row;
+ *     3. code = E4M3(x / s_row): nearest, ties to even, saturating at 448,
+ *        sign kept;
+ *   x_hat = e4m3(code) * s_row, and y = bf16(sum_k x_hat * W) in double. */
+
+static int fp8_weight_ok(const nvo_fp8_weight *w) {
+  return w && w->codes && w->scales && w->n > 0 && w->k > 0;
+}
+
+static void fp8_row(const void *wv, int c, double *row) {
+  const nvo_fp8_weight *w = (const nvo_fp8_weight *)wv;
+  const uint8_t *cr = w->codes + (size_t)c * w->k;
+  const int kb = (w->k + 127) / 128;
+  const float *sr = w->scales + (size_t)(c / 128) * kb;
+  for (int kk = 0; kk < w->k; kk++)
+    row[kk] = nvo_e4m3_value(cr[kk]) * (double)sr[kk / 128];
+}
+
+void nvo_dequant_fp8(const nvo_fp8_weight *w, double *out) {
+  for (int c = 0; c < w->n; c++) fp8_row(w, c, out + (size_t)c * w->k);
+}
+
+int nvo_quantize_rows_fp8(const uint16_t *x, int m, int k, uint8_t *codes,
+                          float *row_scale) {
+  if (m < 0 || k <= 0) return -1;
+  for (int r = 0; r < m; r++) {
+    const uint16_t *xr = x + (size_t)r * k;
+    float amax = 0.0f;
+    for (int kk = 0; kk < k; kk++) {
+      float av = fabsf(bf16_to_float(xr[kk]));
+      if (av > amax) amax = av;
+    }
+    float s_row = amax / 448.0f;
+    if (amax == 0.0f) s_row = 1.0f;
+    row_scale[r] = s_row;
+    for (int kk = 0; kk < k; kk++) {
+      float q = bf16_to_float(xr[kk]) / s_row;
+      codes[(size_t)r * k + kk] = nvo_e4m3_encode(q);
+    }
+  }
+  return 0;
+}
+
+static double *fp8_rows_as_double(const uint16_t *x, int m, int k) {
+  uint8_t *qc = (uint8_t *)malloc((size_t)m * k);
+  float *rs = (float *)malloc(sizeof(float) * (size_t)m);
+  double *xd = (double *)malloc(sizeof(double) * (size_t)m * k);
+  nvo_quantize_rows_fp8(x, m, k, qc, rs);
+  for (int r = 0; r < m; r++)
+    for (int kk = 0; kk < k; kk++)
+      xd[(size_t)r * k + kk] = nvo_e4m3_value(qc[(size_t)r * k + kk]) * (double)rs[r];
+  free(qc);
+  free(rs);
+  return xd;
+}
+
+int nvo_gemm_w8a8(const uint16_t *x, int m, const nvo_fp8_weight *w,
+                  uint16_t *y, double *y_exact, int nthreads) {
+  if (!fp8_weight_ok(w) || m < 0 || (m > 0 && (!x || !y))) return -1;
+  if (m == 0) return 0;
+  double *xd = fp8_rows_as_double(x, m, w->k);
+  project_rows(xd, m, w->n, w->k, w, fp8_row, y, y_exact, nthreads);
+  free(xd);
+  return 0;
+}
+
+/* The W8A8 FFN: gate and up from the quantized input, silu_mul, then the
+ * down projection of the quantized activation (the same step order as the
+ * W4A4 arm of `forward_fixed`). */
+int nvo_dense_ffn_w8a8(const uint16_t *x, int m, int hidden, int inter,
+                       const nvo_fp8_weight *wg, const nvo_fp8_weight *wu,
+                       const nvo_fp8_weight *wd, uint16_t *y, double *y_exact,
+                       uint16_t *g, uint16_t *u, uint16_t *a, int nthreads) {
+  if (m < 0 || !fp8_weight_ok(wg) || !fp8_weight_ok(wu) || !fp8_weight_ok(wd) ||
+      wg->n != inter || wg->k != hidden || wu->n != inter || wu->k != hidden ||
+      wd->n != hidden || wd->k != inter)
+    return -1;
+  if (m == 0) return 0;
+  size_t mi = (size_t)m * inter;
+  uint16_t *gb = g ? g : (uint16_t *)malloc(2 * mi);
+  uint16_t *ub = u ? u : (uint16_t *)malloc(2 * mi);
+  uint16_t *ab = a ? a : (uint16_t *)malloc(2 * mi);
+  double *xd = fp8_rows_as_double(x, m, hidden);
+  project_rows(xd, m, inter, hidden, wg, fp8_row, gb, NULL, nthreads);
+  project_rows(xd, m, inter, hidden, wu, fp8_row, ub, NULL, nthreads);
+  free(xd);
+  nvo_silu_mul(gb, ub, ab, (int64_t)mi);
+  nvo_gemm_w8a8(ab, m, wd, y, y_exact, nthreads);
+  if (!g) free(gb);
+  if (!u) free(ub);
+  if (!a) free(ab);
+  return 0;
 }

@@ -26,6 +26,9 @@
  *     m rows, with dW = scale * B . A a low-rank pair; gate and up get their
  *     deltas after the projections and before silu_mul, the output its
  *     delta after the down projection, with silu(gate)*up as input.
+ *   - the W8A8 fixed format (page layers/dense_ffn_fixed.rs, `Fixed::W8a8`;
+ *     page layers/dense_ffn_overlays.rs, `set_fp8_weights`): block-scaled
+ *     FP8 weights, per-row FP8 activations, the same FFN step order.
  *
  * Layout (host memory, row-major):
  *   x, g, u, a, y : bf16 bit patterns (uint16_t) [rows][cols]
@@ -119,6 +122,26 @@ int nvo_dense_ffn_lora(const uint16_t *x, int m, int hidden, int inter,
                        const nvo_weight *wd, const nvo_lora *lg,
                        const nvo_lora *lu, const nvo_lora *ld, uint16_t *y,
                        double *y_exact, uint16_t *a, int nthreads);
+
+/* W8A8 fixed format (see the .c file for the readings): FP8 E4M3 weight
+ * codes [n][k] with one fp32 scale per 128 x 128 block, grid
+ * [ceil(n/128)][ceil(k/128)]; activations quantized per row to E4M3 with
+ * one fp32 scale per row. */
+typedef struct {
+  const uint8_t *codes; /* [n][k] E4M3 (FN) */
+  const float *scales;  /* [ceil(n/128)][ceil(k/128)] */
+  int n, k;
+} nvo_fp8_weight;
+
+void nvo_dequant_fp8(const nvo_fp8_weight *w, double *out);
+int nvo_quantize_rows_fp8(const uint16_t *x, int m, int k, uint8_t *codes,
+                          float *row_scale);
+int nvo_gemm_w8a8(const uint16_t *x, int m, const nvo_fp8_weight *w,
+                  uint16_t *y, double *y_exact, int nthreads);
+int nvo_dense_ffn_w8a8(const uint16_t *x, int m, int hidden, int inter,
+                       const nvo_fp8_weight *wg, const nvo_fp8_weight *wu,
+                       const nvo_fp8_weight *wd, uint16_t *y, double *y_exact,
+                       uint16_t *g, uint16_t *u, uint16_t *a, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -13,10 +13,15 @@ stand in for them):
 * ``smallm``   m=64, hidden=5120, inter=17408 (deep-K down projection)
 * ``prefill``  m=2048, hidden=5120, inter=17408, 1% of X entries x20
 * ``w4a4``     hidden=4096, inter=14336, m in {1, 8, 64, 512} sharing rows
+* ``w8a8``     the same shapes and rows, with block-scaled FP8 weights
 
 Weight recipe: E2M1 codes uniform over all 16 nibbles (so -0 appears),
 E4M3 block scales 2^u with u ~ U(-4, 0) cast to float8_e4m3fn by torch,
 tensor scale 1.0.  X ~ N(0, 1) cast to bf16 by torch.
+
+FP8 weight recipe (W8A8): E4M3 codes uniform over the 254 non-NaN bytes (so
+subnormals, -0 and +-448 appear), one fp32 scale per 128 x 128 block drawn
+as 2^u with u ~ U(-10, -6) (not powers of two in general).
 """
 
 from __future__ import annotations
@@ -31,13 +36,16 @@ WORKLOADS = {
     "smallm": dict(m=64, hidden=5120, inter=17408, outliers=False),
     "prefill": dict(m=2048, hidden=5120, inter=17408, outliers=True),
     "w4a4": dict(m=512, hidden=4096, inter=14336, outliers=False),
+    "w8a8": dict(m=512, hidden=4096, inter=14336, outliers=False),
 }
 
 W4A4_ROW_COUNTS = (1, 8, 64, 512)
+W8A8_ROW_COUNTS = (1, 8, 64, 512)
 
 # stream ids under one seed
 _X, _WG_C, _WG_S, _WU_C, _WU_S, _WD_C, _WD_S, _OUTLIER = range(8)
 _LORA = 8  # LoRA pairs: streams 8..13
+_FP8 = 16  # FP8 weights: streams 16..21 (codes, scales per matrix)
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -121,3 +129,46 @@ def exact_case(m: int, n: int, k: int, seed: int = 0):
     e = torch.randint(-4, 1, (n, k // 16), generator=_gen(seed, 102)).to(torch.float32)
     scales = torch.exp2(e).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
     return x, NvWeight(codes, scales, 1.0)
+
+
+@dataclass
+class Fp8Weight:
+    """Host (or device) tensors of one block-scaled FP8 matrix [n, k]."""
+    codes: torch.Tensor   # uint8 [n, k] (E4M3 bit patterns)
+    scales: torch.Tensor  # float32 [ceil(n/128), ceil(k/128)]
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.codes.shape[1])
+
+    def to(self, device) -> "Fp8Weight":
+        return Fp8Weight(self.codes.to(device), self.scales.to(device))
+
+
+def fp8_weight(n: int, k: int, seed: int, which: int) -> Fp8Weight:
+    """Codes uniform over the non-NaN E4M3 bytes; block scales 2^U(-10, -6)."""
+    r = torch.randint(0, 254, (n, k), generator=_gen(seed, _FP8 + 2 * which),
+                      dtype=torch.int32)
+    codes = (r + (r >= 0x7F).to(torch.int32)).to(torch.uint8)  # skip 0x7F; max 0xFE
+    u = torch.rand(((n + 127) // 128, (k + 127) // 128),
+                   generator=_gen(seed, _FP8 + 2 * which + 1), dtype=torch.float32)
+    scales = torch.exp2(u * 4.0 - 10.0)
+    return Fp8Weight(codes.contiguous(), scales.contiguous())
+
+
+def fp8_ffn_weights(hidden: int, inter: int, seed: int = 0):
+    return (fp8_weight(inter, hidden, seed, 0), fp8_weight(inter, hidden, seed, 1),
+            fp8_weight(hidden, inter, seed, 2))
+
+
+def fp8_workload(name: str, seed: int = 0, m: int | None = None):
+    """(x bf16 [m, hidden], wg, wu, wd) with FP8 weights, on the CPU; the
+    shapes and X of workload ``name``."""
+    spec = WORKLOADS[name]
+    rows = spec["m"] if m is None else m
+    x = activations(rows, spec["hidden"], seed, spec["outliers"])
+    return (x,) + fp8_ffn_weights(spec["hidden"], spec["inter"], seed)
