@@ -3,8 +3,8 @@
 A step is one dense_ffn_forward (W4A16: gate+up+silu, down) over one batch
 of synthetic rows, inputs resident in HBM.  The headline workload is the
 single-row decode FFN (m=1, hidden=4096, inter=12288); the m=64 and
-m=2048 workloads the metric also names, and the W4A4 arm, are measured in
-the same run and reported under "workloads".
+m=2048 workloads the metric also names, and the W4A4 and W8A8 fixed-format
+arms, are measured in the same run and reported under "workloads".
 
 Cold weights: every weight set fits in the 256 MB Infinity Cache, so each
 step reads the next of R replicas with R x size >= 1 GiB; the reported
@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 REPLICA_BYTES = 1 << 30
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 DOMINANT_KERNEL_SRC = os.path.join(ROOT, "nvfp4_weight_dense_amd", "csrc", "k_gemv.hip")
@@ -48,15 +49,20 @@ COPY_BYTES = 1 << 28
 
 
 def weight_bytes(w) -> int:
-    return int(w.codes.numel() + w.scales.numel())
+    return int(w.codes.numel() * w.codes.element_size() + w.scales.numel() * w.scales.element_size())
 
 
 def _replicas(ws, count, device):
     import nvfp4_weight_dense_amd as nv
     out = []
+    nvfp4 = hasattr(ws[0], "ts")
     for _ in range(count):
-        out.append([nv.NVFP4Weight(w.codes.to(device, copy=True), w.scales.to(device, copy=True),
-                                   w.ts) for w in ws])
+        if nvfp4:
+            out.append([nv.NVFP4Weight(w.codes.to(device, copy=True),
+                                       w.scales.to(device, copy=True), w.ts) for w in ws])
+        else:
+            out.append([nv.FP8Weight(w.codes.to(device, copy=True),
+                                     w.scales.to(device, copy=True)) for w in ws])
     return out
 
 
@@ -75,14 +81,14 @@ def _time_loop(fn, reps, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
-def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=0):
+def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=0, w8a8=False):
     import torch
 
     import nvfp4_weight_dense_amd as nv
     import synthetic_inputs as si
 
     dev = torch.device("cuda:0")
-    x, wg, wu, wd = si.workload(name, m=m)
+    x, wg, wu, wd = (si.fp8_workload if w8a8 else si.workload)(name, m=m)
     m, hidden = x.shape
     inter = wg.n
     wbytes = weight_bytes(wg) + weight_bytes(wu) + weight_bytes(wd)
@@ -105,6 +111,9 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
         wgu = si.NvWeight(torch.cat([wg.codes, wu.codes]), torch.cat([wg.scales, wu.scales]), wg.ts)
         reps = _replicas((wgu, wd), nrep, dev)
         fn = nv.dense_ffn_forward_fused
+    elif w8a8:
+        reps = _replicas((wg, wu, wd), nrep, dev)
+        fn = nv.dense_ffn_forward_w8a8
     else:
         reps = _replicas((wg, wu, wd), nrep, dev)
         fn = nv.dense_ffn_forward_w4a4 if w4a4 else nv.dense_ffn_forward
@@ -112,6 +121,7 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
     flops = 6.0 * m * hidden * inter
     res = {
         "workload": f"{name} m={m} hidden={hidden} inter={inter}" + (" w4a4" if w4a4 else "")
+                    + (" (block-scaled FP8 weights, per-row FP8 activations)" if w8a8 else "")
                     + (" fused gate+up weight" if fused else "")
                     + (f" + LoRA rank {lora_rank} on gate, up, down" if lora_rank else ""),
         "m": m, "hidden": hidden, "inter": inter,
@@ -122,7 +132,7 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
         "replicas": nrep,
     }
     res["hbm_frac"] = res["weight_gbs"] / HBM_PEAK_GBS
-    res["mfma_frac"] = res["tflops"] / BF16_PEAK_TFLOPS
+    res["mfma_frac"] = res["tflops"] / (FP8_PEAK_TFLOPS if w8a8 else BF16_PEAK_TFLOPS)
     ctx = dict(x=xd, weights=reps, out=out, stream=stream, wbytes=wbytes)
     return res, ctx
 
@@ -282,9 +292,13 @@ def main():
                 ("w4a4", max(20, args.steps // 2), True, 1, False, 0),
                 ("w4a4", max(20, args.steps // 2), True, 8, False, 0),
                 ("w4a4", max(20, args.steps // 2), True, 64, False, 0),
-                ("w4a4", max(5, args.steps // 20), True, 512, False, 0)):
+                ("w4a4", max(5, args.steps // 20), True, 512, False, 0),
+                ("w8a8", max(20, args.steps // 2), False, 1, False, 0),
+                ("w8a8", max(20, args.steps // 2), False, 8, False, 0),
+                ("w8a8", max(20, args.steps // 2), False, 64, False, 0),
+                ("w8a8", max(5, args.steps // 20), False, 512, False, 0)):
             r, c = measure_ffn(name, steps, max(3, args.warmup // 2), w4a4=w4a4, m=m, fused=fused,
-                               lora_rank=rank)
+                               lora_rank=rank, w8a8=name == "w8a8")
             del c
             torch.cuda.empty_cache()
             workloads.append(r)

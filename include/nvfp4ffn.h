@@ -195,6 +195,56 @@ int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden,
                            const nvfp4_weight *wu, const nvfp4_weight *wd,
                            const nvfp4_lora *lora, void *out, void *stream);
 
+/* ---- W8A8 fixed format ------------------------------------------------------
+ * The other fixed activation format of the pages (page
+ * layers/dense_ffn_fixed.rs, `Fixed::W8a8`: the declared W8A8 layer, per-row
+ * FP8 activations at every row count) on block-scaled FP8 weights (page
+ * layers/dense_ffn_overlays.rs, `set_fp8_weights`: "native block-scaled FP8"
+ * weights with a scale grid).  The pages fix neither the block shape nor the
+ * activation recipe; the readings taken here: one fp32 scale per 128 x 128
+ * weight block, and one fp32 scale per activation row with amax mapped to
+ * 448, the largest E4M3 magnitude. */
+
+/* One block-scaled FP8 matrix W[n][k] (y = x . W^T):
+ *   codes : device, uint8 [n][k], E4M3FN bit patterns (0x7F/0xFF are NaN);
+ *   scales: device, fp32 [ceil(n/128)][ceil(k/128)], row-major;
+ *   W[r][c] = e4m3(codes[r][c]) * scales[r/128][c/128].
+ *   k must be a positive multiple of 32; codes 16-byte and scales 4-byte
+ *   aligned. */
+typedef struct fp8_weight {
+  const uint8_t *codes;
+  const float *scales;
+  int32_t n;
+  int32_t k;
+} fp8_weight;
+
+/* Per-row FP8 activation quantizer.  x: bf16 [m][k], k % 32 == 0.
+ * Outputs: codes uint8 [m][k] (E4M3FN), row_scale fp32 [m].  Per row, in
+ * fp32 with IEEE rounding: s_row = amax/448 (1 for an all-zero row);
+ * code = E4M3(x / s_row), nearest with ties to the even mantissa,
+ * saturating at 448, sign kept.  Depends on nothing outside its row. */
+int fp8_quantize_rows(const void *x, int32_t m, int32_t k, uint8_t *codes,
+                      float *row_scale, void *stream);
+
+/* W8A8 projection: x is quantized per row (fp8_quantize_rows), then
+ * y[r][c] = bf16( s_row[r] * sum_b scales[c/128][b] *
+ *                 sum_{k in block b} e4m3(xq[r][k]) * e4m3(wq[c][k]) ),
+ * fp32 accumulation, FP8 matrix cores.  Row r's bits are the same for
+ * every m: one kernel and one K order (fixed by n and k) serve every row
+ * count.  x: bf16 [m][k]; y: bf16 [m][n]. */
+int fp8_gemm_w8a8(const void *x, int32_t m, const fp8_weight *w, void *y,
+                  void *stream);
+
+/* Dense SwiGLU FFN, fixed-format W8A8: x and act are quantized per row to
+ * FP8 before each projection; gate, up and silu_mul run in one launch;
+ * row r's output bits do not depend on m (page layers/dense_ffn_fixed.rs,
+ * `forward_fixed`, W8A8 arm).  wg, wu: [inter][hidden]; wd:
+ * [hidden][inter].  Errors as dense_ffn_forward. */
+int dense_ffn_forward_w8a8(const void *x, int32_t m, int32_t hidden,
+                           int32_t inter, const fp8_weight *wg,
+                           const fp8_weight *wu, const fp8_weight *wd,
+                           void *out, void *stream);
+
 /* The calling thread's last error message ("" if none). */
 const char *nvfp4_last_error(void);
 

@@ -10,7 +10,9 @@ raises :class:`Nvfp4LibraryMissing`.
 Tensors: activations are ``torch.bfloat16`` ``[rows, cols]`` contiguous on
 the GPU; a weight is any object with ``codes`` (uint8 ``[n, k/2]``),
 ``scales`` (uint8 ``[n, k/16]``, E4M3 bits) and ``tensor_scale`` (or
-``ts``) -- see :class:`NVFP4Weight`.
+``ts``) -- see :class:`NVFP4Weight`; a W8A8 weight has ``codes`` (uint8
+``[n, k]``, E4M3 bits) and ``scales`` (float32 ``[ceil(n/128),
+ceil(k/128)]``) -- see :class:`FP8Weight`.
 """
 
 from __future__ import annotations
@@ -34,7 +36,8 @@ __all__ = [
     "nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "nvfp4_quantize_rows", "silu_mul",
     "nvfp4_gate_up_silu_w4a16", "dense_ffn_forward", "dense_ffn_forward_w4a4",
     "nvfp4_gate_up_views", "dense_ffn_forward_fused", "LoraPair", "nvfp4_lora_delta",
-    "dense_ffn_forward_lora",
+    "dense_ffn_forward_lora", "FP8Weight", "fp8_quantize_rows", "fp8_gemm_w8a8",
+    "dense_ffn_forward_w8a8",
     "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
 ]
 
@@ -88,6 +91,22 @@ class NVFP4Weight:
     tensor_scale: float = 1.0
 
 
+@dataclass
+class FP8Weight:
+    """One block-scaled FP8 matrix W[n][k] on the GPU."""
+    codes: torch.Tensor   # uint8 [n, k], E4M3FN bit patterns
+    scales: torch.Tensor  # float32 [ceil(n/128), ceil(k/128)]
+
+
+class _CFp8Weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("n", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -114,6 +133,10 @@ def load_library(path: str = LIB_PATH):
         "dense_ffn_forward_fused": [vp, i32, i32, i32, wp, wp, vp, vp],
         "nvfp4_lora_delta": [vp, i32, i32, ctypes.POINTER(_CLoraPair), i32, vp, vp],
         "dense_ffn_forward_lora": [vp, i32, i32, i32, wp, wp, wp, ctypes.POINTER(_CLora), vp, vp],
+        "fp8_quantize_rows": [vp, i32, i32, vp, vp, vp],
+        "fp8_gemm_w8a8": [vp, i32, ctypes.POINTER(_CFp8Weight), vp, vp],
+        "dense_ffn_forward_w8a8": [vp, i32, i32, i32, ctypes.POINTER(_CFp8Weight),
+                                   ctypes.POINTER(_CFp8Weight), ctypes.POINTER(_CFp8Weight), vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -333,4 +356,53 @@ def dense_ffn_forward_lora(x: torch.Tensor, wg, wu, wd, gate: LoraPair | None = 
     cl = _CLora(_clora_pair(gate), _clora_pair(up), _clora_pair(down))
     _check(L.dense_ffn_forward_lora(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
                                     ctypes.byref(cd), ctypes.byref(cl), _ptr(out), _stream(stream)))
+    return out
+
+
+# ---- W8A8 fixed format ----------------------------------------------------------
+
+def _cfp8(w) -> _CFp8Weight:
+    if w.codes.dtype != torch.uint8 or not w.codes.is_contiguous() or not w.codes.is_cuda:
+        raise ValueError("fp8 weight codes: expected a contiguous uint8 GPU tensor")
+    if w.scales.dtype != torch.float32 or not w.scales.is_contiguous() or not w.scales.is_cuda:
+        raise ValueError("fp8 weight scales: expected a contiguous float32 GPU tensor")
+    n, k = w.codes.shape
+    if tuple(w.scales.shape) != ((n + 127) // 128, (k + 127) // 128):
+        raise ValueError("fp8 weight scales: expected [ceil(n/128), ceil(k/128)]")
+    return _CFp8Weight(w.codes.data_ptr(), w.scales.data_ptr(), int(n), int(k))
+
+
+def fp8_quantize_rows(x: torch.Tensor, stream=None):
+    """Per-row FP8 quantizer -> (codes uint8 [m, k] E4M3, row_scale float32 [m])."""
+    L = load_library()
+    x = _act(x, "x")
+    m, k = x.shape
+    codes = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    rs = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(L.fp8_quantize_rows(_ptr(x), m, k, _ptr(codes), _ptr(rs), _stream(stream)))
+    return codes, rs
+
+
+def fp8_gemm_w8a8(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
+    """W8A8 projection: x quantized per row to FP8, then x_q . W^T (block-scaled W)."""
+    L = load_library()
+    x = _act(x, "x")
+    cw = _cfp8(w)
+    if y is None:
+        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    _check(L.fp8_gemm_w8a8(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
+    return y
+
+
+def dense_ffn_forward_w8a8(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None = None,
+                           stream=None):
+    """Fixed-format W8A8 FFN (FP8 activations per row, block-scaled FP8 weights)."""
+    L = load_library()
+    x = _act(x, "x")
+    cg, cu, cd = _cfp8(wg), _cfp8(wu), _cfp8(wd)
+    m, hidden = x.shape
+    if out is None:
+        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
+    _check(L.dense_ffn_forward_w8a8(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
+                                    ctypes.byref(cd), _ptr(out), _stream(stream)))
     return out

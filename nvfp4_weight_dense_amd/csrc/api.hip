@@ -11,6 +11,9 @@
 //          the LDS-shared streaming kernel with 256-row blocks.
 //   W4A4:  quantize x -> gate+up(+silu) -> act -> quantize act -> down.  One
 //          kernel and one K order for every m, so row bits do not depend on m.
+//   W8A8:  the same sequence with per-row FP8 activations and block-scaled
+//          FP8 weights on the FP8 matrix cores (page layers/dense_ffn_fixed.rs,
+//          `Fixed::W8a8`).
 // Every check runs before the first launch; a forced path that cannot serve a
 // shape is an error, never a silent fallback (the pages refuse to start with
 // a requested but missing variant: page layers/mod.rs, `w4a16_v2_kernel`).
@@ -338,6 +341,60 @@ QuantBuf quant_layout(char *base, int m, int k) {
   return q;
 }
 
+// ---- W8A8 ------------------------------------------------------------------------------
+
+int check_fp8_weight(const fp8_weight *w, const char *name) {
+  if (!w) return fail(NVFP4_EINVAL, "%s: null weight descriptor", name);
+  if (!w->codes || !w->scales) return fail(NVFP4_EINVAL, "%s: null codes or scales pointer", name);
+  if (w->n <= 0 || w->k <= 0) return fail(NVFP4_ESHAPE, "%s: n=%d k=%d must be positive", name, w->n, w->k);
+  if (w->k % 32 != 0) return fail(NVFP4_ESHAPE, "%s: k=%d is not a multiple of 32", name, w->k);
+  // n*k codes stay below 2^31 bytes, the range of one buffer resource
+  if (w->k > kMaxDim || w->n > kMaxDim || (int64_t)w->n * w->k > 0x7FFFFFFFll)
+    return fail(NVFP4_ESHAPE, "%s: n=%d k=%d exceed the limits (each <= %d, n*k < 2^31)", name, w->n,
+                w->k, kMaxDim);
+  if (misaligned(w->codes) || ((uintptr_t)w->scales & 3u))
+    return fail(NVFP4_EINVAL, "%s: codes must be 16-byte and scales 4-byte aligned", name);
+  return NVFP4_OK;
+}
+
+// rows of an FP8 activation buffer: m*k codes stay below 2^31 bytes
+int check_fp8_rows(int m, int k, const char *name) {
+  if ((int64_t)m * k > 0x7FFFFFFFll)
+    return fail(NVFP4_ESHAPE, "%s: m=%d rows of k=%d exceed 2^31 bytes of FP8 codes", name, m, k);
+  return NVFP4_OK;
+}
+
+Fp8MatRef fp8_mat(const fp8_weight *w) { return Fp8MatRef{w->codes, w->scales}; }
+
+struct Fp8QuantBuf {
+  uint8_t *codes;
+  float *rs;
+  size_t bytes;
+};
+
+Fp8QuantBuf fp8_quant_layout(char *base, int m, int k) {
+  Fp8QuantBuf q;
+  const size_t c = align256((size_t)m * k);
+  q.codes = (uint8_t *)base;
+  q.rs = base ? (float *)(base + c) : nullptr;
+  q.bytes = c + align256((size_t)m * 4);
+  return q;
+}
+
+size_t w8a8_scratch_bytes(int m, int n, int k, int nmat) {
+  return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+}
+
+int run_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const Fp8MatRef *w, void *y,
+             void *scratch, hipStream_t s) {
+  StreamPlan pl = stream_plan(n, k);
+  unsigned *counters = nullptr;
+  int rc = counters_get(stream_counter_words(pl, m), &counters);
+  if (rc) return rc;
+  return hip_status(launch_w8a8(a, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
+                    "W8A8 projection launch");
+}
+
 }  // namespace
 
 // ---- C ABI ---------------------------------------------------------------------------
@@ -627,6 +684,89 @@ int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden, int32_t int
     return rc;
   return run_proj(ActRef{nullptr, qa.codes, qa.scales, qa.rs}, m, inter, hidden, 1, &wdm, out, scr,
                   Path::Stream, s);
+}
+
+int fp8_quantize_rows(const void *x, int32_t m, int32_t k, uint8_t *codes, float *row_scale,
+                      void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_act(x, m, "x"))) return rc;
+  if (k <= 0 || k % 32 != 0 || k > kMaxDim)
+    return fail(NVFP4_ESHAPE, "fp8_quantize_rows: k=%d must be a positive multiple of 32 up to %d", k,
+                kMaxDim);
+  if ((rc = check_fp8_rows(m, k, "fp8_quantize_rows"))) return rc;
+  if (m == 0) return NVFP4_OK;
+  if (!codes || !row_scale) return fail(NVFP4_EINVAL, "fp8_quantize_rows: null output pointer");
+  if (misaligned(codes) || ((uintptr_t)row_scale & 3u))
+    return fail(NVFP4_EINVAL, "fp8_quantize_rows: codes must be 16-byte and row_scale 4-byte aligned");
+  return hip_status(launch_quantize_rows_fp8(x, m, k, codes, row_scale, (hipStream_t)stream),
+                    "fp8 quantize_rows launch");
+}
+
+int fp8_gemm_w8a8(const void *x, int32_t m, const fp8_weight *w, void *y, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(y, m, "y")) || (rc = check_fp8_weight(w, "w")) ||
+      (rc = check_fp8_rows(m, w->k, "x")))
+    return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  log_path("gemm_w8a8", "w8a8", m, w->n, w->k);
+  Fp8QuantBuf q = fp8_quant_layout(nullptr, m, w->k);
+  const size_t part = w8a8_scratch_bytes(m, w->n, w->k, 1);
+  void *base = nullptr;
+  if ((rc = arena_get(q.bytes + part, &base))) return rc;
+  q = fp8_quant_layout((char *)base, m, w->k);
+  ProfileScope ps("gemm_w8a8", m, s);
+  if ((rc = hip_status(launch_quantize_rows_fp8(x, m, w->k, q.codes, q.rs, s), "fp8 quantize launch")))
+    return rc;
+  Fp8MatRef wm = fp8_mat(w);
+  return run_w8a8(Fp8ActRef{q.codes, q.rs}, m, w->k, w->n, 1, &wm, y, (char *)base + q.bytes, s);
+}
+
+int dense_ffn_forward_w8a8(const void *x, int32_t m, int32_t hidden, int32_t inter,
+                           const fp8_weight *wg, const fp8_weight *wu, const fp8_weight *wd,
+                           void *out, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(out, m, "out"))) return rc;
+  if (hidden <= 0 || inter <= 0)
+    return fail(NVFP4_ESHAPE, "hidden=%d inter=%d must be positive", hidden, inter);
+  if ((rc = check_fp8_weight(wg, "wg")) || (rc = check_fp8_weight(wu, "wu")) ||
+      (rc = check_fp8_weight(wd, "wd")))
+    return rc;
+  if (wg->n != inter || wg->k != hidden || wu->n != inter || wu->k != hidden)
+    return fail(NVFP4_ESHAPE, "wg/wu must be [inter=%d][hidden=%d], got [%d][%d] and [%d][%d]",
+                inter, hidden, wg->n, wg->k, wu->n, wu->k);
+  if (wd->n != hidden || wd->k != inter)
+    return fail(NVFP4_ESHAPE, "wd must be [hidden=%d][inter=%d], got [%d][%d]", hidden, inter,
+                wd->n, wd->k);
+  if ((rc = check_fp8_rows(m, hidden, "x")) || (rc = check_fp8_rows(m, inter, "act"))) return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  log_path("dense_ffn_forward_w8a8", "w8a8", m, inter, hidden);
+  Fp8QuantBuf qx = fp8_quant_layout(nullptr, m, hidden);
+  Fp8QuantBuf qa = fp8_quant_layout(nullptr, m, inter);
+  const size_t act_b = align256((size_t)2 * m * inter);
+  size_t part = w8a8_scratch_bytes(m, inter, hidden, 2);
+  const size_t part_d = w8a8_scratch_bytes(m, hidden, inter, 1);
+  if (part_d > part) part = part_d;
+  void *base = nullptr;
+  if ((rc = arena_get(qx.bytes + qa.bytes + act_b + part, &base))) return rc;
+  char *p = (char *)base;
+  qx = fp8_quant_layout(p, m, hidden);
+  qa = fp8_quant_layout(p + qx.bytes, m, inter);
+  char *act = p + qx.bytes + qa.bytes;
+  char *scr = act + act_b;
+  ProfileScope ps("dense_total w8a8", m, s);
+  Fp8MatRef w2[2] = {fp8_mat(wg), fp8_mat(wu)};
+  Fp8MatRef wdm = fp8_mat(wd);
+  if ((rc = hip_status(launch_quantize_rows_fp8(x, m, hidden, qx.codes, qx.rs, s), "fp8 quantize launch")))
+    return rc;
+  if ((rc = run_w8a8(Fp8ActRef{qx.codes, qx.rs}, m, hidden, inter, 2, w2, act, scr, s))) return rc;
+  if ((rc = hip_status(launch_quantize_rows_fp8(act, m, inter, qa.codes, qa.rs, s), "fp8 quantize launch")))
+    return rc;
+  return run_w8a8(Fp8ActRef{qa.codes, qa.rs}, m, inter, hidden, 1, &wdm, out, scr, s);
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
-// k_elementwise.hip -- silu_mul and the per-row NVFP4 activation quantizer
-// (gfx950).  Both are HBM-bound passes over bf16 rows.
+// k_elementwise.hip -- silu_mul and the per-row NVFP4 and FP8 activation
+// quantizers (gfx950).  All are HBM-bound passes over bf16 rows.
 #include <algorithm>
 
 #include "launchers.h"
@@ -169,7 +169,85 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
   for (int b = t + kKeep * nt; b < nblk; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
 }
 
+// ---- per-row FP8 quantizer of the W8A8 arm ---------------------------------------
+// s_row = amax/448 (1 for an all-zero row), code = E4M3(x / s_row) with the
+// sign kept.  Same layout of work as k_quantize_rows: one workgroup per row,
+// one thread per 16-element block, up to kKeep blocks kept in registers.
+
+__global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const uint16_t *__restrict__ x,
+                                                                       int k,
+                                                                       uint8_t *__restrict__ codes,
+                                                                       float *__restrict__ row_scale) {
+  const int r = blockIdx.x;
+  const int nt = blockDim.x;
+  const int t = threadIdx.x;
+  const int nblk = k >> 4;
+  const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
+
+  auto block_amax = [](const uint4 &v0, const uint4 &v1, float amax) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+    }
+    return amax;
+  };
+
+  uint4 keep[kKeep][2];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    const int b = t + i * nt;
+    if (b < nblk) {
+      keep[i][0] = xv4[2 * b];
+      keep[i][1] = xv4[2 * b + 1];
+      amax = block_amax(keep[i][0], keep[i][1], amax);
+    }
+  }
+  for (int b = t + kKeep * nt; b < nblk; b += nt) amax = block_amax(xv4[2 * b], xv4[2 * b + 1], amax);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float wmax[kQuantMaxThreads / 64];
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = wmax[0];
+  for (int w = 1; w < (nt >> 6); ++w) amax = fmaxf(amax, wmax[w]);
+
+  float s_row = amax / 448.0f;
+  if (amax == 0.0f) s_row = 1.0f;
+  if (t == 0) row_scale[r] = s_row;
+
+  auto encode_block = [&](int b, const uint4 &v0, const uint4 &v1) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+      const float q = bf16_bits_to_f32(h) / s_row;
+      const uint32_t code = ((__float_as_uint(q) >> 31) << 7) | e4m3_encode_sat(q);
+      out[i >> 2] |= code << (8 * (i & 3));
+    }
+    *(uint4 *)(codes + (size_t)r * k + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
+  };
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    const int b = t + i * nt;
+    if (b < nblk) encode_block(b, keep[i][0], keep[i][1]);
+  }
+  for (int b = t + kKeep * nt; b < nblk; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes, float *row_scale,
+                                    hipStream_t stream) {
+  const int nblk = k >> 4;
+  const int threads = std::min(kQuantMaxThreads, (nblk + 63) / 64 * 64);
+  hipLaunchKernelGGL(k_quantize_rows_fp8, dim3(m), dim3(threads), 0, stream, (const uint16_t *)x, k,
+                     codes, row_scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out, int64_t count,
                            hipStream_t stream) {

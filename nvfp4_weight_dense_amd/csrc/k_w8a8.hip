@@ -1,0 +1,325 @@
+// k_w8a8.hip -- the W8A8 fixed-format projection (gfx950): block-scaled FP8
+// weights times per-row FP8 activations, exact products on the matrix cores.
+//
+// Format (page layers/dense_ffn_fixed.rs, `Fixed::W8a8`: per-row FP8
+// activations at every row count; page layers/dense_ffn_overlays.rs,
+// `set_fp8_weights`: block-scaled FP8 weights with a scale grid):
+//   weight  W[c][k] = e4m3(codes[c][k]) * scales[c/128][k/128]   (fp32 grid)
+//   activation  x_hat[r][k] = e4m3(xq[r][k]) * s_row[r]
+//   y[r][c] = bf16( s_row[r] * sum_b scales[c/128][b] * P_b[r][c] ),
+//   P_b = sum over the 128 K of block b of e4m3 * e4m3 (exact products,
+//   fp32 sums).
+//
+// Work decomposition (the same skeleton as the NVFP4 weight-streaming
+// kernel, so the K order of every output depends on (n, k) only):
+//   * A workgroup owns CTW column tiles of 16 output columns (of NMAT
+//     weight matrices: 1, or 2 for gate+up with a fused silu epilogue), up
+//     to 64 rows, and a range of K; its 4 waves take interleaved 128-element
+//     steps.  A step is one weight block along K, and the 16 columns of a
+//     tile lie in one block along N, so a step needs one scale per tile.
+//   * Lane (c = lane%16, g = lane/16) loads 32 bytes of weight row c at K
+//     offset 32g of the step (two 128-bit buffer loads), and the same 32
+//     bytes of each activation row.  The hardware FP8 -> fp16 conversion
+//     (exact: an E4M3 value has 4 significant bits and lies in
+//     [2^-9, 448]) turns them into four operand fragments of
+//     v_mfma_f32_16x16x32_f16, whose products are exact and whose sums are
+//     fp32; P_b is the sum of the four.
+//     The FP8 matrix-core forms (v_mfma_scale_f32_16x16x128_f8f6f4,
+//     v_mfma_f32_16x16x32_fp8_fp8) take the bytes directly but do not keep
+//     every product: measured on this part, inside one group of eight
+//     products a term 2^18 or more below the group's largest is dropped
+//     (448*448 + 1 gives 448*448, 1 + 2^-18 gives 1), while the fp16 form
+//     returns both sums exactly.  So the products here are exact and only
+//     the fp32 sums round, as for the NVFP4 paths.
+//   * acc = fma(scale_b, P_b, acc) per step, in the wave's step order; waves
+//     reduce through LDS in fixed wave order; with ksplit > 1 the last
+//     workgroup of a tile to arrive sums the fp32 partials in split order.
+//   * Epilogue: times s_row, bf16 (or silu(bf16 g) * bf16 u for NMAT = 2).
+// Buffer loads return zero outside a resource's range, so ragged rows,
+// columns and K need no branches.
+#include "launchers.h"
+#include "nvfp4_common.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kNW = 4;  // waves per workgroup
+
+
+struct W8Args {
+  const uint8_t *xc;  // E4M3 [m][k]
+  const float *xr;    // [m]
+  int m, k, n;
+  const uint8_t *codes0, *codes1;  // E4M3 [n][k]
+  const float *scales0, *scales1;  // [ceil(n/128)][ceil(k/128)]
+  void *y;
+  float *partial;      // [tiles * row blocks][NMAT][ksplit][CTW][16*MT][16]
+  unsigned *counters;  // [gridDim.z][gridDim.x], zero between calls
+  int ksplit, steps_per_split;
+};
+
+template <int MT, int NMAT, int CTW>
+struct W8Cfg {
+  static constexpr int kRegsPerStep = (NMAT * CTW + MT) * 8;
+  static constexpr int U = kRegsPerStep * 4 <= 128 ? 4 : 2;
+};
+
+// Eight E4M3 bytes (K order from the low byte of lo) -> eight exact fp16
+// values, one MFMA operand fragment.
+__device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// the four fragments of 32 bytes: fragment j covers bytes 8j..8j+7
+__device__ __forceinline__ void fp8x32_to_f16(const uint4 &q0, const uint4 &q1, f16x8 (&f)[4]) {
+  f[0] = fp8x8_to_f16(q0.x, q0.y);
+  f[1] = fp8x8_to_f16(q0.z, q0.w);
+  f[2] = fp8x8_to_f16(q1.x, q1.y);
+  f[3] = fp8x8_to_f16(q1.z, q1.w);
+}
+
+template <int MT, int NMAT, int CTW>
+__global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
+  constexpr int U = W8Cfg<MT, NMAT, CTW>::U;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+  const int k = p.k;
+  const int col0 = blockIdx.x * (16 * CTW);
+  const int row0 = blockIdx.z * 64;
+  const int nsteps = (k + 127) >> 7;  // = scale blocks along K
+  const int s_begin = blockIdx.y * p.steps_per_split;
+  const int s_end = min(nsteps, s_begin + p.steps_per_split);
+  const int nbn = (p.n + 127) >> 7;   // scale blocks along N
+
+  const int ncols = min(16 * CTW, p.n - col0);
+  const int nrows = min(64, p.m - row0);
+  __amdgpu_buffer_rsrc_t wc[NMAT];
+  const float *wsc[NMAT];
+  wc[0] = rsrc(p.codes0 + (size_t)col0 * k, (size_t)ncols * k);
+  wsc[0] = p.scales0;
+  if constexpr (NMAT > 1) {
+    wc[1] = rsrc(p.codes1 + (size_t)col0 * k, (size_t)ncols * k);
+    wsc[1] = p.scales1;
+  }
+  const __amdgpu_buffer_rsrc_t ax = rsrc(p.xc + (size_t)row0 * k, (size_t)nrows * k);
+
+  f32x4 acc[NMAT][CTW][MT];
+#pragma unroll
+  for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int base = s_begin + wave; base < s_end; base += kNW * U) {
+    uint4 bw[U][NMAT][CTW][2];
+    uint4 aw[U][MT][2];
+    float sc[U][NMAT][CTW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = base + u * kNW;
+      const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
+      const bool ok = t < s_end && kk < (uint32_t)k;
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const uint32_t off = ok ? (uint32_t)(ct * 16 + c16) * (uint32_t)k + kk : kOOB;
+          bw[u][i][ct][0] = ld16_nt(wc[i], off);
+          bw[u][i][ct][1] = ld16_nt(wc[i], off + 16u);
+          // the tile's 16 columns share one scale row (col0 + 16 ct is a
+          // multiple of 16, blocks are 128 wide); steps past the end read
+          // block 0 and multiply zeros
+          const int tb = t < s_end ? t : 0;
+          const int cb = min((col0 + ct * 16) >> 7, nbn - 1);  // a tile past n: any valid row
+          sc[u][i][ct] = wsc[i][(size_t)cb * nsteps + tb];
+        }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t off = ok ? (uint32_t)(mt * 16 + c16) * (uint32_t)k + kk : kOOB;
+        aw[u][mt][0] = ld16(ax, off);
+        aw[u][mt][1] = ld16(ax, off + 16u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f16x8 bf[NMAT][CTW][4];
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) fp8x32_to_f16(bw[u][i][ct][0], bw[u][i][ct][1], bf[i][ct]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f16x8 af[4];
+        fp8x32_to_f16(aw[u][mt][0], aw[u][mt][1], af);
+#pragma unroll
+        for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+          for (int ct = 0; ct < CTW; ++ct) {
+            f32x4 pb = zero;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bf[i][ct][j], pb, 0, 0, 0);
+            const float s = sc[u][i][ct];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][ct][mt][e] = __builtin_fmaf(s, pb[e], acc[i][ct][mt][e]);
+          }
+      }
+    }
+  }
+
+  // fixed-order reduction over the workgroup's waves
+  __shared__ float red[kNW - 1][MT][4][64];
+#pragma unroll
+  for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      if (wave > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[wave - 1][mt][e][lane] = acc[i][ct][mt][e];
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float s = acc[i][ct][mt][e];
+#pragma unroll
+            for (int w = 0; w < kNW - 1; ++w) s += red[w][mt][e][lane];
+            acc[i][ct][mt][e] = s;
+          }
+      }
+      __syncthreads();
+    }
+  if (wave != 0) return;
+
+  if (p.ksplit > 1) {
+    constexpr int kTile = 16 * MT * 16;
+    const size_t wg = (size_t)blockIdx.z * gridDim.x + blockIdx.x;
+    const __amdgpu_buffer_rsrc_t pres = rsrc(p.partial + wg * NMAT * p.ksplit * CTW * kTile,
+                                             (size_t)NMAT * p.ksplit * CTW * kTile * 4);
+    auto poff = [&](int i, int sp, int ct, int mt, int e) -> uint32_t {
+      const uint32_t r = mt * 16 + 4 * g + e;
+      return ((((uint32_t)(i * p.ksplit + sp) * CTW + ct) * kTile) + r * 16u + c16) * 4u;
+    };
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int i = 0; i < NMAT; ++i)
+            st_coherent(pres, poff(i, blockIdx.y, ct, mt, e), acc[i][ct][mt][e]);
+    unsigned *cnt = p.counters + wg;
+    wait_all_memory();
+    unsigned old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old != (unsigned)(p.ksplit - 1)) return;
+    // last arrival: sum the partials in split order
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < p.ksplit; ++sp) {
+      float v[NMAT][CTW][MT][4];
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i) v[i][ct][mt][e] = ld_coherent(pres, poff(i, sp, ct, mt, e));
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i) acc[i][ct][mt][e] += v[i][ct][mt][e];
+    }
+    if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // epilogue: output element (row0 + mt*16 + 4g + e, col0 + ct*16 + c16)
+#pragma unroll
+  for (int ct = 0; ct < CTW; ++ct) {
+    const int col = col0 + ct * 16 + c16;
+    if (col >= p.n) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = row0 + mt * 16 + 4 * g + e;
+        if (r >= p.m) continue;
+        const float rs = p.xr[r];
+        const float v0 = acc[0][ct][mt][e] * rs;
+        __bf16 out;
+        if constexpr (NMAT > 1)
+          out = swiglu_bf16(v0, acc[NMAT - 1][ct][mt][e] * rs);
+        else
+          out = (__bf16)v0;
+        ((__bf16 *)p.y)[(size_t)r * p.n + col] = out;
+      }
+  }
+}
+
+template <int MT, int NMAT, int CTW>
+hipError_t launch_one(const W8Args &p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_w8a8<MT, NMAT, CTW>), grid, dim3(kNW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int NMAT, int CTW>
+hipError_t launch_mt(const W8Args &p, int mt, dim3 grid, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_one<1, NMAT, CTW>(p, grid, s);
+    case 2: return launch_one<2, NMAT, CTW>(p, grid, s);
+    case 3: return launch_one<3, NMAT, CTW>(p, grid, s);
+    default: return launch_one<4, NMAT, CTW>(p, grid, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const Fp8MatRef *w, void *y,
+                       float *partial, unsigned *counters, const StreamPlan &pl, hipStream_t stream) {
+  W8Args p{};
+  p.xc = a.codes;
+  p.xr = a.row_scale;
+  p.m = m;
+  p.k = k;
+  p.n = n;
+  p.codes0 = w[0].codes;
+  p.scales0 = w[0].scales;
+  p.codes1 = nmat > 1 ? w[1].codes : nullptr;
+  p.scales1 = nmat > 1 ? w[1].scales : nullptr;
+  p.y = y;
+  p.partial = partial;
+  p.counters = counters;
+  p.ksplit = pl.ksplit;
+  p.steps_per_split = pl.steps_per_split;
+  const int mt = m >= 64 ? 4 : cdiv(m, 16);
+  dim3 grid(pl.tiles, pl.ksplit, cdiv(m, 64));
+  if (stream_ctw(n) == 2)
+    return nmat == 1 ? launch_mt<1, 2>(p, mt, grid, stream) : launch_mt<2, 2>(p, mt, grid, stream);
+  return nmat == 1 ? launch_mt<1, 1>(p, mt, grid, stream) : launch_mt<2, 1>(p, mt, grid, stream);
+}
+
+}  // namespace nvfp4

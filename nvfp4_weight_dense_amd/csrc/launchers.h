@@ -132,4 +132,27 @@ hipError_t launch_quantize_rows(const void *x, int m, int k, uint8_t *codes,
                                 uint8_t *scales, float *row_scale,
                                 hipStream_t stream);
 
+// Column tiles per workgroup of the weight-streaming kernels (1 or 2).
+int stream_ctw(int n);
+
+// ---- W8A8 fixed format: block-scaled FP8 weights, per-row FP8 activations ----
+struct Fp8MatRef {
+  const uint8_t *codes;  // E4M3 [n][k]
+  const float *scales;   // [ceil(n/128)][ceil(k/128)]
+};
+struct Fp8ActRef {
+  const uint8_t *codes;    // E4M3 [m][k]
+  const float *row_scale;  // [m]
+};
+// Per-row FP8 quantizer: s_row = amax/448, codes = E4M3(x / s_row).
+hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes,
+                                    float *row_scale, hipStream_t stream);
+// FP8 projection, nmat 1 or 2 (gate+up+silu) as launch_stream, with the
+// same plan, partial and counter rules (stream_plan, stream_partial_floats,
+// stream_counter_words).
+hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat,
+                       const Fp8MatRef *w, void *y, float *partial,
+                       unsigned *counters, const StreamPlan &pl,
+                       hipStream_t stream);
+
 }  // namespace nvfp4

@@ -35,7 +35,8 @@ def test_header_declares_the_abi():
     for want in ["nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "silu_mul", "dense_ffn_forward",
                  "dense_ffn_forward_w4a4", "nvfp4_quantize_rows", "nvfp4_gate_up_silu_w4a16",
                  "nvfp4_gate_up_views", "dense_ffn_forward_fused", "nvfp4_lora_delta",
-                 "dense_ffn_forward_lora",
+                 "dense_ffn_forward_lora", "fp8_quantize_rows", "fp8_gemm_w8a8",
+                 "dense_ffn_forward_w8a8",
                  "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version"]:
         assert want in names
 
@@ -161,6 +162,37 @@ def test_lora_argument_checks():
     assert L.dense_ffn_forward_lora(x, 2, hidden, inter, ctypes.byref(wg), ctypes.byref(wu),
                                     ctypes.byref(wd), ctypes.byref(bad), base, s) == nv.NVFP4_ESHAPE
     assert "lora.up" in nv.nvfp4_last_error()
+
+
+def _f8(n=64, k=64, codes=0x10000, scales=0x20000):
+    return nv._CFp8Weight(codes, scales, n, k)
+
+
+def test_w8a8_argument_checks():
+    L = _lib()
+    x, y, s = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x80000), ctypes.c_void_p(None)
+    assert L.fp8_gemm_w8a8(x, 4, None, y, s) == nv.NVFP4_EINVAL
+    assert L.fp8_gemm_w8a8(x, 4, ctypes.byref(_f8(scales=0)), y, s) == nv.NVFP4_EINVAL
+    assert L.fp8_gemm_w8a8(x, 4, ctypes.byref(_f8(k=48)), y, s) == nv.NVFP4_ESHAPE
+    assert "multiple of 32" in nv.nvfp4_last_error()
+    assert L.fp8_gemm_w8a8(x, 4, ctypes.byref(_f8(scales=0x20002)), y, s) == nv.NVFP4_EINVAL
+    assert "4-byte" in nv.nvfp4_last_error()
+    # n*k codes beyond one 2 GiB buffer range
+    assert L.fp8_gemm_w8a8(x, 4, ctypes.byref(_f8(n=1 << 20, k=1 << 12)), y, s) == nv.NVFP4_ESHAPE
+    assert L.fp8_gemm_w8a8(x, 0, ctypes.byref(_f8()), y, s) == nv.NVFP4_OK
+    assert L.fp8_quantize_rows(x, 2, 40, y, y, s) == nv.NVFP4_ESHAPE
+    assert L.fp8_quantize_rows(x, 0, 64, y, y, s) == nv.NVFP4_OK
+    assert L.fp8_quantize_rows(x, 2, 64, None, y, s) == nv.NVFP4_EINVAL
+    hidden, inter = 64, 96
+    wg, wu, wd = _f8(inter, hidden), _f8(inter, hidden), _f8(hidden, inter)
+    fn = L.dense_ffn_forward_w8a8
+    r = lambda g, u, d, m=2: fn(x, m, hidden, inter, ctypes.byref(g), ctypes.byref(u),
+                                ctypes.byref(d), y, s)
+    assert r(wg, wu, _f8(inter, hidden)) == nv.NVFP4_ESHAPE
+    assert "wd must be" in nv.nvfp4_last_error()
+    assert r(_f8(inter, 32), wu, wd) == nv.NVFP4_ESHAPE
+    assert r(wg, wu, wd, m=0) == nv.NVFP4_OK
+    assert r(wg, wu, wd, m=-1) == nv.NVFP4_EINVAL
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,141 @@
+"""GPU parity of the W8A8 fixed format (block-scaled FP8 weights, per-row
+FP8 activations) against the oracle, through the C-ABI.
+
+* The per-row FP8 quantizer is bit-exact (codes and row scales).
+* Projections and the FFN match the oracle's fp64 value ref element by
+  element within |err_i| <= 2e-2 * rms(ref) + 2^-8 * |ref_i|, on shapes that
+  span several tiles, ragged columns and K, split K, both column-tile
+  widths, and the full workload (sampled rows).  The second term is one
+  bf16 ulp of the element: the block-scaled FP8 weights here (codes uniform
+  over every E4M3 byte, up to 448) with outlier activations give outputs
+  beyond 10 * rms, whose bf16 rounding alone (up to 2^-9 * |ref_i|) exceeds
+  2e-2 * rms.  Where the outputs are not that heavy-tailed (the full
+  workload), the plain 2e-2 * rms bound is asserted as well.
+* Batch invariance is bit-exact, GPU against GPU: rows 0..m-1 at m in
+  {1, 8, 64} equal the m = 512 run, and a permutation of the rows permutes
+  the output rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_weight_dense_amd as nv
+import oracle
+import synthetic_inputs as si
+from gpu_helpers import assert_close, bf16_f64, bits, sync
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def g8(w: si.Fp8Weight) -> nv.FP8Weight:
+    return nv.FP8Weight(w.codes.cuda().contiguous(), w.scales.cuda().contiguous())
+
+
+def o8(w: si.Fp8Weight) -> oracle.Fp8Weight:
+    return oracle.Fp8Weight(w.codes.numpy(), w.scales.numpy())
+
+
+def assert_close_elem(gpu_bits, ref, what):
+    """|gpu - ref| <= 2e-2 * rms(ref) + 2^-8 * |ref| element by element."""
+    g = bf16_f64(gpu_bits)
+    assert np.all(np.isfinite(g)), what + ": non-finite output"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    bound = 2e-2 * rms + 2.0 ** -8 * np.abs(ref)
+    worst = float(np.max(np.abs(g - ref) / bound))
+    assert worst <= 1.0, f"{what}: max |err| / bound = {worst:.4g}"
+
+
+def _rows_with_edge_cases(m, k, seed):
+    x = si.activations(m, k, seed=seed, outliers=True)
+    if m >= 3:
+        x[1, :] = 0.0                      # all-zero row: s_row = 1
+        x[2, ::2] = -0.0                   # signed zeros
+    return x
+
+
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (7, 4096), (5, 14336), (2, 17408 * 2)])
+def test_fp8_quantizer_bit_exact(m, k):
+    _say(f"fp8 quantize m={m} k={k}")
+    x = _rows_with_edge_cases(m, k, seed=m + k)
+    c, r = nv.fp8_quantize_rows(x.cuda())
+    sync()
+    co, ro = oracle.quantize_rows_fp8(bits(x))
+    assert np.array_equal(c.cpu().numpy(), co)
+    assert np.array_equal(r.cpu().numpy(), ro)
+
+
+# (m, n, k): ragged columns and K; n = 64, k = 4096 splits K over 4
+# workgroups; n >= 16384 takes two column tiles per workgroup, 16400 with a
+# last 16-column tile and a partial scale block along N and K
+@pytest.mark.parametrize("m,n,k", [(1, 48, 96), (5, 300, 384), (17, 130, 224), (70, 257, 640),
+                                   (3, 64, 4096), (3, 16400, 160), (64, 1000, 2048)])
+def test_fp8_gemm_w8a8_matches_oracle(m, n, k):
+    _say(f"fp8 gemm m={m} n={n} k={k}")
+    x = _rows_with_edge_cases(m, k, seed=n)
+    w = si.fp8_weight(n, k, seed=m, which=0)
+    y = nv.fp8_gemm_w8a8(x.cuda(), g8(w))
+    sync()
+    _, ye = oracle.gemm_w8a8(bits(x), o8(w))
+    assert_close_elem(bits(y), ye, f"gemm w8a8 m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("m", [1, 4, 17, 65, 130])
+def test_dense_ffn_w8a8_tiny_matches_oracle(m):
+    _say(f"ffn w8a8 tiny m={m}")
+    x, wg, wu, wd = si.fp8_workload("tiny", m=m)
+    y = nv.dense_ffn_forward_w8a8(x.cuda(), g8(wg), g8(wu), g8(wd))
+    sync()
+    _, ye = oracle.dense_ffn_w8a8(bits(x), o8(wg), o8(wu), o8(wd))
+    assert_close_elem(bits(y), ye, f"ffn w8a8 tiny m={m}")
+
+
+def _rows(m, count, seed):
+    if m <= count:
+        return np.arange(m)
+    rng = np.random.default_rng(seed)
+    picked = set(rng.choice(m, count - 2, replace=False).tolist()) | {0, m - 1}
+    return np.array(sorted(picked))
+
+
+@pytest.mark.parametrize("m,nrows", [(1, 1), (64, 3), (512, 4)])
+def test_dense_ffn_w8a8_full_workload_matches_oracle(m, nrows):
+    _say(f"ffn w8a8 full m={m}")
+    x, wg, wu, wd = si.fp8_workload("w8a8", m=m)
+    y = nv.dense_ffn_forward_w8a8(x.cuda(), g8(wg), g8(wu), g8(wd))
+    sync()
+    rows = _rows(m, nrows, seed=3)
+    _, ye = oracle.dense_ffn_w8a8(bits(x)[rows], o8(wg), o8(wu), o8(wd))
+    assert_close_elem(bits(y)[rows], ye, f"ffn w8a8 m={m}")
+    assert_close(bits(y)[rows], ye, f"ffn w8a8 m={m}")
+
+
+def test_dense_ffn_w8a8_batch_invariance():
+    _say("ffn w8a8 invariance")
+    x, wg, wu, wd = si.fp8_workload("w8a8")  # m = 512
+    xd = x.cuda()
+    W = [g8(w) for w in (wg, wu, wd)]
+    ref = nv.dense_ffn_forward_w8a8(xd, *W)
+    for m in si.W8A8_ROW_COUNTS[:-1]:
+        y = nv.dense_ffn_forward_w8a8(xd[:m].contiguous(), *W)
+        sync()
+        assert torch.equal(y.view(torch.int16), ref[:m].view(torch.int16)), f"m={m}"
+    perm = torch.randperm(512, generator=torch.Generator().manual_seed(0)).cuda()
+    y = nv.dense_ffn_forward_w8a8(xd[perm].contiguous(), *W)
+    sync()
+    assert torch.equal(y.view(torch.int16), ref[perm].view(torch.int16))
+
+
+def test_w8a8_m_zero_and_errors_touch_nothing():
+    _say("w8a8 m=0 / errors")
+    x, wg, wu, wd = si.fp8_workload("tiny", m=4)
+    out = torch.full((4, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    nv.dense_ffn_forward_w8a8(x[:0].cuda(), g8(wg), g8(wu), g8(wd), out=out[:0])
+    with pytest.raises(nv.Nvfp4Error):
+        nv.dense_ffn_forward_w8a8(x.cuda(), g8(wg), g8(wu), g8(wg), out=out)  # wd has the wrong shape
+    sync()
+    assert bool((out == 7.0).all())
