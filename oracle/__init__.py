@@ -97,6 +97,12 @@ def lib():
         L.nvo_gemm_w8a8.restype = ip
         L.nvo_dense_ffn_w8a8.argtypes = [vp, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp, ip]
         L.nvo_dense_ffn_w8a8.restype = ip
+        L.nvo_fp16_value.argtypes, L.nvo_fp16_value.restype = [ctypes.c_uint16], dbl
+        L.nvo_dequant_q2.argtypes, L.nvo_dequant_q2.restype = [vp, vp], None
+        L.nvo_gemm_q2.argtypes = [vp, ip, vp, vp, vp, ip]
+        L.nvo_gemm_q2.restype = ip
+        L.nvo_dense_ffn_q2.argtypes = [vp, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp, ip]
+        L.nvo_dense_ffn_q2.restype = ip
         _lib = L
     return _lib
 
@@ -411,4 +417,86 @@ def dense_ffn_w8a8(x: np.ndarray, wg: Fp8Weight, wu: Fp8Weight, wd: Fp8Weight,
                                   a.ctypes.data, nthreads)
     if rc != 0:
         raise ValueError("oracle dense_ffn_w8a8: bad shapes")
+    return (y, ye, g, u, a) if intermediates else (y, ye)
+
+
+# ---- packed-Q2 weights ----------------------------------------------------------
+
+class _Q2Weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("group", ctypes.c_int),
+        ("n", ctypes.c_int),
+        ("k", ctypes.c_int),
+    ]
+
+
+@dataclass
+class Q2Weight:
+    """Packed-Q2 weight: ``codes`` uint8 ``[n, k/4]`` (element 4j+i in bits
+    2i..2i+1 of byte j), ``scales`` uint16 fp16 bits ``[n, k/group]``."""
+    codes: np.ndarray
+    scales: np.ndarray
+    group: int = 128
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.codes.shape[1] * 4)
+
+    def _struct(self):
+        self.codes = np.ascontiguousarray(self.codes, dtype=np.uint8)
+        self.scales = np.ascontiguousarray(self.scales, dtype=np.uint16)
+        assert self.scales.shape == (self.n, self.k // self.group)
+        return _Q2Weight(self.codes.ctypes.data, self.scales.ctypes.data, int(self.group),
+                         self.n, self.k)
+
+
+def fp16_value(h: int) -> float:
+    return lib().nvo_fp16_value(h)
+
+
+def dequant_q2(w: Q2Weight) -> np.ndarray:
+    out = np.empty((w.n, w.k), dtype=np.float64)
+    s = w._struct()
+    lib().nvo_dequant_q2(ctypes.byref(s), out.ctypes.data)
+    return out
+
+
+def gemm_q2(x: np.ndarray, w: Q2Weight, nthreads: int = 0):
+    """Returns (y bf16 bits [m, n], y_exact float64 [m, n])."""
+    x = _u16(x)
+    m = x.shape[0]
+    y = np.empty((m, w.n), dtype=np.uint16)
+    ye = np.empty((m, w.n), dtype=np.float64)
+    s = w._struct()
+    rc = lib().nvo_gemm_q2(x.ctypes.data, m, ctypes.byref(s), y.ctypes.data, ye.ctypes.data,
+                           nthreads)
+    if rc != 0:
+        raise ValueError("oracle gemm_q2: bad shape")
+    return y, ye
+
+
+def dense_ffn_q2(x: np.ndarray, wg: Q2Weight, wu: Q2Weight, wd: Q2Weight, nthreads: int = 0,
+                 intermediates: bool = False):
+    """Packed-Q2 FFN.  Returns (y bf16 [m, hidden], y_exact f64[, g, u, a])."""
+    x = _u16(x)
+    m, hidden = x.shape
+    inter = wg.n
+    y = np.empty((m, hidden), dtype=np.uint16)
+    ye = np.empty((m, hidden), dtype=np.float64)
+    g = np.empty((m, inter), dtype=np.uint16)
+    u = np.empty((m, inter), dtype=np.uint16)
+    a = np.empty((m, inter), dtype=np.uint16)
+    sg, su, sd = wg._struct(), wu._struct(), wd._struct()
+    rc = lib().nvo_dense_ffn_q2(x.ctypes.data, m, hidden, inter, ctypes.byref(sg),
+                                ctypes.byref(su), ctypes.byref(sd), y.ctypes.data,
+                                ye.ctypes.data, g.ctypes.data, u.ctypes.data, a.ctypes.data,
+                                nthreads)
+    if rc != 0:
+        raise ValueError("oracle dense_ffn_q2: bad shapes")
     return (y, ye, g, u, a) if intermediates else (y, ye)

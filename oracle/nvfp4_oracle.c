@@ -579,3 +579,83 @@ int nvo_dense_ffn_w8a8(const uint16_t *x, int m, int hidden, int inter,
   if (!a) free(ab);
   return 0;
 }
+
+/* ---- packed-Q2 weights ------------------------------------------------------
+ * Page layers/dense_ffn_prefill.rs, `prefill_q2`: the packed-Q2 FFN, SiLU
+ * only, by default dequantizes each projection's Q2_0 weight to BF16
+ * (`dequant_q2_0_gn_to_bf16`, groups of `group` elements) and runs the BF16
+ * GEMM on it; gate, up, silu_mul (over gate), down.  The pages do not define
+ * Q2_0 itself; the reading (by analogy with the GGUF 4-bit Q4_0 form,
+ * value = (code - 8) * d): a 2-bit code q per element, four per byte with
+ * element 4j+i in bits 2i..2i+1 of byte j, and one fp16 scale d per group of
+ * `group` consecutive K elements; value = (q - 2) * d, which the dequant
+ * step rounds to bf16 (nearest, ties to even). */
+
+static double fp16_value(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, t = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)t, -24);
+  else if (e == 31)
+    v = t ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + t / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+double nvo_fp16_value(uint16_t h) { return fp16_value(h); }
+
+static int q2_weight_ok(const nvo_q2_weight *w) {
+  return w && w->codes && w->scales && w->n > 0 && w->k > 0 && w->k % 4 == 0 &&
+         w->group > 0 && w->k % w->group == 0;
+}
+
+static void q2_row(const void *wv, int c, double *row) {
+  const nvo_q2_weight *w = (const nvo_q2_weight *)wv;
+  const uint8_t *cr = w->codes + (size_t)c * (w->k / 4);
+  const uint16_t *sr = w->scales + (size_t)c * (w->k / w->group);
+  for (int kk = 0; kk < w->k; kk++) {
+    int q = (cr[kk >> 2] >> (2 * (kk & 3))) & 3;
+    double v = (double)(q - 2) * fp16_value(sr[kk / w->group]);
+    row[kk] = nvo_bf16_value(nvo_bf16_from_double(v));
+  }
+}
+
+void nvo_dequant_q2(const nvo_q2_weight *w, double *out) {
+  for (int c = 0; c < w->n; c++) q2_row(w, c, out + (size_t)c * w->k);
+}
+
+int nvo_gemm_q2(const uint16_t *x, int m, const nvo_q2_weight *w, uint16_t *y,
+                double *y_exact, int nthreads) {
+  if (!q2_weight_ok(w) || m < 0 || (m > 0 && (!x || !y))) return -1;
+  if (m == 0) return 0;
+  size_t cnt = (size_t)m * w->k;
+  double *xd = (double *)malloc(sizeof(double) * cnt);
+  for (size_t i = 0; i < cnt; i++) xd[i] = nvo_bf16_value(x[i]);
+  project_rows(xd, m, w->n, w->k, w, q2_row, y, y_exact, nthreads);
+  free(xd);
+  return 0;
+}
+
+int nvo_dense_ffn_q2(const uint16_t *x, int m, int hidden, int inter,
+                     const nvo_q2_weight *wg, const nvo_q2_weight *wu,
+                     const nvo_q2_weight *wd, uint16_t *y, double *y_exact,
+                     uint16_t *g, uint16_t *u, uint16_t *a, int nthreads) {
+  if (m < 0 || !q2_weight_ok(wg) || !q2_weight_ok(wu) || !q2_weight_ok(wd) ||
+      wg->n != inter || wg->k != hidden || wu->n != inter || wu->k != hidden ||
+      wd->n != hidden || wd->k != inter)
+    return -1;
+  if (m == 0) return 0;
+  size_t mi = (size_t)m * inter;
+  uint16_t *gb = g ? g : (uint16_t *)malloc(2 * mi);
+  uint16_t *ub = u ? u : (uint16_t *)malloc(2 * mi);
+  uint16_t *ab = a ? a : (uint16_t *)malloc(2 * mi);
+  nvo_gemm_q2(x, m, wg, gb, NULL, nthreads);
+  nvo_gemm_q2(x, m, wu, ub, NULL, nthreads);
+  nvo_silu_mul(gb, ub, ab, (int64_t)mi);
+  nvo_gemm_q2(ab, m, wd, y, y_exact, nthreads);
+  if (!g) free(gb);
+  if (!u) free(ub);
+  if (!a) free(ab);
+  return 0;
+}

@@ -29,6 +29,9 @@
  *   - the W8A8 fixed format (page layers/dense_ffn_fixed.rs, `Fixed::W8a8`;
  *     page layers/dense_ffn_overlays.rs, `set_fp8_weights`): block-scaled
  *     FP8 weights, per-row FP8 activations, the same FFN step order.
+ *   - packed-Q2 weights (page layers/dense_ffn_prefill.rs, `prefill_q2`):
+ *     2-bit codes with an fp16 scale per group, dequantized to bf16, then
+ *     the W4A16 step order with bf16 activations.
  *
  * Layout (host memory, row-major):
  *   x, g, u, a, y : bf16 bit patterns (uint16_t) [rows][cols]
@@ -142,6 +145,25 @@ int nvo_dense_ffn_w8a8(const uint16_t *x, int m, int hidden, int inter,
                        const nvo_fp8_weight *wg, const nvo_fp8_weight *wu,
                        const nvo_fp8_weight *wd, uint16_t *y, double *y_exact,
                        uint16_t *g, uint16_t *u, uint16_t *a, int nthreads);
+
+/* Packed-Q2 weights (see the .c file for the reading): 2-bit codes
+ * [n][k/4] (element 4j+i in bits 2i..2i+1 of byte j), fp16 scales
+ * [n][k/group]; W = bf16((q - 2) * d). */
+typedef struct {
+  const uint8_t *codes;   /* [n][k/4] */
+  const uint16_t *scales; /* [n][k/group], fp16 bit patterns */
+  int group;
+  int n, k;
+} nvo_q2_weight;
+
+double nvo_fp16_value(uint16_t h);
+void nvo_dequant_q2(const nvo_q2_weight *w, double *out);
+int nvo_gemm_q2(const uint16_t *x, int m, const nvo_q2_weight *w, uint16_t *y,
+                double *y_exact, int nthreads);
+int nvo_dense_ffn_q2(const uint16_t *x, int m, int hidden, int inter,
+                     const nvo_q2_weight *wg, const nvo_q2_weight *wu,
+                     const nvo_q2_weight *wd, uint16_t *y, double *y_exact,
+                     uint16_t *g, uint16_t *u, uint16_t *a, int nthreads);
 
 #ifdef __cplusplus
 }

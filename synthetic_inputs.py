@@ -19,6 +19,10 @@ Weight recipe: E2M1 codes uniform over all 16 nibbles (so -0 appears),
 E4M3 block scales 2^u with u ~ U(-4, 0) cast to float8_e4m3fn by torch,
 tensor scale 1.0.  X ~ N(0, 1) cast to bf16 by torch.
 
+Packed-Q2 weight recipe: 2-bit codes uniform over 0..3, one fp16 scale per
+group of 128 K elements drawn as 2^u with u ~ U(-4, 0) cast to float16 by
+torch (11-bit mantissas, so the bf16 dequantization rounds).
+
 FP8 weight recipe (W8A8): E4M3 codes uniform over the 254 non-NaN bytes (so
 subnormals, -0 and +-448 appear), one fp32 scale per 128 x 128 block drawn
 as 2^u with u ~ U(-10, -6) (not powers of two in general).
@@ -46,6 +50,8 @@ W8A8_ROW_COUNTS = (1, 8, 64, 512)
 _X, _WG_C, _WG_S, _WU_C, _WU_S, _WD_C, _WD_S, _OUTLIER = range(8)
 _LORA = 8  # LoRA pairs: streams 8..13
 _FP8 = 16  # FP8 weights: streams 16..21 (codes, scales per matrix)
+_Q2 = 24   # packed-Q2 weights: streams 24..29
+Q2_GROUP = 128
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -172,3 +178,46 @@ def fp8_workload(name: str, seed: int = 0, m: int | None = None):
     rows = spec["m"] if m is None else m
     x = activations(rows, spec["hidden"], seed, spec["outliers"])
     return (x,) + fp8_ffn_weights(spec["hidden"], spec["inter"], seed)
+
+
+@dataclass
+class Q2Weight:
+    """Host (or device) tensors of one packed-Q2 matrix [n, k]."""
+    codes: torch.Tensor   # uint8 [n, k/4]
+    scales: torch.Tensor  # uint16 [n, k/group] (fp16 bit patterns)
+    group: int = Q2_GROUP
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.codes.shape[1] * 4)
+
+    def to(self, device) -> "Q2Weight":
+        return Q2Weight(self.codes.to(device), self.scales.to(device), self.group)
+
+
+def q2_weight(n: int, k: int, seed: int, which: int, group: int = Q2_GROUP) -> Q2Weight:
+    assert k % group == 0
+    codes = torch.randint(0, 256, (n, k // 4), generator=_gen(seed, _Q2 + 2 * which),
+                          dtype=torch.uint8)
+    u = torch.rand((n, k // group), generator=_gen(seed, _Q2 + 2 * which + 1),
+                   dtype=torch.float32) * -4.0
+    scales = torch.exp2(u).to(torch.float16).view(torch.int16).view(torch.uint16)
+    return Q2Weight(codes, scales.contiguous(), group)
+
+
+def q2_ffn_weights(hidden: int, inter: int, seed: int = 0, group: int = Q2_GROUP):
+    return (q2_weight(inter, hidden, seed, 0, group), q2_weight(inter, hidden, seed, 1, group),
+            q2_weight(hidden, inter, seed, 2, group))
+
+
+def q2_workload(name: str, seed: int = 0, m: int | None = None):
+    """(x bf16 [m, hidden], wg, wu, wd) with packed-Q2 weights, on the CPU;
+    the shapes and X of workload ``name``."""
+    spec = WORKLOADS[name]
+    rows = spec["m"] if m is None else m
+    x = activations(rows, spec["hidden"], seed, spec["outliers"])
+    return (x,) + q2_ffn_weights(spec["hidden"], spec["inter"], seed)
