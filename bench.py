@@ -3,8 +3,9 @@
 A step is one dense_ffn_forward (W4A16: gate+up+silu, down) over one batch
 of synthetic rows, inputs resident in HBM.  The headline workload is the
 single-row decode FFN (m=1, hidden=4096, inter=12288); the m=64 and
-m=2048 workloads the metric also names, and the W4A4 and W8A8 fixed-format
-arms, are measured in the same run and reported under "workloads".
+m=2048 workloads the metric also names, the W4A4 and W8A8 fixed-format arms
+and the packed-Q2 weights are measured in the same run and reported under
+"workloads".
 
 Cold weights: every weight set fits in the 256 MB Infinity Cache, so each
 step reads the next of R replicas with R x size >= 1 GiB; the reported
@@ -56,10 +57,14 @@ def _replicas(ws, count, device):
     import nvfp4_weight_dense_amd as nv
     out = []
     nvfp4 = hasattr(ws[0], "ts")
+    q2 = hasattr(ws[0], "group")
     for _ in range(count):
         if nvfp4:
             out.append([nv.NVFP4Weight(w.codes.to(device, copy=True),
                                        w.scales.to(device, copy=True), w.ts) for w in ws])
+        elif q2:
+            out.append([nv.Q2Weight(w.codes.to(device, copy=True),
+                                    w.scales.to(device, copy=True), w.group) for w in ws])
         else:
             out.append([nv.FP8Weight(w.codes.to(device, copy=True),
                                      w.scales.to(device, copy=True)) for w in ws])
@@ -81,14 +86,16 @@ def _time_loop(fn, reps, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
-def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=0, w8a8=False):
+def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=0, w8a8=False,
+                q2=False):
     import torch
 
     import nvfp4_weight_dense_amd as nv
     import synthetic_inputs as si
 
     dev = torch.device("cuda:0")
-    x, wg, wu, wd = (si.fp8_workload if w8a8 else si.workload)(name, m=m)
+    gen = si.fp8_workload if w8a8 else (si.q2_workload if q2 else si.workload)
+    x, wg, wu, wd = gen(name, m=m)
     m, hidden = x.shape
     inter = wg.n
     wbytes = weight_bytes(wg) + weight_bytes(wu) + weight_bytes(wd)
@@ -111,9 +118,9 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
         wgu = si.NvWeight(torch.cat([wg.codes, wu.codes]), torch.cat([wg.scales, wu.scales]), wg.ts)
         reps = _replicas((wgu, wd), nrep, dev)
         fn = nv.dense_ffn_forward_fused
-    elif w8a8:
+    elif w8a8 or q2:
         reps = _replicas((wg, wu, wd), nrep, dev)
-        fn = nv.dense_ffn_forward_w8a8
+        fn = nv.dense_ffn_forward_w8a8 if w8a8 else nv.dense_ffn_forward_q2
     else:
         reps = _replicas((wg, wu, wd), nrep, dev)
         fn = nv.dense_ffn_forward_w4a4 if w4a4 else nv.dense_ffn_forward
@@ -122,6 +129,7 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
     res = {
         "workload": f"{name} m={m} hidden={hidden} inter={inter}" + (" w4a4" if w4a4 else "")
                     + (" (block-scaled FP8 weights, per-row FP8 activations)" if w8a8 else "")
+                    + (" (packed-Q2 weights, group 128, bf16 activations)" if q2 else "")
                     + (" fused gate+up weight" if fused else "")
                     + (f" + LoRA rank {lora_rank} on gate, up, down" if lora_rank else ""),
         "m": m, "hidden": hidden, "inter": inter,
@@ -284,6 +292,14 @@ def main():
     del ctx
     workloads = []
     if not args.only_headline:
+        for name, steps, w4a4, m, fused, rank, q2 in (
+                ("decode", args.steps, False, None, False, 0, True),
+                ("smallm", max(20, args.steps // 2), False, None, False, 0, True),
+                ("prefill", max(5, args.steps // 20), False, None, False, 0, True)):
+            r, c = measure_ffn(name, steps, max(3, args.warmup // 2), q2=q2)
+            del c
+            torch.cuda.empty_cache()
+            workloads.append(r)
         for name, steps, w4a4, m, fused, rank in (
                 ("decode", args.steps, False, None, True, 0),
                 ("decode", args.steps, False, None, False, 16),

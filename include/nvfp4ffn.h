@@ -245,6 +245,39 @@ int dense_ffn_forward_w8a8(const void *x, int32_t m, int32_t hidden,
                            const fp8_weight *wu, const fp8_weight *wd,
                            void *out, void *stream);
 
+/* ---- packed-Q2 weights -----------------------------------------------------
+ * The packed-Q2 FFN of the pages (page layers/dense_ffn_prefill.rs,
+ * `prefill_q2`, SiLU only): Q2_0 weights with a group size, dequantized to
+ * BF16 and multiplied by the bf16 activations (the default leg there; the
+ * W2A8 MMQ leg is opt-in).  Q2_0 is not defined on the pages; the reading:
+ *   codes : device, uint8 [n][k/4]; element 4j+i in bits 2i..2i+1 of byte j;
+ *   scales: device, fp16 bit patterns [n][k/group];
+ *   W[r][c] = bf16((q - 2) * scales[r][c/group]), nearest-even.
+ * group is a power of two, at least 32, dividing k (the pages' MMQ leg
+ * uses 128); k % 32 == 0; codes 16-byte and scales 2-byte aligned.  The
+ * kernels dequantize in registers: no bf16 copy of the weight is made. */
+typedef struct q2_weight {
+  const uint8_t *codes;
+  const uint16_t *scales;
+  int32_t group;
+  int32_t n;
+  int32_t k;
+} q2_weight;
+
+/* y[m][n] = bf16( sum_k x[m][k] * W[n][k] ), fp32 accumulation.
+ * x: bf16 [m][k]; y: bf16 [m][n]. */
+int q2_gemm_w2a16(const void *x, int32_t m, const q2_weight *w, void *y,
+                  void *stream);
+
+/* Dense SwiGLU FFN on packed-Q2 weights: gate, up and silu_mul in one
+ * launch, then down (page layers/dense_ffn_prefill.rs, `prefill_q2`).
+ * wg, wu: [inter][hidden]; wd: [hidden][inter].  Errors as
+ * dense_ffn_forward. */
+int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden,
+                         int32_t inter, const q2_weight *wg,
+                         const q2_weight *wu, const q2_weight *wd, void *out,
+                         void *stream);
+
 /* The calling thread's last error message ("" if none). */
 const char *nvfp4_last_error(void);
 

@@ -37,7 +37,7 @@ __all__ = [
     "nvfp4_gate_up_silu_w4a16", "dense_ffn_forward", "dense_ffn_forward_w4a4",
     "nvfp4_gate_up_views", "dense_ffn_forward_fused", "LoraPair", "nvfp4_lora_delta",
     "dense_ffn_forward_lora", "FP8Weight", "fp8_quantize_rows", "fp8_gemm_w8a8",
-    "dense_ffn_forward_w8a8",
+    "dense_ffn_forward_w8a8", "Q2Weight", "q2_gemm_w2a16", "dense_ffn_forward_q2",
     "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
 ]
 
@@ -107,6 +107,24 @@ class _CFp8Weight(ctypes.Structure):
     ]
 
 
+@dataclass
+class Q2Weight:
+    """One packed-Q2 matrix W[n][k] on the GPU."""
+    codes: torch.Tensor   # uint8 [n, k/4], element 4j+i in bits 2i..2i+1 of byte j
+    scales: torch.Tensor  # fp16 (or its uint16/int16 bits) [n, k/group]
+    group: int = 128
+
+
+class _CQ2Weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("group", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -133,6 +151,9 @@ def load_library(path: str = LIB_PATH):
         "dense_ffn_forward_fused": [vp, i32, i32, i32, wp, wp, vp, vp],
         "nvfp4_lora_delta": [vp, i32, i32, ctypes.POINTER(_CLoraPair), i32, vp, vp],
         "dense_ffn_forward_lora": [vp, i32, i32, i32, wp, wp, wp, ctypes.POINTER(_CLora), vp, vp],
+        "q2_gemm_w2a16": [vp, i32, ctypes.POINTER(_CQ2Weight), vp, vp],
+        "dense_ffn_forward_q2": [vp, i32, i32, i32, ctypes.POINTER(_CQ2Weight),
+                                 ctypes.POINTER(_CQ2Weight), ctypes.POINTER(_CQ2Weight), vp, vp],
         "fp8_quantize_rows": [vp, i32, i32, vp, vp, vp],
         "fp8_gemm_w8a8": [vp, i32, ctypes.POINTER(_CFp8Weight), vp, vp],
         "dense_ffn_forward_w8a8": [vp, i32, i32, i32, ctypes.POINTER(_CFp8Weight),
@@ -405,4 +426,42 @@ def dense_ffn_forward_w8a8(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None
         out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
     _check(L.dense_ffn_forward_w8a8(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
                                     ctypes.byref(cd), _ptr(out), _stream(stream)))
+    return out
+
+
+# ---- packed-Q2 weights ------------------------------------------------------------
+
+def _cq2(w) -> _CQ2Weight:
+    if w.codes.dtype != torch.uint8 or not w.codes.is_contiguous() or not w.codes.is_cuda:
+        raise ValueError("q2 weight codes: expected a contiguous uint8 GPU tensor")
+    if w.scales.element_size() != 2 or not w.scales.is_contiguous() or not w.scales.is_cuda:
+        raise ValueError("q2 weight scales: expected a contiguous 16-bit GPU tensor of fp16 bits")
+    n, k4 = w.codes.shape
+    if tuple(w.scales.shape) != (n, (4 * k4) // int(w.group)):
+        raise ValueError("q2 weight scales: expected [n, k/group]")
+    return _CQ2Weight(w.codes.data_ptr(), w.scales.data_ptr(), int(w.group), int(n), int(4 * k4))
+
+
+def q2_gemm_w2a16(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
+    """y = bf16(x . W^T) with W = bf16((q - 2) * d) from a packed-Q2 weight."""
+    L = load_library()
+    x = _act(x, "x")
+    cw = _cq2(w)
+    if y is None:
+        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    _check(L.q2_gemm_w2a16(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
+    return y
+
+
+def dense_ffn_forward_q2(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None = None,
+                         stream=None):
+    """Dense SwiGLU FFN on packed-Q2 weights (bf16 activations)."""
+    L = load_library()
+    x = _act(x, "x")
+    cg, cu, cd = _cq2(wg), _cq2(wu), _cq2(wd)
+    m, hidden = x.shape
+    if out is None:
+        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
+    _check(L.dense_ffn_forward_q2(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
+                                  ctypes.byref(cd), _ptr(out), _stream(stream)))
     return out

@@ -395,6 +395,38 @@ int run_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const Fp8MatRef 
                     "W8A8 projection launch");
 }
 
+// ---- packed Q2 ----------------------------------------------------------------------
+
+int check_q2_weight(const q2_weight *w, const char *name, int *gshift) {
+  if (!w) return fail(NVFP4_EINVAL, "%s: null weight descriptor", name);
+  if (!w->codes || !w->scales) return fail(NVFP4_EINVAL, "%s: null codes or scales pointer", name);
+  if (w->n <= 0 || w->k <= 0) return fail(NVFP4_ESHAPE, "%s: n=%d k=%d must be positive", name, w->n, w->k);
+  if (w->k % 32 != 0) return fail(NVFP4_ESHAPE, "%s: k=%d is not a multiple of 32", name, w->k);
+  if (w->k > kMaxDim || w->n > kMaxDim)
+    return fail(NVFP4_ESHAPE, "%s: n=%d k=%d exceed %d", name, w->n, w->k, kMaxDim);
+  int sh = 5;
+  while (sh < 21 && (1 << sh) != w->group) ++sh;
+  if (w->group < 32 || (1 << sh) != w->group || w->k % w->group != 0)
+    return fail(NVFP4_ESHAPE, "%s: group=%d must be a power of two >= 32 dividing k=%d", name,
+                w->group, w->k);
+  if (misaligned(w->codes) || ((uintptr_t)w->scales & 1u))
+    return fail(NVFP4_EINVAL, "%s: codes must be 16-byte and scales 2-byte aligned", name);
+  *gshift = sh;
+  return NVFP4_OK;
+}
+
+Q2MatRef q2_mat(const q2_weight *w) { return Q2MatRef{w->codes, w->scales}; }
+
+int run_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w, void *y,
+           void *scratch, hipStream_t s) {
+  StreamPlan pl = stream_plan(n, k);
+  unsigned *counters = nullptr;
+  int rc = counters_get(stream_counter_words(pl, m), &counters);
+  if (rc) return rc;
+  return hip_status(launch_q2(x, m, k, n, gshift, nmat, w, y, (float *)scratch, counters, pl, s),
+                    "packed-Q2 projection launch");
+}
+
 }  // namespace
 
 // ---- C ABI ---------------------------------------------------------------------------
@@ -767,6 +799,58 @@ int dense_ffn_forward_w8a8(const void *x, int32_t m, int32_t hidden, int32_t int
   if ((rc = hip_status(launch_quantize_rows_fp8(act, m, inter, qa.codes, qa.rs, s), "fp8 quantize launch")))
     return rc;
   return run_w8a8(Fp8ActRef{qa.codes, qa.rs}, m, inter, hidden, 1, &wdm, out, scr, s);
+}
+
+int q2_gemm_w2a16(const void *x, int32_t m, const q2_weight *w, void *y, void *stream) {
+  g_err.clear();
+  int rc, gs = 0;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(y, m, "y")) || (rc = check_q2_weight(w, "w", &gs)))
+    return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  log_path("gemm_q2", "q2", m, w->n, w->k);
+  const size_t part = w8a8_scratch_bytes(m, w->n, w->k, 1);
+  void *scr = nullptr;
+  if (part && (rc = arena_get(part, &scr))) return rc;
+  ProfileScope ps("gemm_q2", m, s);
+  Q2MatRef wm = q2_mat(w);
+  return run_q2(x, m, w->k, w->n, gs, 1, &wm, y, scr, s);
+}
+
+int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden, int32_t inter, const q2_weight *wg,
+                         const q2_weight *wu, const q2_weight *wd, void *out, void *stream) {
+  g_err.clear();
+  int rc, gsg = 0, gsu = 0, gsd = 0;
+  if ((rc = check_act(x, m, "x")) || (rc = check_act(out, m, "out"))) return rc;
+  if (hidden <= 0 || inter <= 0)
+    return fail(NVFP4_ESHAPE, "hidden=%d inter=%d must be positive", hidden, inter);
+  if ((rc = check_q2_weight(wg, "wg", &gsg)) || (rc = check_q2_weight(wu, "wu", &gsu)) ||
+      (rc = check_q2_weight(wd, "wd", &gsd)))
+    return rc;
+  if (wg->n != inter || wg->k != hidden || wu->n != inter || wu->k != hidden)
+    return fail(NVFP4_ESHAPE, "wg/wu must be [inter=%d][hidden=%d], got [%d][%d] and [%d][%d]",
+                inter, hidden, wg->n, wg->k, wu->n, wu->k);
+  if (wd->n != hidden || wd->k != inter)
+    return fail(NVFP4_ESHAPE, "wd must be [hidden=%d][inter=%d], got [%d][%d]", hidden, inter,
+                wd->n, wd->k);
+  if (gsg != gsu)
+    return fail(NVFP4_ESHAPE, "wg and wu must share one group size (got %d and %d)", wg->group, wu->group);
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  log_path("dense_ffn_forward_q2", "q2", m, inter, hidden);
+  const size_t act_b = align256((size_t)2 * m * inter);
+  size_t part = w8a8_scratch_bytes(m, inter, hidden, 2);
+  const size_t part_d = w8a8_scratch_bytes(m, hidden, inter, 1);
+  if (part_d > part) part = part_d;
+  void *base = nullptr;
+  if ((rc = arena_get(act_b + part, &base))) return rc;
+  char *act = (char *)base;
+  char *scr = act + act_b;
+  ProfileScope ps("dense_total q2", m, s);
+  Q2MatRef w2[2] = {q2_mat(wg), q2_mat(wu)};
+  Q2MatRef wdm = q2_mat(wd);
+  if ((rc = run_q2(x, m, hidden, inter, gsg, 2, w2, act, scr, s))) return rc;
+  return run_q2(act, m, inter, hidden, gsd, 1, &wdm, out, scr, s);
 }
 
 }  // extern "C"

@@ -147,6 +147,19 @@ struct Fp8ActRef {
 // Per-row FP8 quantizer: s_row = amax/448, codes = E4M3(x / s_row).
 hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes,
                                     float *row_scale, hipStream_t stream);
+// ---- packed-Q2 weights: 2-bit codes, fp16 scale per group, bf16 activations ----
+struct Q2MatRef {
+  const uint8_t *codes;    // [n][k/4]
+  const uint16_t *scales;  // fp16 [n][k >> gshift]
+};
+// Projection (nmat 1) or gate+up+silu (nmat 2) with W = bf16((q - 2) * d);
+// plan, partial and counter rules as launch_stream.  group = 1 << gshift,
+// 32 <= group, k % group == 0.
+hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat,
+                     const Q2MatRef *w, void *y, float *partial,
+                     unsigned *counters, const StreamPlan &pl,
+                     hipStream_t stream);
+
 // FP8 projection, nmat 1 or 2 (gate+up+silu) as launch_stream, with the
 // same plan, partial and counter rules (stream_plan, stream_partial_floats,
 // stream_counter_words).

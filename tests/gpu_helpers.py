@@ -56,5 +56,22 @@ def assert_close(gpu_bits: np.ndarray, ref_exact: np.ndarray, what: str = ""):
     return e
 
 
+def assert_close_elem(gpu_bits: np.ndarray, ref: np.ndarray, what: str = ""):
+    """|gpu - ref| <= 2e-2 * rms(ref) + 2^-8 * |ref| element by element.
+
+    The second term is one bf16 ulp of the element: rounding an output to
+    bf16 moves it by up to 2^-9 * |ref_i|, so an output beyond about 10 *
+    rms(ref) cannot meet the plain 2e-2 * rms(ref) bound in bf16 at all;
+    one more ulp covers a double rounding at a tie after an fp32 sum."""
+    assert gpu_bits.shape == ref.shape, (gpu_bits.shape, ref.shape)
+    g = bf16_f64(gpu_bits)
+    assert np.all(np.isfinite(g)), what + ": non-finite output"
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    bound = TOL * rms + 2.0 ** -8 * np.abs(ref)
+    worst = float(np.max(np.abs(g - ref) / np.maximum(bound, 1e-300)))
+    assert worst <= 1.0, f"{what}: max |err| / bound = {worst:.4g}"
+    return worst
+
+
 def sync():
     torch.cuda.synchronize()

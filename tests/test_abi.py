@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
                  "dense_ffn_forward_w4a4", "nvfp4_quantize_rows", "nvfp4_gate_up_silu_w4a16",
                  "nvfp4_gate_up_views", "dense_ffn_forward_fused", "nvfp4_lora_delta",
                  "dense_ffn_forward_lora", "fp8_quantize_rows", "fp8_gemm_w8a8",
-                 "dense_ffn_forward_w8a8",
+                 "dense_ffn_forward_w8a8", "q2_gemm_w2a16", "dense_ffn_forward_q2",
                  "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version"]:
         assert want in names
 
@@ -193,6 +193,32 @@ def test_w8a8_argument_checks():
     assert r(_f8(inter, 32), wu, wd) == nv.NVFP4_ESHAPE
     assert r(wg, wu, wd, m=0) == nv.NVFP4_OK
     assert r(wg, wu, wd, m=-1) == nv.NVFP4_EINVAL
+
+
+def _q2(n=64, k=256, group=128, codes=0x10000, scales=0x20000):
+    return nv._CQ2Weight(codes, scales, group, n, k)
+
+
+def test_q2_argument_checks():
+    L = _lib()
+    x, y, s = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x80000), ctypes.c_void_p(None)
+    assert L.q2_gemm_w2a16(x, 4, None, y, s) == nv.NVFP4_EINVAL
+    assert L.q2_gemm_w2a16(x, 4, ctypes.byref(_q2(codes=0)), y, s) == nv.NVFP4_EINVAL
+    assert L.q2_gemm_w2a16(x, 4, ctypes.byref(_q2(k=240)), y, s) == nv.NVFP4_ESHAPE
+    for bad_group in (0, 16, 96, 512):  # below 32, not a power of two, not dividing k
+        assert L.q2_gemm_w2a16(x, 4, ctypes.byref(_q2(group=bad_group)), y, s) == nv.NVFP4_ESHAPE
+        assert "group" in nv.nvfp4_last_error()
+    assert L.q2_gemm_w2a16(x, 4, ctypes.byref(_q2(scales=0x20001)), y, s) == nv.NVFP4_EINVAL
+    assert L.q2_gemm_w2a16(x, 0, ctypes.byref(_q2()), y, s) == nv.NVFP4_OK
+    hidden, inter = 256, 384
+    wg, wu, wd = _q2(inter, hidden), _q2(inter, hidden), _q2(hidden, inter)
+    fn = L.dense_ffn_forward_q2
+    r = lambda g, u, d, m=2: fn(x, m, hidden, inter, ctypes.byref(g), ctypes.byref(u),
+                                ctypes.byref(d), y, s)
+    assert r(wg, wu, _q2(inter, hidden)) == nv.NVFP4_ESHAPE
+    assert "wd must be" in nv.nvfp4_last_error()
+    assert r(wg, _q2(inter, hidden, group=64), wd) == nv.NVFP4_ESHAPE   # gate and up groups differ
+    assert r(wg, wu, wd, m=0) == nv.NVFP4_OK
 
 
 def test_binding_refuses_cpu_tensors():

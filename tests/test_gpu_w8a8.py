@@ -23,7 +23,7 @@ import torch
 import nvfp4_weight_dense_amd as nv
 import oracle
 import synthetic_inputs as si
-from gpu_helpers import assert_close, bf16_f64, bits, sync
+from gpu_helpers import assert_close, assert_close_elem, bits, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -38,16 +38,6 @@ def g8(w: si.Fp8Weight) -> nv.FP8Weight:
 
 def o8(w: si.Fp8Weight) -> oracle.Fp8Weight:
     return oracle.Fp8Weight(w.codes.numpy(), w.scales.numpy())
-
-
-def assert_close_elem(gpu_bits, ref, what):
-    """|gpu - ref| <= 2e-2 * rms(ref) + 2^-8 * |ref| element by element."""
-    g = bf16_f64(gpu_bits)
-    assert np.all(np.isfinite(g)), what + ": non-finite output"
-    rms = float(np.sqrt(np.mean(ref ** 2)))
-    bound = 2e-2 * rms + 2.0 ** -8 * np.abs(ref)
-    worst = float(np.max(np.abs(g - ref) / bound))
-    assert worst <= 1.0, f"{what}: max |err| / bound = {worst:.4g}"
 
 
 def _rows_with_edge_cases(m, k, seed):
