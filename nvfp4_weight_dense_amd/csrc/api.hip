@@ -29,6 +29,8 @@
 #include <string>
 #include <tuple>
 
+#include <rocblas/rocblas.h>
+
 #include "launchers.h"
 #include "nvfp4_common.h"
 #include "nvfp4ffn.h"
@@ -417,6 +419,46 @@ int check_q2_weight(const q2_weight *w, const char *name, int *gshift) {
 
 Q2MatRef q2_mat(const q2_weight *w) { return Q2MatRef{w->codes, w->scales}; }
 
+// ---- many rows on packed-Q2 weights: dequantize to bf16, then a library GEMM ------
+// (page layers/dense_ffn_prefill.rs, `prefill_q2`: the default leg dequantizes
+// each projection to BF16 into one shared scratch and runs the BF16 GEMM; the
+// projections run in order on the stream, so one scratch serves all three).
+// One rocBLAS handle per device, created on first use; calls on a device are
+// serialized by a mutex because the handle's stream is per call.
+std::mutex g_blas_mu;
+rocblas_handle g_blas[kMaxDevices];
+
+int blas_gemm_bf16(const void *x, int m, int k, const void *wbf16, int n, void *y, hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
+    g_blas[dev] = nullptr;
+    return fail(NVFP4_EHIP, "rocblas_create_handle failed");
+  }
+  rocblas_handle h = g_blas[dev];
+  if (rocblas_set_stream(h, s) != rocblas_status_success) return fail(NVFP4_EHIP, "rocblas_set_stream failed");
+  // row-major y[m][n] = x[m][k] . W[n][k]^T is column-major y^T = W^T' x^T':
+  // A = W seen as column-major [k][n] (transposed), B = x as column-major [k][m]
+  const float alpha = 1.0f, beta = 0.0f;
+  const rocblas_status st = rocblas_gemm_ex(
+      h, rocblas_operation_transpose, rocblas_operation_none, n, m, k, &alpha, wbf16,
+      rocblas_datatype_bf16_r, k, x, rocblas_datatype_bf16_r, k, &beta, y, rocblas_datatype_bf16_r, n, y,
+      rocblas_datatype_bf16_r, n, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  if (st != rocblas_status_success) return fail(NVFP4_EHIP, "rocblas_gemm_ex failed (status %d)", (int)st);
+  return NVFP4_OK;
+}
+
+int q2_gemm_many_rows(const void *x, int m, int k, int n, int gshift, const Q2MatRef &w, void *y,
+                      void *wbf16, hipStream_t s) {
+  int rc;
+  if ((rc = hip_status(launch_dequant_q2_bf16(w, n, k, gshift, wbf16, s), "Q2 dequant launch"))) return rc;
+  return blas_gemm_bf16(x, m, k, wbf16, n, y, s);
+}
+
+bool q2_many_rows(int m) { return m > cfg().smallm_max_m; }
+
 int run_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w, void *y,
            void *scratch, hipStream_t s) {
   StreamPlan pl = stream_plan(n, k);
@@ -438,6 +480,18 @@ int32_t nvfp4_abi_version(void) { return 1; }
 const char *nvfp4_last_error(void) { return g_err.c_str(); }
 
 void nvfp4_release(void) {
+  {
+    std::lock_guard<std::mutex> lb(g_blas_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (int d = 0; d < kMaxDevices; ++d)
+      if (g_blas[d]) {
+        (void)hipSetDevice(d);
+        (void)rocblas_destroy_handle(g_blas[d]);
+        g_blas[d] = nullptr;
+      }
+    (void)hipSetDevice(cur);
+  }
   std::lock_guard<std::mutex> lk(g_arena_mu);
   int cur = 0;
   (void)hipGetDevice(&cur);
@@ -808,12 +862,19 @@ int q2_gemm_w2a16(const void *x, int32_t m, const q2_weight *w, void *y, void *s
     return rc;
   if (m == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
+  Q2MatRef wm = q2_mat(w);
+  if (q2_many_rows(m)) {
+    log_path("gemm_q2", "dequant+gemm", m, w->n, w->k);
+    void *wb = nullptr;
+    if ((rc = arena_get(align256((size_t)2 * w->n * w->k), &wb))) return rc;
+    ProfileScope ps("gemm_q2", m, s);
+    return q2_gemm_many_rows(x, m, w->k, w->n, gs, wm, y, wb, s);
+  }
   log_path("gemm_q2", "q2", m, w->n, w->k);
   const size_t part = w8a8_scratch_bytes(m, w->n, w->k, 1);
   void *scr = nullptr;
   if (part && (rc = arena_get(part, &scr))) return rc;
   ProfileScope ps("gemm_q2", m, s);
-  Q2MatRef wm = q2_mat(w);
   return run_q2(x, m, w->k, w->n, gs, 1, &wm, y, scr, s);
 }
 
@@ -837,6 +898,23 @@ int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden, int32_t inter
     return fail(NVFP4_ESHAPE, "wg and wu must share one group size (got %d and %d)", wg->group, wu->group);
   if (m == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
+  Q2MatRef mg = q2_mat(wg), mu = q2_mat(wu), md = q2_mat(wd);
+  if (q2_many_rows(m)) {
+    // gate and up into [m][inter] bf16 buffers, silu_mul over gate, down;
+    // one bf16 weight scratch shared by the three projections in turn
+    log_path("dense_ffn_forward_q2", "dequant+gemm", m, inter, hidden);
+    const size_t gu_b = align256((size_t)2 * m * inter);
+    const size_t wb_b = align256((size_t)2 * inter * hidden);
+    void *base = nullptr;
+    if ((rc = arena_get(2 * gu_b + wb_b, &base))) return rc;
+    char *g = (char *)base, *u = g + gu_b, *wb = u + gu_b;
+    ProfileScope ps("dense_total q2", m, s);
+    if ((rc = q2_gemm_many_rows(x, m, hidden, inter, gsg, mg, g, wb, s)) ||
+        (rc = q2_gemm_many_rows(x, m, hidden, inter, gsu, mu, u, wb, s)))
+      return rc;
+    if ((rc = hip_status(launch_silu_mul(g, u, g, (int64_t)m * inter, s), "silu_mul launch"))) return rc;
+    return q2_gemm_many_rows(g, m, inter, hidden, gsd, md, out, wb, s);
+  }
   log_path("dense_ffn_forward_q2", "q2", m, inter, hidden);
   const size_t act_b = align256((size_t)2 * m * inter);
   size_t part = w8a8_scratch_bytes(m, inter, hidden, 2);
@@ -847,10 +925,9 @@ int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden, int32_t inter
   char *act = (char *)base;
   char *scr = act + act_b;
   ProfileScope ps("dense_total q2", m, s);
-  Q2MatRef w2[2] = {q2_mat(wg), q2_mat(wu)};
-  Q2MatRef wdm = q2_mat(wd);
+  Q2MatRef w2[2] = {mg, mu};
   if ((rc = run_q2(x, m, hidden, inter, gsg, 2, w2, act, scr, s))) return rc;
-  return run_q2(act, m, inter, hidden, gsd, 1, &wdm, out, scr, s);
+  return run_q2(act, m, inter, hidden, gsd, 1, &md, out, scr, s);
 }
 
 }  // extern "C"

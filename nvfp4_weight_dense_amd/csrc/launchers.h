@@ -160,6 +160,10 @@ hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat,
                      unsigned *counters, const StreamPlan &pl,
                      hipStream_t stream);
 
+// W -> bf16 [n][k] (out 16-byte aligned), for the many-row library GEMM.
+hipError_t launch_dequant_q2_bf16(const Q2MatRef &w, int n, int k, int gshift,
+                                  void *out, hipStream_t stream);
+
 // FP8 projection, nmat 1 or 2 (gate+up+silu) as launch_stream, with the
 // same plan, partial and counter rules (stream_plan, stream_partial_floats,
 // stream_counter_words).

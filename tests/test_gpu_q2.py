@@ -9,6 +9,9 @@ C-ABI.
   where the bf16 rounding of the output alone exceeds 2e-2 * rms, so it is
   held to the element-wise bound 2e-2 * rms(ref) + 2^-8 * |ref_i| (one
   bf16 ulp of the element).
+* Up to 64 rows the projections stream the packed weight (k_q2); more rows
+  take the pages' default leg (dequantize to bf16, then a library GEMM).
+  Both are covered: tiny FFNs at m in {65, 130}, the prefill workload.
 * Exact case, bit for bit at a full projection shape: integer activations
   in [-2, 2] and power-of-two scales make every dequantized weight, every
   product and every fp32 partial sum exact, so any summation order gives
@@ -53,7 +56,8 @@ def test_q2_gemm_matches_oracle(m, n, k, group):
     assert_close(bits(y), ye, f"q2 gemm m={m} n={n} k={k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(2, 12288, 4096), (33, 4096, 12288)])
+# m = 130 takes the many-row leg (dequantize to bf16, library GEMM)
+@pytest.mark.parametrize("m,n,k", [(2, 12288, 4096), (33, 4096, 12288), (130, 4096, 12288)])
 def test_q2_gemm_exact_case_bit_exact(m, n, k):
     _say(f"q2 gemm exact m={m} n={n} k={k}")
     g = torch.Generator().manual_seed(n)
