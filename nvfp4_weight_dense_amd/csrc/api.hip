@@ -384,12 +384,12 @@ Fp8QuantBuf fp8_quant_layout(char *base, int m, int k) {
 }
 
 size_t w8a8_scratch_bytes(int m, int n, int k, int nmat) {
-  return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+  return align256(4 * w8a8_partial_floats(w8a8_plan(n, k), nmat, m, n));
 }
 
 int run_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const Fp8MatRef *w, void *y,
              void *scratch, hipStream_t s) {
-  StreamPlan pl = stream_plan(n, k);
+  StreamPlan pl = w8a8_plan(n, k);
   unsigned *counters = nullptr;
   int rc = counters_get(stream_counter_words(pl, m), &counters);
   if (rc) return rc;
@@ -418,6 +418,10 @@ int check_q2_weight(const q2_weight *w, const char *name, int *gshift) {
 }
 
 Q2MatRef q2_mat(const q2_weight *w) { return Q2MatRef{w->codes, w->scales}; }
+
+size_t q2_scratch_bytes(int m, int n, int k, int nmat) {
+  return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+}
 
 // ---- many rows on packed-Q2 weights: dequantize to bf16, then a library GEMM ------
 // (page layers/dense_ffn_prefill.rs, `prefill_q2`: the default leg dequantizes
@@ -871,7 +875,7 @@ int q2_gemm_w2a16(const void *x, int32_t m, const q2_weight *w, void *y, void *s
     return q2_gemm_many_rows(x, m, w->k, w->n, gs, wm, y, wb, s);
   }
   log_path("gemm_q2", "q2", m, w->n, w->k);
-  const size_t part = w8a8_scratch_bytes(m, w->n, w->k, 1);
+  const size_t part = q2_scratch_bytes(m, w->n, w->k, 1);
   void *scr = nullptr;
   if (part && (rc = arena_get(part, &scr))) return rc;
   ProfileScope ps("gemm_q2", m, s);
@@ -917,8 +921,8 @@ int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden, int32_t inter
   }
   log_path("dense_ffn_forward_q2", "q2", m, inter, hidden);
   const size_t act_b = align256((size_t)2 * m * inter);
-  size_t part = w8a8_scratch_bytes(m, inter, hidden, 2);
-  const size_t part_d = w8a8_scratch_bytes(m, hidden, inter, 1);
+  size_t part = q2_scratch_bytes(m, inter, hidden, 2);
+  const size_t part_d = q2_scratch_bytes(m, hidden, inter, 1);
   if (part_d > part) part = part_d;
   void *base = nullptr;
   if ((rc = arena_get(act_b + part, &base))) return rc;

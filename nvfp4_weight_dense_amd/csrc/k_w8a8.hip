@@ -62,7 +62,9 @@ struct W8Args {
 template <int MT, int NMAT, int CTW>
 struct W8Cfg {
   static constexpr int kRegsPerStep = (NMAT * CTW + MT) * 8;
-  static constexpr int U = kRegsPerStep * 4 <= 128 ? 4 : 2;
+  // steps whose loads are issued together; the largest tiles take one, which
+  // keeps them at two waves per SIMD (measured: m = 64 FFN 127 -> 102 us)
+  static constexpr int U = kRegsPerStep * 4 <= 128 ? 4 : (kRegsPerStep * 2 < 128 ? 2 : 1);
 };
 
 // Eight E4M3 bytes (K order from the low byte of lo) -> eight exact fp16
@@ -298,6 +300,37 @@ hipError_t launch_mt(const W8Args &p, int mt, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
+// Column tiles per workgroup: two, so each activation fragment (loaded and
+// converted once per step) feeds twice as many MFMAs; a function of n only,
+// like the K split, so every row count runs the same K order.
+int w8a8_ctw(int n) { return n > 16 ? 2 : 1; }
+
+StreamPlan w8a8_plan(int n, int k) {
+  constexpr int kTarget = 512;  // workgroups before K is split
+  const int tiles = cdiv(n, 16 * w8a8_ctw(n));
+  const int nsteps = cdiv(k, 128);
+  int ksplit = 1;
+  if (tiles < kTarget) {
+    const int want = cdiv(kTarget, tiles);
+    const int cap = nsteps / (kNW * 2);  // at least two steps per wave
+    ksplit = want < cap ? want : cap;
+    if (ksplit < 1) ksplit = 1;
+  }
+  StreamPlan pl;
+  pl.steps_per_split = cdiv(nsteps, ksplit);
+  pl.ksplit = cdiv(nsteps, pl.steps_per_split);
+  pl.tiles = tiles;
+  return pl;
+}
+
+size_t w8a8_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
+  // per workgroup: [nmat][ksplit][CTW][16*MT][16]
+  const int mt = m >= 64 ? 4 : cdiv(m, 16);
+  return pl.ksplit > 1
+             ? (size_t)pl.tiles * cdiv(m, 64) * nmat * pl.ksplit * w8a8_ctw(n) * 16 * mt * 16
+             : 0;
+}
+
 hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const Fp8MatRef *w, void *y,
                        float *partial, unsigned *counters, const StreamPlan &pl, hipStream_t stream) {
   W8Args p{};
@@ -317,7 +350,7 @@ hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const 
   p.steps_per_split = pl.steps_per_split;
   const int mt = m >= 64 ? 4 : cdiv(m, 16);
   dim3 grid(pl.tiles, pl.ksplit, cdiv(m, 64));
-  if (stream_ctw(n) == 2)
+  if (w8a8_ctw(n) == 2)
     return nmat == 1 ? launch_mt<1, 2>(p, mt, grid, stream) : launch_mt<2, 2>(p, mt, grid, stream);
   return nmat == 1 ? launch_mt<1, 1>(p, mt, grid, stream) : launch_mt<2, 1>(p, mt, grid, stream);
 }

@@ -164,9 +164,12 @@ hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat,
 hipError_t launch_dequant_q2_bf16(const Q2MatRef &w, int n, int k, int gshift,
                                   void *out, hipStream_t stream);
 
-// FP8 projection, nmat 1 or 2 (gate+up+silu) as launch_stream, with the
-// same plan, partial and counter rules (stream_plan, stream_partial_floats,
-// stream_counter_words).
+// FP8 projection, nmat 1 or 2 (gate+up+silu) as launch_stream, with its own
+// plan (w8a8_plan: depends on n and k only) and partial size
+// (w8a8_partial_floats); counters as stream_counter_words.
+int w8a8_ctw(int n);
+StreamPlan w8a8_plan(int n, int k);
+size_t w8a8_partial_floats(const StreamPlan &pl, int nmat, int m, int n);
 hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat,
                        const Fp8MatRef *w, void *y, float *partial,
                        unsigned *counters, const StreamPlan &pl,
