@@ -420,7 +420,7 @@ int check_q2_weight(const q2_weight *w, const char *name, int *gshift) {
 Q2MatRef q2_mat(const q2_weight *w) { return Q2MatRef{w->codes, w->scales}; }
 
 size_t q2_scratch_bytes(int m, int n, int k, int nmat) {
-  return align256(4 * stream_partial_floats(stream_plan(n, k), nmat, m, n));
+  return align256(4 * q2_partial_floats(q2_plan(m, n, k), nmat, m, n));
 }
 
 // ---- many rows on packed-Q2 weights: dequantize to bf16, then a library GEMM ------
@@ -465,7 +465,7 @@ bool q2_many_rows(int m) { return m > cfg().smallm_max_m; }
 
 int run_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w, void *y,
            void *scratch, hipStream_t s) {
-  StreamPlan pl = stream_plan(n, k);
+  StreamPlan pl = q2_plan(m, n, k);
   unsigned *counters = nullptr;
   int rc = counters_get(stream_counter_words(pl, m), &counters);
   if (rc) return rc;

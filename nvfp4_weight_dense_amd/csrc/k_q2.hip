@@ -45,7 +45,8 @@ struct Q2Args {
 template <int MT, int NMAT, int CTW>
 struct Q2Cfg {
   static constexpr int kRegsPerStep = NMAT * CTW * 3 + MT * 16;
-  static constexpr int U = kRegsPerStep * 8 <= 128 ? 8 : (kRegsPerStep * 4 <= 128 ? 4 : 2);
+  static constexpr int U =
+      kRegsPerStep * 8 <= 128 ? 8 : (kRegsPerStep * 4 <= 128 ? 4 : (kRegsPerStep * 2 < 128 ? 2 : 1));
 };
 
 __device__ __forceinline__ uint2 ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -302,6 +303,37 @@ __global__ __launch_bounds__(256) void k_dequant_q2_bf16(const uint32_t *__restr
 
 }  // namespace
 
+// Column tiles per workgroup: with more than 16 rows each activation
+// fragment (64 bytes per row and step) is shared by four column tiles, which
+// divides the activation re-reads from L2 by four; with few rows the tiles
+// stay narrow so that the weight stream spreads over many workgroups.
+int q2_ctw(int m, int n) { return m > 16 ? 4 : (n >= 16 * 2 * 512 ? 2 : 1); }
+
+StreamPlan q2_plan(int m, int n, int k) {
+  constexpr int kTarget = 512;  // workgroups before K is split
+  const int tiles = cdiv(n, 16 * q2_ctw(m, n));
+  const int nsteps = cdiv(k, 128);
+  int ksplit = 1;
+  if (tiles < kTarget) {
+    const int want = cdiv(kTarget, tiles);
+    const int cap = nsteps / (kNW * 2);  // at least two steps per wave
+    ksplit = want < cap ? want : cap;
+    if (ksplit < 1) ksplit = 1;
+  }
+  StreamPlan pl;
+  pl.steps_per_split = cdiv(nsteps, ksplit);
+  pl.ksplit = cdiv(nsteps, pl.steps_per_split);
+  pl.tiles = tiles;
+  return pl;
+}
+
+size_t q2_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
+  const int mt = m >= 64 ? 4 : cdiv(m, 16);
+  return pl.ksplit > 1
+             ? (size_t)pl.tiles * cdiv(m, 64) * nmat * pl.ksplit * q2_ctw(m, n) * 16 * mt * 16
+             : 0;
+}
+
 hipError_t launch_dequant_q2_bf16(const Q2MatRef &w, int n, int k, int gshift, void *out,
                                   hipStream_t stream) {
   const int64_t total = (int64_t)n * (k >> 4);
@@ -332,9 +364,11 @@ hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat, c
   p.steps_per_split = pl.steps_per_split;
   const int mt = m >= 64 ? 4 : cdiv(m, 16);
   dim3 grid(pl.tiles, pl.ksplit, cdiv(m, 64));
-  if (stream_ctw(n) == 2)
-    return nmat == 1 ? launch_mt<1, 2>(p, mt, grid, stream) : launch_mt<2, 2>(p, mt, grid, stream);
-  return nmat == 1 ? launch_mt<1, 1>(p, mt, grid, stream) : launch_mt<2, 1>(p, mt, grid, stream);
+  switch (q2_ctw(m, n)) {
+    case 4: return nmat == 1 ? launch_mt<1, 4>(p, mt, grid, stream) : launch_mt<2, 4>(p, mt, grid, stream);
+    case 2: return nmat == 1 ? launch_mt<1, 2>(p, mt, grid, stream) : launch_mt<2, 2>(p, mt, grid, stream);
+    default: return nmat == 1 ? launch_mt<1, 1>(p, mt, grid, stream) : launch_mt<2, 1>(p, mt, grid, stream);
+  }
 }
 
 }  // namespace nvfp4

@@ -153,8 +153,10 @@ struct Q2MatRef {
   const uint16_t *scales;  // fp16 [n][k >> gshift]
 };
 // Projection (nmat 1) or gate+up+silu (nmat 2) with W = bf16((q - 2) * d);
-// plan, partial and counter rules as launch_stream.  group = 1 << gshift,
-// 32 <= group, k % group == 0.
+// plan q2_plan(m, n, k), partials q2_partial_floats, counters as
+// stream_counter_words.  group = 1 << gshift, 32 <= group, k % group == 0.
+StreamPlan q2_plan(int m, int n, int k);
+size_t q2_partial_floats(const StreamPlan &pl, int nmat, int m, int n);
 hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat,
                      const Q2MatRef *w, void *y, float *partial,
                      unsigned *counters, const StreamPlan &pl,
