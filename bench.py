@@ -199,29 +199,41 @@ def _traffic_per_launch():
         return None
 
 
-def traffic_run(steps):
+def traffic_run(steps, what="gemv"):
     """Launch pattern for the rocprofv3 FETCH_SIZE / WRITE_SIZE passes: `steps`
-    launches of the dominant kernel over rotating cold replicas, then `steps`
-    plain device copies of COPY_BYTES, whose counter readings calibrate the
-    counters against a transfer of known size."""
+    launches of the dominant kernel over rotating cold replicas (what="gemv"),
+    or `steps` whole decode FFNs in the W8A8 ("w8a8", m=1, hidden 4096, inter
+    14336) or packed-Q2 ("q2", m=1, hidden 4096, inter 12288) formats, then
+    `steps` plain device copies of COPY_BYTES, whose counter readings
+    calibrate the counters against a transfer of known size."""
     import torch
 
     import nvfp4_weight_dense_amd as nv
 
-    _, ctx = measure_ffn("decode", 1, 1)
+    if what == "gemv":
+        _, ctx = measure_ffn("decode", 1, 1)
+    else:
+        _, ctx = measure_ffn("w8a8" if what == "w8a8" else "decode", 1, 1, m=1,
+                             w8a8=what == "w8a8", q2=what == "q2")
     xd, reps, stream = ctx["x"], ctx["weights"], ctx["stream"]
     act = torch.empty((xd.shape[0], reps[0][0].codes.shape[0]), dtype=torch.bfloat16,
                       device=xd.device)
+    out = ctx["out"]
     for i in range(steps):
         r = reps[i % len(reps)]
-        nv.nvfp4_gate_up_silu_w4a16(xd, r[0], r[1], act=act, stream=stream)
+        if what == "gemv":
+            nv.nvfp4_gate_up_silu_w4a16(xd, r[0], r[1], act=act, stream=stream)
+        elif what == "w8a8":
+            nv.dense_ffn_forward_w8a8(xd, *r, out=out, stream=stream)
+        else:
+            nv.dense_ffn_forward_q2(xd, *r, out=out, stream=stream)
     torch.cuda.synchronize()
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=xd.device)
     dst = torch.empty_like(src)
     for _ in range(steps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_run": DOMINANT_KERNEL, "launches": steps,
+    print(json.dumps({"traffic_run": DOMINANT_KERNEL if what == "gemv" else what, "launches": steps,
                       "copy_bytes": COPY_BYTES, "source_hash": _kernel_source_hash()}),
           flush=True)
 
@@ -266,9 +278,10 @@ def main():
     ap.add_argument("--only-headline", action="store_true",
                     help="time only the decode workload (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--traffic-run", action="store_true",
-                    help="only launch the dominant kernel and a calibration copy "
-                         "(for rocprofv3 --pmc passes)")
+    ap.add_argument("--traffic-run", nargs="?", const="gemv", default=None,
+                    choices=("gemv", "w8a8", "q2"),
+                    help="only launch the dominant kernel (or a W8A8 / packed-Q2 decode FFN) "
+                         "and a calibration copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -284,7 +297,7 @@ def main():
         sys.exit(2)
     nv.load_library()  # raises if the HIP library is not built
     if args.traffic_run:
-        traffic_run(args.steps)
+        traffic_run(args.steps, args.traffic_run)
         return
 
     head, ctx = measure_ffn("decode", args.steps, args.warmup)
