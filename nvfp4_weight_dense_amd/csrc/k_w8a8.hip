@@ -310,7 +310,7 @@ hipError_t launch_mt(const W8Args &p, int mt, dim3 grid, hipStream_t s) {
 int w8a8_ctw(int n) { return n > 16 ? 2 : 1; }
 
 StreamPlan w8a8_plan(int n, int k) {
-  constexpr int kTarget = 512;  // workgroups before K is split
+  constexpr int kTarget = 256;  // workgroups before K is split (fewer splits: less partial traffic)
   const int tiles = cdiv(n, 16 * w8a8_ctw(n));
   const int nsteps = cdiv(k, 128);
   int ksplit = 1;
