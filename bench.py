@@ -202,8 +202,9 @@ def _traffic_per_launch():
 def traffic_run(steps, what="gemv"):
     """Launch pattern for the rocprofv3 FETCH_SIZE / WRITE_SIZE passes: `steps`
     launches of the dominant kernel over rotating cold replicas (what="gemv"),
-    or `steps` whole decode FFNs in the W8A8 ("w8a8", m=1, hidden 4096, inter
-    14336) or packed-Q2 ("q2", m=1, hidden 4096, inter 12288) formats, then
+    or `steps` whole decode FFNs in the W4A4 or W8A8 ("w4a4", "w8a8": m=1,
+    hidden 4096, inter 14336) or packed-Q2 ("q2", m=1, hidden 4096, inter
+    12288) formats, then
     `steps` plain device copies of COPY_BYTES, whose counter readings
     calibrate the counters against a transfer of known size."""
     import torch
@@ -212,6 +213,8 @@ def traffic_run(steps, what="gemv"):
 
     if what == "gemv":
         _, ctx = measure_ffn("decode", 1, 1)
+    elif what == "w4a4":
+        _, ctx = measure_ffn("w4a4", 1, 1, m=1, w4a4=True)
     else:
         _, ctx = measure_ffn("w8a8" if what == "w8a8" else "decode", 1, 1, m=1,
                              w8a8=what == "w8a8", q2=what == "q2")
@@ -225,6 +228,8 @@ def traffic_run(steps, what="gemv"):
             nv.nvfp4_gate_up_silu_w4a16(xd, r[0], r[1], act=act, stream=stream)
         elif what == "w8a8":
             nv.dense_ffn_forward_w8a8(xd, *r, out=out, stream=stream)
+        elif what == "w4a4":
+            nv.dense_ffn_forward_w4a4(xd, *r, out=out, stream=stream)
         else:
             nv.dense_ffn_forward_q2(xd, *r, out=out, stream=stream)
     torch.cuda.synchronize()
@@ -279,7 +284,7 @@ def main():
                     help="time only the decode workload (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--traffic-run", nargs="?", const="gemv", default=None,
-                    choices=("gemv", "w8a8", "q2"),
+                    choices=("gemv", "w4a4", "w8a8", "q2"),
                     help="only launch the dominant kernel (or a W8A8 / packed-Q2 decode FFN) "
                          "and a calibration copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()
