@@ -45,7 +45,8 @@ def oq(w: si.Q2Weight) -> oracle.Q2Weight:
 
 @pytest.mark.parametrize("m,n,k,group", [(1, 48, 128, 128), (5, 300, 384, 128), (17, 130, 224, 32),
                                          (70, 257, 640, 64), (3, 64, 4096, 128),
-                                         (3, 16400, 256, 128), (64, 1000, 2048, 128)])
+                                         (3, 16400, 256, 128), (64, 1000, 2048, 128),
+                                         (2, 40, 512, 256), (130, 96, 768, 256)])
 def test_q2_gemm_matches_oracle(m, n, k, group):
     _say(f"q2 gemm m={m} n={n} k={k} group={group}")
     x = si.activations(m, k, seed=n, outliers=True)
@@ -99,3 +100,17 @@ def test_dense_ffn_q2_full_workload_matches_oracle(name, nrows):
     rows = _rows(x.shape[0], nrows, seed=5)
     _, ye = oracle.dense_ffn_q2(bits(x)[rows], oq(wg), oq(wu), oq(wd))
     assert_close(bits(y)[rows], ye, f"ffn q2 {name}")
+
+
+def test_q2_m_zero_and_errors_touch_nothing():
+    _say("q2 m=0 / errors")
+    x, wg, wu, wd = si.q2_workload("tiny", m=4)
+    out = torch.full((4, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    nv.dense_ffn_forward_q2(x[:0].cuda(), gq(wg), gq(wu), gq(wd), out=out[:0])
+    with pytest.raises(nv.Nvfp4Error):
+        nv.dense_ffn_forward_q2(x.cuda(), gq(wg), gq(wu), gq(wg), out=out)  # wd has the wrong shape
+    bad = si.Q2Weight(wg.codes, wg.scales[:, :1].contiguous(), 256)  # group 256 on hidden 256: fine shape,
+    with pytest.raises(nv.Nvfp4Error):                              # but gate and up groups differ
+        nv.dense_ffn_forward_q2(x.cuda(), gq(bad), gq(wu), gq(wd), out=out)
+    sync()
+    assert bool((out == 7.0).all())
