@@ -59,6 +59,29 @@ def test_fp8_quantizer_bit_exact(m, k):
     assert np.array_equal(r.cpu().numpy(), ro)
 
 
+def test_fp8_quantizer_every_bf16_quotient():
+    """Every finite bf16 value of magnitude <= 7 (both signs), in rows that
+    each hold 7.0: s_row = 7/448 = 2^-6 exactly, so the quotient is 64 x and
+    every E4M3 rounding decision a bf16 input can reach (ties at every
+    midpoint, the subnormal grid, saturation at 448) is taken on the GPU and
+    compared with the oracle bit for bit."""
+    _say("fp8 quantize every bf16 value")
+    allb = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    v = allb[torch.isfinite(allb) & (allb.abs() <= 7.0)]
+    k = 4096
+    rows = -(-v.numel() // (k - 1))
+    x = torch.zeros(rows * (k - 1), dtype=torch.bfloat16)
+    x[: v.numel()] = v
+    x = torch.cat([x.view(rows, k - 1), torch.full((rows, 1), 7.0, dtype=torch.bfloat16)], dim=1)
+    x = x.contiguous()
+    c, r = nv.fp8_quantize_rows(x.cuda())
+    sync()
+    co, ro = oracle.quantize_rows_fp8(bits(x))
+    assert np.all(ro == np.float32(2.0 ** -6))
+    assert np.array_equal(r.cpu().numpy(), ro)
+    assert np.array_equal(c.cpu().numpy(), co)
+
+
 # (m, n, k): ragged columns and K; n = 64, k = 4096 splits K over 4
 # workgroups; n >= 16384 takes two column tiles per workgroup, 16400 with a
 # last 16-column tile and a partial scale block along N and K

@@ -102,6 +102,22 @@ def test_fp8_quantizer_matches_torch_cast_of_the_quotient():
     assert np.array_equal(codes, lib)
 
 
+def test_fp8_quantizer_every_bf16_value_matches_torch_cast():
+    """Every finite bf16 value with |x| <= 7 in one row holding 7.0: s_row is
+    2^-6, the quotient 64 x is exact, and the codes must equal torch's own
+    float8_e4m3fn cast of it (every midpoint tie, the subnormal grid, 448)."""
+    allb = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    v = allb[torch.isfinite(allb) & (allb.abs() <= 7.0)]
+    x = torch.cat([v, torch.tensor([7.0], dtype=torch.bfloat16)]).reshape(1, -1)
+    pad = (-x.shape[1]) % 32
+    x = torch.cat([x, torch.zeros((1, pad), dtype=torch.bfloat16)], dim=1)
+    codes, rs = oracle.quantize_rows_fp8(_bits(x))
+    assert rs[0] == np.float32(2.0 ** -6)
+    q = x.float() * 64.0
+    lib = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, lib)
+
+
 def test_fp8_quantizer_codes_are_nearest_grid_values():
     xb = _random_rows(6, 256, seed=4)
     codes, rs = oracle.quantize_rows_fp8(xb)
