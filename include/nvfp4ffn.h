@@ -38,7 +38,10 @@
  * Scratch: intermediates and split-K partials live in a per-device arena
  *   owned by the library (grown on first use of a larger shape, freed by
  *   nvfp4_release).  Calls that may run concurrently on different streams
- *   of one device race on it; calls on one stream are ordered.
+ *   of one device race on it; calls on one stream are ordered.  The
+ *   packed-Q2 calls above 64 rows also use one rocBLAS handle per device
+ *   (created on first use, destroyed by nvfp4_release), which may allocate
+ *   its own workspace.
  */
 #ifndef NVFP4FFN_H
 #define NVFP4FFN_H

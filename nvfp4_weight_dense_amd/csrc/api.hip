@@ -12,8 +12,12 @@
 //   W4A4:  quantize x -> gate+up(+silu) -> act -> quantize act -> down.  One
 //          kernel and one K order for every m, so row bits do not depend on m.
 //   W8A8:  the same sequence with per-row FP8 activations and block-scaled
-//          FP8 weights on the FP8 matrix cores (page layers/dense_ffn_fixed.rs,
-//          `Fixed::W8a8`).
+//          FP8 weights, exact fp16 products on the matrix cores (page
+//          layers/dense_ffn_fixed.rs, `Fixed::W8a8`).
+//   Q2:    packed-Q2 weights, bf16 activations (page layers/dense_ffn_prefill.rs,
+//          `prefill_q2`): up to NVFP4_SMALLM_MAX_M rows the weight-streaming
+//          kernel (gate+up+silu fused, then down); more rows dequantize each
+//          weight to bf16 and run a rocBLAS bf16 GEMM, silu_mul over gate.
 // Every check runs before the first launch; a forced path that cannot serve a
 // shape is an error, never a silent fallback (the pages refuse to start with
 // a requested but missing variant: page layers/mod.rs, `w4a16_v2_kernel`).
