@@ -94,13 +94,14 @@ def test_w4a4_activation_codes_match_oracle_on_gpu_activations():
     assert np.array_equal(r.cpu().numpy(), ro)
 
 
-@pytest.mark.parametrize("m", [1, 40, 200])
-def test_dense_ffn_fused_gate_up_weight(m):
+@pytest.mark.parametrize("name,m", [("tiny", 1), ("tiny", 40), ("tiny", 200), ("decode", 1)])
+def test_dense_ffn_fused_gate_up_weight(name, m):
     """A [2*inter, hidden] buffer holding gate then up gives the same bits
-    as the separate weights (GEMV, small-m and many-row paths), and the
-    oracle's result within tolerance."""
-    _say(f"ffn fused gate+up weight m={m}")
-    x, wg, wu, wd = si.workload("tiny", m=m)
+    as the separate weights (GEMV, small-m and many-row paths; the full
+    decode workload as the benchmark runs it), and the oracle's result
+    within tolerance."""
+    _say(f"ffn fused gate+up weight {name} m={m}")
+    x, wg, wu, wd = si.workload(name, m=m)
     assert wg.ts == wu.ts
     wgu = nv.NVFP4Weight(torch.cat([wg.codes, wu.codes]).cuda(),
                          torch.cat([wg.scales, wu.scales]).cuda(), wg.ts)
@@ -113,4 +114,4 @@ def test_dense_ffn_fused_gate_up_weight(m):
     sync()
     assert torch.equal(y_fused.view(torch.int16), y_sep.view(torch.int16))
     _, ye = oracle.dense_ffn(bits(x), o_weight(wg), o_weight(wu), o_weight(wd))
-    assert_close(bits(y_fused), ye, f"ffn fused m={m}")
+    assert_close(bits(y_fused), ye, f"ffn fused {name} m={m}")
