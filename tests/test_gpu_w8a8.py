@@ -97,6 +97,29 @@ def test_fp8_gemm_w8a8_matches_oracle(m, n, k):
     assert_close_elem(bits(y), ye, f"gemm w8a8 m={m} n={n} k={k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(3, 14336, 4096), (65, 4096, 14336)])
+def test_fp8_gemm_w8a8_exact_case_bit_exact(m, n, k):
+    """Exact case at full projection shapes: every row holds 7 (amax), the
+    rest integers in [-2, 2], so s_row = 2^-6 and every code is exact; the
+    weights are E4M3 integers in [-2, 2] with block scales 1, 2 or 4.  Every
+    product and every fp32 partial sum is then an integer below 2^24, so any
+    summation order gives the oracle's value and the bf16 results must match
+    bit for bit (a wrong block-scale index or K order cannot hide here)."""
+    _say(f"fp8 gemm exact m={m} n={n} k={k}")
+    g = torch.Generator().manual_seed(n + k)
+    x = torch.randint(-2, 3, (m, k), generator=g).to(torch.float32)
+    x[:, 0] = 7.0
+    x = x.to(torch.bfloat16)
+    vals = torch.tensor([0xC0, 0xB8, 0x00, 0x38, 0x40], dtype=torch.uint8)  # -2 -1 0 1 2
+    codes = vals[torch.randint(0, 5, (n, k), generator=g)].contiguous()
+    e = torch.randint(0, 3, ((n + 127) // 128, (k + 127) // 128), generator=g).to(torch.float32)
+    w = si.Fp8Weight(codes, torch.exp2(e).contiguous())
+    y = nv.fp8_gemm_w8a8(x.cuda(), g8(w))
+    sync()
+    yo, _ = oracle.gemm_w8a8(bits(x), o8(w))
+    assert np.array_equal(bits(y), yo)
+
+
 @pytest.mark.parametrize("m", [1, 4, 17, 65, 130])
 def test_dense_ffn_w8a8_tiny_matches_oracle(m):
     _say(f"ffn w8a8 tiny m={m}")
