@@ -702,9 +702,15 @@ int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden, int32_t int
   ProfileScope ps("dense_total lora", m, s);
   MatRef mg = mat(wg), mu = mat(wu), md = mat(wd);
   const ActRef ax{x, nullptr, nullptr, nullptr};
-  if ((rc = run_proj(ax, m, hidden, inter, 1, &mg, g, scr, p_up, s)) ||
-      (rc = run_proj(ax, m, hidden, inter, 1, &mu, u, scr, p_up, s)))
+  if (p_up == Path::Gemv) {
+    // one launch streams both weights and writes gate and up apart
+    const MatRef w2[2] = {mg, mu};
+    if ((rc = hip_status(launch_gemv(x, m, hidden, inter, 2, w2, g, s, u), "gemv projection launch")))
+      return rc;
+  } else if ((rc = run_proj(ax, m, hidden, inter, 1, &mg, g, scr, p_up, s)) ||
+             (rc = run_proj(ax, m, hidden, inter, 1, &mu, u, scr, p_up, s))) {
     return rc;
+  }
   auto ref = [](const nvfp4_lora_pair &l) {
     return lora_on(l) ? LoraRef{l.a, l.b, l.rank, l.scale} : LoraRef{nullptr, nullptr, 0, 0.f};
   };

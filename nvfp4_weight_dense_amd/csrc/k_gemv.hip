@@ -43,6 +43,7 @@ struct GemvArgs {
   const uint8_t *codes1, *scales1;
   float ts0, ts1;
   void *y;                // bf16 [m][n]
+  void *y2;               // NMAT = 2 only: non-null -> gate into y, up into y2, no silu
   int nbatch;
 };
 
@@ -224,8 +225,15 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
       } else {
         const float up = xor_shfl<8>(tot[r]);  // entry 2c+1 (up) next to 2c (gate)
         const int c = lane >> 4;
-        if ((lane & 15) == 0 && c < ncols)
-          ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = swiglu_bf16(tot[r] * p.ts0, up * p.ts1);
+        if ((lane & 15) == 0 && c < ncols) {
+          const size_t o = (size_t)r * p.n + c0 + c;
+          if (p.y2) {  // gate and up kept apart (an overlay adds to each before silu)
+            ((__bf16 *)p.y)[o] = (__bf16)(tot[r] * p.ts0);
+            ((__bf16 *)p.y2)[o] = (__bf16)(up * p.ts1);
+          } else {
+            ((__bf16 *)p.y)[o] = swiglu_bf16(tot[r] * p.ts0, up * p.ts1);
+          }
+        }
       }
     }
   };
@@ -312,7 +320,7 @@ bool gemv_eligible(int m, int k) {
 }
 
 hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat, const MatRef *w, void *y,
-                       hipStream_t stream) {
+                       hipStream_t stream, void *y2) {
   GemvArgs p{};
   p.x = x;
   p.m = m;
@@ -325,6 +333,7 @@ hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat, const MatRe
   p.scales1 = nmat > 1 ? w[1].scales : nullptr;
   p.ts1 = nmat > 1 ? w[1].ts : 0.f;
   p.y = y;
+  p.y2 = nmat > 1 ? y2 : nullptr;
   p.nbatch = cdiv(n, kCB / nmat);
   const GemvShape s = gemv_shape(m, k);
   return nmat == 1 ? launch_n<1>(p, s, stream) : launch_n<2>(p, s, stream);

@@ -102,7 +102,8 @@ hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat,
                           const MatRef *w, void *y, const PrefillPlan &pl,
                           hipStream_t stream);
 
-// Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above.
+// Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above;
+// with nmat 2 and y2 set, gate goes to y and up to y2 (no silu).
 // Eligible when K splits into at most 4 waves of register-resident granules.
 // LoRA delta: base[m][n] (bf16, in place) += scale * (x . A^T) . B^T with
 // A bf16 [r][k], B bf16 [n][r]; xa is fp32 scratch of lora_xa_floats(m, k,
@@ -123,7 +124,8 @@ hipError_t launch_lora_gate_up_silu(const void *x, int m, int k, const LoraRef &
 
 bool gemv_eligible(int m, int k);
 hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat,
-                       const MatRef *w, void *y, hipStream_t stream);
+                       const MatRef *w, void *y, hipStream_t stream,
+                       void *y2 = nullptr);
 
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out,
                            int64_t count, hipStream_t stream);
