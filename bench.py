@@ -323,6 +323,8 @@ def main():
                 ("decode", args.steps, False, None, False, 16),
                 ("smallm", max(20, args.steps // 2), False, None, False, 0),
                 ("prefill", max(5, args.steps // 20), False, None, False, 0),
+                ("decode_tp8", args.steps, False, None, False, 0),
+                ("prefill_tp8", max(5, args.steps // 20), False, None, False, 0),
                 ("w4a4", max(20, args.steps // 2), True, 1, False, 0),
                 ("w4a4", max(20, args.steps // 2), True, 8, False, 0),
                 ("w4a4", max(20, args.steps // 2), True, 64, False, 0),

@@ -14,6 +14,8 @@ stand in for them):
 * ``prefill``  m=2048, hidden=5120, inter=17408, 1% of X entries x20
 * ``w4a4``     hidden=4096, inter=14336, m in {1, 8, 64, 512} sharing rows
 * ``w8a8``     the same shapes and rows, with block-scaled FP8 weights
+* ``decode_tp8``, ``prefill_tp8``  one GPU's share of the decode / prefill
+  FFN under 8-way tensor parallelism (inter 1536 / 2176)
 
 Weight recipe: E2M1 codes uniform over all 16 nibbles (so -0 appears),
 E4M3 block scales 2^u with u ~ U(-4, 0) cast to float8_e4m3fn by torch,
@@ -41,6 +43,10 @@ WORKLOADS = {
     "prefill": dict(m=2048, hidden=5120, inter=17408, outliers=True),
     "w4a4": dict(m=512, hidden=4096, inter=14336, outliers=False),
     "w8a8": dict(m=512, hidden=4096, inter=14336, outliers=False),
+    # one GPU's share under 8-way tensor parallelism (inter split 8 ways):
+    # the decode and prefill shapes as each shard runs them
+    "decode_tp8": dict(m=1, hidden=4096, inter=12288 // 8, outliers=False),
+    "prefill_tp8": dict(m=2048, hidden=5120, inter=17408 // 8, outliers=True),
 }
 
 W4A4_ROW_COUNTS = (1, 8, 64, 512)

@@ -31,7 +31,8 @@ def _rows(m, count, seed):
     return np.array(sorted(picked))
 
 
-@pytest.mark.parametrize("name,nrows", [("tiny", 4), ("decode", 1), ("smallm", 6), ("prefill", 6)])
+@pytest.mark.parametrize("name,nrows", [("tiny", 4), ("decode", 1), ("smallm", 6), ("prefill", 6),
+                                        ("decode_tp8", 1), ("prefill_tp8", 6)])
 def test_dense_ffn_w4a16_matches_oracle(name, nrows):
     _say(f"ffn w4a16 {name}")
     x, wg, wu, wd = si.workload(name)
