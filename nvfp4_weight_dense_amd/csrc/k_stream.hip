@@ -9,10 +9,13 @@
 //     NMAT weight matrices: 1, or 2 for gate+up with a fused silu epilogue)
 //     and a range of K; its 4 waves split that range into interleaved
 //     128-element steps.
-//   * In one step, lane (c = lane%16, g = lane/16) loads 16 bytes of codes
+//   * In one step, lane (c = lane%16, g = lane/16) needs 16 bytes of codes
 //     (32 K elements of weight row col0+c at K offset 32g) and their 2 scale
-//     bytes with one 128-bit and one 16-bit buffer load; per column tile a
-//     wave's load covers 16 rows x 64 contiguous bytes.  Buffer loads return
+//     bytes; per column tile a wave covers 16 rows x 64 contiguous bytes.
+//     The loads (one 128-bit, one 16-bit) are issued in the row-contiguous
+//     layout -- lane s reads row s/4, piece s%4, so four neighbouring lanes
+//     read one 64-byte run -- and ds_bpermute moves each piece to lane
+//     (c, g); the bytes a lane ends with are the same.  Buffer loads return
 //     zero outside the resource's range, so ragged columns, rows and K need
 //     no branches.  The codes are dequantized in registers to four B
 //     fragments of v_mfma_f32_16x16x32_bf16 (bf16 activations), or of
@@ -76,6 +79,8 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int g = lane >> 4;
+  const int src_addr = load_layout_src_addr(lane);
+  const uint32_t lrow = (uint32_t)(lane >> 2), lpiece = (uint32_t)(lane & 3);  // load layout
   const int k = p.k;
   const int col0 = blockIdx.x * (16 * CTW);
   const int row0 = blockIdx.z * 64;
@@ -121,13 +126,15 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
       const int t = base + u * kNW;
       const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
       const bool ok = t < s_end && kk < (uint32_t)k;
+      const uint32_t kl = (uint32_t)t * 128u + 32u * lpiece;  // K of this lane's weight load
+      const bool okl = t < s_end && kl < (uint32_t)k;
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-          const uint32_t row = (uint32_t)(ct * 16 + c16);
-          bw[u][i][ct] = ld16(wc[i], ok ? row * kb2 + (kk >> 1) : kOOB);
-          bsc[u][i][ct] = ld2(ws[i], ok ? row * kb16 + (kk >> 4) : kOOB);
+          const uint32_t row = (uint32_t)(ct * 16) + lrow;
+          bw[u][i][ct] = ld16(wc[i], okl ? row * kb2 + (kl >> 1) : kOOB);
+          bsc[u][i][ct] = ld2(ws[i], okl ? row * kb16 + (kl >> 4) : kOOB);
         }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -150,9 +157,10 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-          const uint4 w = bw[u][i][ct];
-          const float s0 = e4m3_to_f32_sel<0>(bsc[u][i][ct]);
-          const float s1 = e4m3_to_f32_sel<1>(bsc[u][i][ct]);
+          const uint4 w = from_load_layout(bw[u][i][ct], src_addr);
+          const uint32_t sc = from_load_layout(bsc[u][i][ct], src_addr);
+          const float s0 = e4m3_to_f32_sel<0>(sc);
+          const float s1 = e4m3_to_f32_sel<1>(sc);
           if constexpr (AFP4) {
             const f16x2 m0 = scale_mantissa_f16x2(s0), m1 = scale_mantissa_f16x2(s1);
             bf[i][ct][0] = dequant8_f16(w.x, s0, m0);

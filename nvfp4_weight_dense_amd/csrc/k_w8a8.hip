@@ -17,9 +17,17 @@
 //     to 64 rows, and a range of K; its 4 waves take interleaved 128-element
 //     steps.  A step is one weight block along K, and the 16 columns of a
 //     tile lie in one block along N, so a step needs one scale per tile.
-//   * Lane (c = lane%16, g = lane/16) loads 32 bytes of weight row c at K
-//     offset 32g of the step (two 128-bit buffer loads), and the same 32
-//     bytes of each activation row.  The hardware FP8 -> fp16 conversion
+//   * Lane (c = lane%16, g = lane/16) holds 32 bytes of weight row c: the
+//     16 at K offset 16g of the step and the 16 at 64 + 16g; and the same
+//     bytes of each activation row.  Loading the weight bytes that way
+//     would give four neighbouring lanes four different rows, and the
+//     texture addresser, not HBM, then sets the streaming rate (measured:
+//     the m=1 FFN 53.6 us with such loads, 49.5 us with these).  So lane s
+//     loads 16 bytes at 16(s%4) (and 64 + 16(s%4)) of row s/4 -- four
+//     lanes cover 64 contiguous bytes -- and a ds_bpermute hands lane
+//     (c, g) the registers of lane 4c + g.  Activations are few rows, read
+//     from cache, and are loaded in place.
+//     The hardware FP8 -> fp16 conversion
 //     (exact: an E4M3 value has 4 significant bits and lies in
 //     [2^-9, 448]) turns them into four operand fragments of
 //     v_mfma_f32_16x16x32_f16, whose products are exact and whose sums are
@@ -77,7 +85,10 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// the four fragments of 32 bytes: fragment j covers bytes 8j..8j+7
+// the four fragments of a lane's 32 bytes (q0 = K offsets 16g.., q1 =
+// 64 + 16g..): fragment j covers bytes 8j..8j+7 of q0 then q1, so MFMA j of
+// a step sums the 32 K offsets 16g' + 8j (j < 2) or 64 + 16g' + 8(j-2)
+// (j >= 2), plus 0..7, over g' = 0..3
 __device__ __forceinline__ void fp8x32_to_f16(const uint4 &q0, const uint4 &q1, f16x8 (&f)[4]) {
   f[0] = fp8x8_to_f16(q0.x, q0.y);
   f[1] = fp8x8_to_f16(q0.z, q0.w);
@@ -92,6 +103,8 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int g = lane >> 4;
+  const int src_addr = load_layout_src_addr(lane);
+  const uint32_t wrow = (uint32_t)(lane >> 2);    // weight row this lane loads
   const int k = p.k;
   const int col0 = blockIdx.x * (16 * CTW);
   const int row0 = blockIdx.z * 64;
@@ -128,19 +141,24 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + u * kNW;
-      const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
-      const bool ok = t < s_end && kk < (uint32_t)k;
+      // K offsets of the 16-byte loads: weights (load layout), activations
+      // (operand layout); each is checked on its own (k is only a multiple
+      // of 32, so the second 64 bytes of the last step can lie past k)
+      const bool in_split = t < s_end;
+      const uint32_t kw = (uint32_t)t * 128u + 16u * (uint32_t)(lane & 3);
+      const uint32_t ka = (uint32_t)t * 128u + 16u * (uint32_t)g;
+      const bool okw0 = in_split && kw < (uint32_t)k, okw1 = in_split && kw + 64u < (uint32_t)k;
+      const bool oka0 = in_split && ka < (uint32_t)k, oka1 = in_split && ka + 64u < (uint32_t)k;
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-          const uint32_t off = ok ? (uint32_t)(ct * 16 + c16) * (uint32_t)k + kk : kOOB;
-          // cached loads: the two halves of a lane's 32 bytes share 128-byte
-          // lines with the other lanes' chunks, and the non-temporal hint let
-          // lines go before their second half was read (FETCH_SIZE of the
-          // m=1 gate+up launch 1.35x -> 1.11x its algorithmic bytes)
-          bw[u][i][ct][0] = ld16(wc[i], off);
-          bw[u][i][ct][1] = ld16(wc[i], off + 16u);
+          const uint32_t roff = (uint32_t)(ct * 16) + wrow;
+          // cached loads: the non-temporal hint let lines go before every
+          // lane of a line had read it (FETCH_SIZE of the m=1 gate+up launch
+          // 1.35x its algorithmic bytes with the hint, 1.11x without)
+          bw[u][i][ct][0] = ld16(wc[i], okw0 ? roff * (uint32_t)k + kw : kOOB);
+          bw[u][i][ct][1] = ld16(wc[i], okw1 ? roff * (uint32_t)k + kw + 64u : kOOB);
           // the tile's 16 columns share one scale row (col0 + 16 ct is a
           // multiple of 16, blocks are 128 wide); steps past the end read
           // block 0 and multiply zeros
@@ -150,9 +168,9 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
         }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t off = ok ? (uint32_t)(mt * 16 + c16) * (uint32_t)k + kk : kOOB;
-        aw[u][mt][0] = ld16(ax, off);
-        aw[u][mt][1] = ld16(ax, off + 16u);
+        const uint32_t roff = (uint32_t)(mt * 16 + c16) * (uint32_t)k;
+        aw[u][mt][0] = ld16(ax, oka0 ? roff + ka : kOOB);
+        aw[u][mt][1] = ld16(ax, oka1 ? roff + ka + 64u : kOOB);
       }
     }
 #pragma unroll
@@ -161,7 +179,9 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) fp8x32_to_f16(bw[u][i][ct][0], bw[u][i][ct][1], bf[i][ct]);
+        for (int ct = 0; ct < CTW; ++ct)
+          fp8x32_to_f16(from_load_layout(bw[u][i][ct][0], src_addr), from_load_layout(bw[u][i][ct][1], src_addr),
+                        bf[i][ct]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f16x8 af[4];

@@ -158,6 +158,24 @@ __device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
 
+// ---- row-contiguous weight loads ------------------------------------------------
+// In the 16x16 MFMA operand layout lane (c, g) = (lane%16, lane/16) holds
+// row c, so four neighbouring lanes read four different rows, and a
+// streaming kernel is then held by the texture addresser rather than by
+// HBM.  The load layout instead gives lane s row s/4 and piece s%4 of it
+// (four neighbours read one contiguous run); one ds_bpermute per dword then
+// hands lane (c, g) the registers of lane 4c + g, i.e. row c, piece g.
+__device__ __forceinline__ int load_layout_src_addr(int lane) {
+  return (((lane & 15) << 2) | (lane >> 4)) << 2;  // byte address of lane 4c + g
+}
+__device__ __forceinline__ uint32_t from_load_layout(uint32_t v, int src_addr) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v);
+}
+__device__ __forceinline__ uint4 from_load_layout(const uint4 &v, int src_addr) {
+  return uint4{from_load_layout(v.x, src_addr), from_load_layout(v.y, src_addr),
+               from_load_layout(v.z, src_addr), from_load_layout(v.w, src_addr)};
+}
+
 // A 16-bit store through a buffer resource: offsets beyond its range are
 // dropped, so rows past the end need no branch.
 __device__ __forceinline__ void st2(__amdgpu_buffer_rsrc_t r, uint32_t off, __bf16 v) {
