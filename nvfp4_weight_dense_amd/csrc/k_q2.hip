@@ -15,9 +15,14 @@
 // kernels): a workgroup owns CTW tiles of 16 columns of NMAT matrices (2:
 // gate and up with the silu epilogue), up to 64 rows and a range of K; its 4
 // waves take interleaved 128-element steps.  Lane (c = lane%16, g = lane/16)
-// loads the 8 code bytes of column c for K offsets 32g..32g+31 of the step
-// (one 64-bit load; a wave's load covers 16 rows x 32 contiguous bytes) and
-// that chunk's scale (a chunk lies in one group), dequantizes them into the
+// takes the 8 code bytes of column c for K offsets 32g..32g+31 of the step
+// (a wave covers 16 rows x 32 contiguous bytes) and that chunk's scale (a
+// chunk lies in one group); for up to 16 rows both are loaded in the
+// row-contiguous layout (lane s reads row s/4, chunk s%4) and moved to lane
+// (c, g) with ds_bpermute, the same bytes as a direct load (measured FFN:
+// m=8 48.7 -> 43.1 us; with more rows the activation loads dominate and the
+// permute costs more than it saves: m=64 178 -> 196 us, so those load
+// directly); it dequantizes them into the
 // four B fragments of v_mfma_f32_16x16x32_bf16, and loads the same 32 K of
 // each activation row (64 bytes).  K order inside a step is (g, element) on
 // both operands.  Waves reduce through LDS in wave order; with ksplit > 1
@@ -77,6 +82,10 @@ __global__ __launch_bounds__(kNW * 64) void k_q2(Q2Args p) {
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int g = lane >> 4;
+  const int src_addr = load_layout_src_addr(lane);
+  constexpr bool kRowLoads = MT == 1;
+  const uint32_t lrow = kRowLoads ? (uint32_t)(lane >> 2) : (uint32_t)c16;  // weight row loaded
+  const uint32_t lpiece = kRowLoads ? (uint32_t)(lane & 3) : (uint32_t)g;   // 32-K chunk loaded
   const int k = p.k;
   const int col0 = blockIdx.x * (16 * CTW);
   const int row0 = blockIdx.z * 64;
@@ -115,13 +124,15 @@ __global__ __launch_bounds__(kNW * 64) void k_q2(Q2Args p) {
       const int t = base + u * kNW;
       const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
       const bool ok = t < s_end && kk < (uint32_t)k;
+      const uint32_t kl = (uint32_t)t * 128u + 32u * lpiece;  // K of this lane's weight load
+      const bool okl = t < s_end && kl < (uint32_t)k;
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-          const uint32_t row = (uint32_t)(ct * 16 + c16);
-          bw[u][i][ct] = ld8_nt(wc[i], ok ? row * kb4 + (kk >> 2) : kOOB);
-          bsc[u][i][ct] = ld2_nt(ws[i], ok ? (row * ngroups + (kk >> p.gshift)) * 2u : kOOB);
+          const uint32_t row = (uint32_t)(ct * 16) + lrow;
+          bw[u][i][ct] = ld8_nt(wc[i], okl ? row * kb4 + (kl >> 2) : kOOB);
+          bsc[u][i][ct] = ld2_nt(ws[i], okl ? (row * ngroups + (kl >> p.gshift)) * 2u : kOOB);
         }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -137,9 +148,14 @@ __global__ __launch_bounds__(kNW * 64) void k_q2(Q2Args p) {
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-          const float d = fp16_bits_to_f32(bsc[u][i][ct]);
+          uint32_t sc = bsc[u][i][ct];
+          uint2 w = bw[u][i][ct];
+          if constexpr (kRowLoads) {
+            sc = from_load_layout(sc, src_addr);
+            w = uint2{from_load_layout(w.x, src_addr), from_load_layout(w.y, src_addr)};
+          }
+          const float d = fp16_bits_to_f32(sc);
           const float m2d = -2.0f * d;
-          const uint2 w = bw[u][i][ct];
           bf[i][ct][0] = dequant_q2x8(w.x & 0xFFFFu, d, m2d);
           bf[i][ct][1] = dequant_q2x8(w.x >> 16, d, m2d);
           bf[i][ct][2] = dequant_q2x8(w.y & 0xFFFFu, d, m2d);
