@@ -7,7 +7,7 @@
 //   W4A16: gate+up(+silu) -> act, then down -> out.  Up to NVFP4_SMALLM_MAX_M
 //          rows (default 64, the pages' small-m edge) take the weight-streaming
 //          kernel with gate, up and silu_mul fused; more rows take the
-//          many-row kernel (also gate+up+silu fused) when k % 256 == 0, else
+//          many-row kernel (also gate+up+silu fused) when k % 64 == 0, else
 //          the LDS-shared streaming kernel with 256-row blocks.
 //   W4A4:  quantize x -> gate+up(+silu) -> act -> quantize act -> down.  One
 //          kernel and one K order for every m, so row bits do not depend on m.
@@ -211,11 +211,11 @@ bool choose_path(int m, int k, Path *out) {
       *out = Path::Gemv;
       return gemv_eligible(m, k);
     case Force::Stream: *out = stream_kind(m, k); return true;
-    case Force::Prefill: *out = Path::Prefill; return k % 256 == 0;
+    case Force::Prefill: *out = Path::Prefill; return k % 64 == 0;
     default:
       if (gemv_eligible(m, k)) *out = Path::Gemv;
       else if (m <= cfg().smallm_max_m) *out = stream_kind(m, k);
-      else *out = k % 256 == 0 ? Path::Prefill : Path::StreamLds;
+      else *out = k % 64 == 0 ? Path::Prefill : Path::StreamLds;
       return true;
   }
 }
@@ -223,7 +223,7 @@ bool choose_path(int m, int k, Path *out) {
 int path_or_fail(int m, int k, Path *out) {
   if (!choose_path(m, k, out))
     return fail(NVFP4_ESHAPE, "NVFP4_FORCE_PATH=%s cannot serve m=%d k=%d (gemv needs m<=4 and a K "
-                "that fits four waves of register-resident activations; prefill needs k %% 256 == 0)",
+                "that fits four waves of register-resident activations; prefill needs k %% 64 == 0)",
                 cfg().force == Force::Gemv ? "gemv" : "prefill", m, k);
   return NVFP4_OK;
 }

@@ -47,7 +47,13 @@
 // shape tried: the split parts lose the L2 sharing and the hand-off reads
 // wait on memory latency.)
 //
-// Requires k % 256 == 0 (16-byte aligned scale groups).
+// Requires k % 64 == 0 (whole steps).  When k % 256 != 0 the last weight
+// group is partial: the steps it lacks are never run, so the code bytes its
+// requests bring from beyond each row's end are never read, and its scales
+// come a dword (one step) at a time -- for every group, since the scale
+// rows are then only 4-byte aligned -- so that no scale load reaches past
+// the last row's end, where a 16-byte load would straddle the resource
+// bound.
 #include <algorithm>
 #include <cstdint>
 #include <initializer_list>
@@ -184,9 +190,19 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
   uint4 sc[2][kNB];
   auto load_scales = [&](int G, uint4 (&sv)[kNB]) {
     const uint32_t goff = (uint32_t)(s_begin + kGroup * G) * 4u;
-    const bool ok = kGroup * G < len;
+    const int nst = len - kGroup * G;  // steps of this group that run (uniform)
+    if (nst >= kGroup && (kb16 & 15u) == 0) {
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) sv[i] = ld16(ws[i], ok ? (uint32_t)c32 * kb16 + goff : kOOB);
+      for (int i = 0; i < kNB; ++i) sv[i] = ld16(ws[i], (uint32_t)c32 * kb16 + goff);
+    } else {
+      // k % 256 != 0 (scale rows only 4-byte aligned; the last group
+      // partial) or past the end: one dword per step that runs
+      const uint32_t o = (uint32_t)c32 * kb16 + goff;
+#pragma unroll
+      for (int i = 0; i < kNB; ++i)
+        sv[i] = uint4{ld4(ws[i], nst > 0 ? o : kOOB), ld4(ws[i], nst > 1 ? o + 4u : kOOB),
+                      ld4(ws[i], nst > 2 ? o + 8u : kOOB), ld4(ws[i], nst > 3 ? o + 12u : kOOB)};
+    }
   };
   auto dequant_j = [&](const uint4 (&w)[kNB], const uint32_t (&s)[kNB], int j, bf16x8 (&out)[kNB]) {
 #pragma unroll

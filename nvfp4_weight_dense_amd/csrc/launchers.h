@@ -82,7 +82,7 @@ hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat,
                          unsigned *counters, const SmallPlan &pl,
                          hipStream_t stream);
 
-// Many-row projection (bf16 activations, k % 256 == 0): tiles of 32*mt rows
+// Many-row projection (bf16 activations, k % 64 == 0): tiles of 32*mt rows
 // (mt in {8, 6, 5, 4, 2}, chosen per shape) x 128 (nmat 2, gate+up+silu
 // fused) or 256 (nmat 1) columns over the whole K, walked by one persistent
 // workgroup per CU.  Columns [0, n_bulk) take one launch; when n_bulk < n

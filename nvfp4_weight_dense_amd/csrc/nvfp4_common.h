@@ -154,6 +154,9 @@ __device__ __forceinline__ uint32_t ld2_nt(__amdgpu_buffer_rsrc_t r, uint32_t of
   return (uint32_t)__builtin_bit_cast(uint16_t,
                                       __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kStreamPolicy));
 }
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 __device__ __forceinline__ uint32_t ld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }

@@ -59,6 +59,9 @@ SHAPES = [
     (65, 130, 1024), (130, 300, 416), (257, 129, 96), (200, 64, 2048),
     # many-row kernel with tiles split over workgroups by K steps (stream-K)
     (600, 520, 2048), (300, 1000, 1024),
+    # many-row kernel with k % 256 != 0: a partial last weight group of 1, 2
+    # or 3 steps, scale rows only 4-byte aligned
+    (130, 300, 448), (257, 96, 320), (300, 200, 2176), (65, 40, 64),
 ]
 
 
@@ -80,6 +83,7 @@ EXACT_SHAPES = [
     ("smallm down", 64, 5120, 17408, 512),
     ("prefill gate", 2048, 17408, 5120, 256),
     ("prefill down", 2048, 5120, 17408, 128),
+    ("prefill down, one-eighth of inter", 2048, 5120, 2176, 128),
 ]
 
 
