@@ -83,43 +83,42 @@ __device__ __forceinline__ uint32_t e2m1_encode_sat(float q) {
 // One workgroup per row, one thread per 16-element block (k % 32 == 0): the
 // workgroup size follows the row length up to 1024 threads, and each thread
 // keeps up to kKeep of its blocks in registers between the row-amax pass and
-// the encode pass (longer rows re-read the rest).  The row amax is a plain
-// maximum, so the thread count does not change any result.
+// the encode pass (longer rows re-read the rest).  With few rows the row is
+// cut into gridDim.y slices, one workgroup each: every slice takes the amax
+// of the whole row (from cache after the first reads it) and encodes its own
+// blocks, so the divisions of one row spread over several CUs.  The row
+// amax is a plain maximum, so neither the thread count nor the slicing
+// changes any result.
 constexpr int kQuantMaxThreads = 1024;
 constexpr int kKeep = 4;
+constexpr int kSliceThreads = 256;
 
-__global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16_t *__restrict__ x, int k,
-                                                                   uint8_t *__restrict__ codes,
-                                                                   uint8_t *__restrict__ scales,
-                                                                   float *__restrict__ row_scale) {
-  const int r = blockIdx.x;
-  const int nt = blockDim.x;
-  const int t = threadIdx.x;
-  const int nblk = k >> 4;
-  const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
-
-  auto block_amax = [](const uint4 &v0, const uint4 &v1, float amax) {
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+// The row's absolute maximum, known to every thread.  One slice per row:
+// each thread keeps its first kKeep blocks in keep[].
+__device__ __forceinline__ float block_amax(const uint4 &v0, const uint4 &v1, float amax) {
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)));
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
-    }
-    return amax;
-  };
-
-  uint4 keep[kKeep][2];
+  for (int q = 0; q < 8; ++q) {
+    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)));
+    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
+  }
+  return amax;
+}
+__device__ __forceinline__ float row_amax(const uint4 *xv4, int nblk, uint4 (&keep)[kKeep][2]) {
+  const int nt = blockDim.x, t = threadIdx.x;
   float amax = 0.0f;
+  int b = t;
+  if (gridDim.y == 1) {
 #pragma unroll
-  for (int i = 0; i < kKeep; ++i) {
-    const int b = t + i * nt;
-    if (b < nblk) {
-      keep[i][0] = xv4[2 * b];
-      keep[i][1] = xv4[2 * b + 1];
-      amax = block_amax(keep[i][0], keep[i][1], amax);
+    for (int i = 0; i < kKeep; ++i, b += nt) {
+      if (b < nblk) {
+        keep[i][0] = xv4[2 * b];
+        keep[i][1] = xv4[2 * b + 1];
+        amax = block_amax(keep[i][0], keep[i][1], amax);
+      }
     }
   }
-  for (int b = t + kKeep * nt; b < nblk; b += nt) amax = block_amax(xv4[2 * b], xv4[2 * b + 1], amax);
+  for (; b < nblk; b += nt) amax = block_amax(xv4[2 * b], xv4[2 * b + 1], amax);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   __shared__ float wmax[kQuantMaxThreads / 64];
@@ -127,10 +126,41 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
   __syncthreads();
   amax = wmax[0];
   for (int w = 1; w < (nt >> 6); ++w) amax = fmaxf(amax, wmax[w]);
+  return amax;
+}
 
+// Encode this workgroup's blocks: all of the row (one slice: the kept blocks
+// from registers), or slice blockIdx.y's run of blocks.
+template <class Enc>
+__device__ __forceinline__ void encode_blocks(const uint4 *xv4, int nblk, const uint4 (&keep)[kKeep][2],
+                                              Enc &&encode_block) {
+  const int nt = blockDim.x, t = threadIdx.x;
+  if (gridDim.y == 1) {
+    int b = t;
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i, b += nt)
+      if (b < nblk) encode_block(b, keep[i][0], keep[i][1]);
+    for (; b < nblk; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
+  } else {
+    const int per = (nblk + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int b0 = (int)blockIdx.y * per, b1 = min(nblk, b0 + per);
+    for (int b = b0 + t; b < b1; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
+  }
+}
+
+__global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16_t *__restrict__ x, int k,
+                                                                   uint8_t *__restrict__ codes,
+                                                                   uint8_t *__restrict__ scales,
+                                                                   float *__restrict__ row_scale) {
+  const int r = blockIdx.x;
+  const int nblk = k >> 4;
+  const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
+
+  uint4 keep[kKeep][2];
+  const float amax = row_amax(xv4, nblk, keep);
   float s_row = amax / 2688.0f;
   if (amax == 0.0f) s_row = 1.0f;
-  if (t == 0) row_scale[r] = s_row;
+  if (threadIdx.x == 0 && blockIdx.y == 0) row_scale[r] = s_row;
 
   auto encode_block = [&](int b, const uint4 &v0, const uint4 &v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -161,62 +191,27 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
     *(uint2 *)(codes + (size_t)r * (k >> 1) + 8 * b) = make_uint2(packed[0], packed[1]);
     scales[(size_t)r * nblk + b] = (uint8_t)sb;
   };
-#pragma unroll
-  for (int i = 0; i < kKeep; ++i) {
-    const int b = t + i * nt;
-    if (b < nblk) encode_block(b, keep[i][0], keep[i][1]);
-  }
-  for (int b = t + kKeep * nt; b < nblk; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
+  encode_blocks(xv4, nblk, keep, encode_block);
 }
 
 // ---- per-row FP8 quantizer of the W8A8 arm ---------------------------------------
 // s_row = amax/448 (1 for an all-zero row), code = E4M3(x / s_row) with the
-// sign kept.  Same layout of work as k_quantize_rows: one workgroup per row,
-// one thread per 16-element block, up to kKeep blocks kept in registers.
+// sign kept.  Same layout of work as k_quantize_rows (row_amax and
+// encode_blocks above).
 
 __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const uint16_t *__restrict__ x,
                                                                        int k,
                                                                        uint8_t *__restrict__ codes,
                                                                        float *__restrict__ row_scale) {
   const int r = blockIdx.x;
-  const int nt = blockDim.x;
-  const int t = threadIdx.x;
   const int nblk = k >> 4;
   const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
 
-  auto block_amax = [](const uint4 &v0, const uint4 &v1, float amax) {
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] & 0xFFFFu)));
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[q] >> 16)));
-    }
-    return amax;
-  };
-
   uint4 keep[kKeep][2];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kKeep; ++i) {
-    const int b = t + i * nt;
-    if (b < nblk) {
-      keep[i][0] = xv4[2 * b];
-      keep[i][1] = xv4[2 * b + 1];
-      amax = block_amax(keep[i][0], keep[i][1], amax);
-    }
-  }
-  for (int b = t + kKeep * nt; b < nblk; b += nt) amax = block_amax(xv4[2 * b], xv4[2 * b + 1], amax);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  __shared__ float wmax[kQuantMaxThreads / 64];
-  if ((t & 63) == 0) wmax[t >> 6] = amax;
-  __syncthreads();
-  amax = wmax[0];
-  for (int w = 1; w < (nt >> 6); ++w) amax = fmaxf(amax, wmax[w]);
-
+  const float amax = row_amax(xv4, nblk, keep);
   float s_row = amax / 448.0f;
   if (amax == 0.0f) s_row = 1.0f;
-  if (t == 0) row_scale[r] = s_row;
+  if (threadIdx.x == 0 && blockIdx.y == 0) row_scale[r] = s_row;
 
   auto encode_block = [&](int b, const uint4 &v0, const uint4 &v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -230,22 +225,30 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const ui
     }
     *(uint4 *)(codes + (size_t)r * k + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
   };
-#pragma unroll
-  for (int i = 0; i < kKeep; ++i) {
-    const int b = t + i * nt;
-    if (b < nblk) encode_block(b, keep[i][0], keep[i][1]);
-  }
-  for (int b = t + kKeep * nt; b < nblk; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
+  encode_blocks(xv4, nblk, keep, encode_block);
+}
+
+// Quantizer launch shape: below 64 rows, slices of at least 32 blocks so
+// that about 64 workgroups share the work (at most 16 per row).
+struct QuantShape {
+  dim3 grid, block;
+};
+QuantShape quant_shape(int m, int k) {
+  const int nblk = k >> 4;
+  const int slices = (m <= 0 || m >= 64) ? 1 : std::min(std::min(16, (64 + m - 1) / m), std::max(1, nblk / 32));
+  QuantShape q;
+  q.grid = dim3(m, slices);
+  q.block = dim3(slices == 1 ? std::min(kQuantMaxThreads, (nblk + 63) / 64 * 64) : kSliceThreads);
+  return q;
 }
 
 }  // namespace
 
 hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes, float *row_scale,
                                     hipStream_t stream) {
-  const int nblk = k >> 4;
-  const int threads = std::min(kQuantMaxThreads, (nblk + 63) / 64 * 64);
-  hipLaunchKernelGGL(k_quantize_rows_fp8, dim3(m), dim3(threads), 0, stream, (const uint16_t *)x, k,
-                     codes, row_scale);
+  const QuantShape q = quant_shape(m, k);
+  hipLaunchKernelGGL(k_quantize_rows_fp8, q.grid, q.block, 0, stream, (const uint16_t *)x, k, codes,
+                     row_scale);
   return hipGetLastError();
 }
 
@@ -260,12 +263,12 @@ hipError_t launch_silu_mul(const void *gate, const void *up, void *out, int64_t 
   return hipGetLastError();
 }
 
+
 hipError_t launch_quantize_rows(const void *x, int m, int k, uint8_t *codes, uint8_t *scales,
                                 float *row_scale, hipStream_t stream) {
-  const int nblk = k >> 4;
-  const int threads = std::min(kQuantMaxThreads, (nblk + 63) / 64 * 64);
-  hipLaunchKernelGGL(k_quantize_rows, dim3(m), dim3(threads), 0, stream, (const uint16_t *)x, k,
-                     codes, scales, row_scale);
+  const QuantShape q = quant_shape(m, k);
+  hipLaunchKernelGGL(k_quantize_rows, q.grid, q.block, 0, stream, (const uint16_t *)x, k, codes, scales,
+                     row_scale);
   return hipGetLastError();
 }
 
