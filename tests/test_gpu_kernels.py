@@ -55,6 +55,7 @@ def test_dequant_every_code_and_scale_exact(m):
 
 SHAPES = [
     (1, 16, 32), (1, 50, 96), (2, 200, 160), (4, 64, 4096), (15, 33, 128), (16, 64, 256),
+    (9, 70, 224), (6, 20, 96),
     (17, 80, 384), (33, 33, 512), (48, 100, 640), (64, 130, 1024),
     (65, 130, 1024), (130, 300, 416), (257, 129, 96), (200, 64, 2048),
     # many-row kernel with tiles split over workgroups by K steps (stream-K)
@@ -169,7 +170,8 @@ def test_quantize_golden_rows_on_gpu():
 
 # ---- W4A4 projection ------------------------------------------------------------------------
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 32), (3, 100, 160), (64, 130, 1024), (100, 64, 512)])
+@pytest.mark.parametrize("m,n,k", [(1, 16, 32), (3, 100, 160), (64, 130, 1024), (100, 64, 512),
+                                   (5, 40, 96), (12, 48, 352)])
 def test_gemm_w4a4_matches_oracle(m, n, k):
     _say(f"gemm_w4a4 m={m} n={n} k={k}")
     x = si.activations(m, k, seed=m + 2 * n)

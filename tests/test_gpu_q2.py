@@ -46,7 +46,9 @@ def oq(w: si.Q2Weight) -> oracle.Q2Weight:
 @pytest.mark.parametrize("m,n,k,group", [(1, 48, 128, 128), (5, 300, 384, 128), (17, 130, 224, 32),
                                          (70, 257, 640, 64), (3, 64, 4096, 128),
                                          (3, 16400, 256, 128), (64, 1000, 2048, 128),
-                                         (2, 40, 512, 256), (130, 96, 768, 256)])
+                                         (2, 40, 512, 256), (130, 96, 768, 256),
+                                         # up to 16 rows with a ragged last 128-K step
+                                         (4, 72, 160, 32), (9, 33, 96, 32), (1, 16, 224, 32)])
 def test_q2_gemm_matches_oracle(m, n, k, group):
     _say(f"q2 gemm m={m} n={n} k={k} group={group}")
     x = si.activations(m, k, seed=n, outliers=True)

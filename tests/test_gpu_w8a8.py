@@ -86,7 +86,8 @@ def test_fp8_quantizer_every_bf16_quotient():
 # workgroups; n >= 16384 takes two column tiles per workgroup, 16400 with a
 # last 16-column tile and a partial scale block along N and K
 @pytest.mark.parametrize("m,n,k", [(1, 48, 96), (5, 300, 384), (17, 130, 224), (70, 257, 640),
-                                   (3, 64, 4096), (3, 16400, 160), (64, 1000, 2048)])
+                                   (3, 64, 4096), (3, 16400, 160), (64, 1000, 2048),
+                                   (9, 200, 320), (2, 40, 64)])
 def test_fp8_gemm_w8a8_matches_oracle(m, n, k):
     _say(f"fp8 gemm m={m} n={n} k={k}")
     x = _rows_with_edge_cases(m, k, seed=n)
