@@ -320,10 +320,14 @@ __global__ __launch_bounds__(256) void k_dequant_q2_bf16(const uint32_t *__restr
 }  // namespace
 
 // Column tiles per workgroup: with more than 16 rows each activation
-// fragment (64 bytes per row and step) is shared by four column tiles, which
-// divides the activation re-reads from L2 by four; with few rows the tiles
-// stay narrow so that the weight stream spreads over many workgroups.
-int q2_ctw(int m, int n) { return m > 16 ? 4 : (n >= 16 * 2 * 512 ? 2 : 1); }
+// fragment (64 bytes per row and step) is shared by several column tiles,
+// which divides the activation re-reads from L2 -- two tiles up to 32 rows,
+// four above (four tiles of 32 rows need 440 registers per lane, one wave
+// per SIMD: FFN on the small-m shape at m=17 and 32 in 107 and 125 us with
+// two, 130 and 139 us with four; at m=64 185 against 177 us); with few rows
+// the tiles stay narrow so that the weight stream spreads over many
+// workgroups.
+int q2_ctw(int m, int n) { return m > 32 ? 4 : (m > 16 ? 2 : (n >= 16 * 2 * 512 ? 2 : 1)); }
 
 StreamPlan q2_plan(int m, int n, int k) {
   constexpr int kTarget = 512;  // workgroups before K is split
