@@ -702,28 +702,37 @@ int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden, int32_t int
   ProfileScope ps("dense_total lora", m, s);
   MatRef mg = mat(wg), mu = mat(wu), md = mat(wd);
   const ActRef ax{x, nullptr, nullptr, nullptr};
-  if (p_up == Path::Gemv) {
-    // one launch streams both weights and writes gate and up apart
-    const MatRef w2[2] = {mg, mu};
-    if ((rc = hip_status(launch_gemv(x, m, hidden, inter, 2, w2, g, s, u), "gemv projection launch")))
-      return rc;
-  } else if ((rc = run_proj(ax, m, hidden, inter, 1, &mg, g, scr, p_up, s)) ||
-             (rc = run_proj(ax, m, hidden, inter, 1, &mu, u, scr, p_up, s))) {
-    return rc;
-  }
   auto ref = [](const nvfp4_lora_pair &l) {
     return lora_on(l) ? LoraRef{l.a, l.b, l.rank, l.scale} : LoraRef{nullptr, nullptr, 0, 0.f};
   };
-  // gate and up deltas, then silu_mul, in one pass over gate/up (act over gate)
-  if ((rc = hip_status(launch_lora_gate_up_silu(x, m, hidden, ref(lora->gate), ref(lora->up), inter, g,
-                                                u, xa, s),
-                       "lora gate/up + silu launch")))
+  const LoraRef lg = ref(lora->gate), lu = ref(lora->up), ld = ref(lora->down);
+  const LoraRef none{nullptr, nullptr, 0, 0.f};
+  if (p_up == Path::Gemv) {
+    // x . A^T of both pairs, then one GEMV launch streams both weights and
+    // adds the deltas and silu_mul in its epilogue (act over gate)
+    const MatRef w2[2] = {mg, mu};
+    const GemvLora gl{xa, lora_chunks(hidden), std::max(lg.r, lu.r), {lg.b, lu.b}, {lg.r, lu.r},
+                      {lg.scale, lu.scale}};
+    if ((rc = hip_status(launch_lora_xa_pair(x, m, hidden, lg, lu, xa, s), "lora x.A launch")) ||
+        (rc = hip_status(launch_gemv(x, m, hidden, inter, 2, w2, g, s, &gl), "gemv projection launch")))
+      return rc;
+  } else if ((rc = run_proj(ax, m, hidden, inter, 1, &mg, g, scr, p_up, s)) ||
+             (rc = run_proj(ax, m, hidden, inter, 1, &mu, u, scr, p_up, s)) ||
+             // gate and up deltas, then silu_mul, in one pass over gate/up (act over gate)
+             (rc = hip_status(launch_lora_gate_up_silu(x, m, hidden, lg, lu, inter, g, u, xa, s),
+                              "lora gate/up + silu launch"))) {
     return rc;
-  if ((rc = run_proj(ActRef{g, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &md, out, scr, p_down, s)))
-    return rc;
-  if (!lora_on(lora->down)) return NVFP4_OK;
-  return hip_status(launch_lora_delta(g, m, inter, lora->down.a, lora->down.b, lora->down.rank, hidden,
-                                      lora->down.scale, out, xa, s),
+  }
+  const ActRef aact{g, nullptr, nullptr, nullptr};
+  if (ld.r == 0) return run_proj(aact, m, inter, hidden, 1, &md, out, scr, p_down, s);
+  if (p_down == Path::Gemv) {
+    // act . A^T, then the down GEMV adds the delta in its epilogue
+    const GemvLora gl{xa, lora_chunks(inter), ld.r, {ld.b, nullptr}, {ld.r, 0}, {ld.scale, 0.f}};
+    if ((rc = hip_status(launch_lora_xa_pair(g, m, inter, ld, none, xa, s), "lora act.A launch"))) return rc;
+    return hip_status(launch_gemv(g, m, inter, hidden, 1, &md, out, s, &gl), "gemv projection launch");
+  }
+  if ((rc = run_proj(aact, m, inter, hidden, 1, &md, out, scr, p_down, s))) return rc;
+  return hip_status(launch_lora_delta(g, m, inter, ld.a, ld.b, ld.r, hidden, ld.scale, out, xa, s),
                     "lora delta launch");
 }
 

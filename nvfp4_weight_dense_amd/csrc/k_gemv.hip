@@ -43,9 +43,62 @@ struct GemvArgs {
   const uint8_t *codes1, *scales1;
   float ts0, ts1;
   void *y;                // bf16 [m][n]
-  void *y2;               // NMAT = 2 only: non-null -> gate into y, up into y2, no silu
   int nbatch;
+  // LoRA epilogue (lora_xa non-null; see GemvLora)
+  const float *lora_xa;
+  int lora_nkc, lora_rmax;
+  const uint16_t *lora_b[2];
+  int lora_r[2];
+  float lora_scale[2];
 };
+
+// The LoRA epilogue's xa into LDS, once per workgroup: xs[row][i][j] is the
+// sum of pair i's chunk partials in chunk order (loads issued four at a
+// time, added in order).
+template <int M>
+__device__ void lora_gather(const GemvArgs &p, float (&xs)[M][2][kMaxRank]) {
+  const int rmax = p.lora_rmax, nkc = p.lora_nkc;
+  const size_t cstride = (size_t)p.m * rmax;
+  for (int idx = threadIdx.x; idx < M * 2 * rmax; idx += blockDim.x) {
+    const int j = idx % rmax, i = (idx / rmax) % 2, row = idx / (2 * rmax);
+    float v = 0.f;
+    if (row < p.m && j < p.lora_r[i]) {
+      const float *part = p.lora_xa + (size_t)i * nkc * cstride + (size_t)row * rmax + j;
+      int kc = 0;
+      for (; kc + 4 <= nkc; kc += 4) {
+        const float a0 = part[kc * cstride], a1 = part[(kc + 1) * cstride];
+        const float a2 = part[(kc + 2) * cstride], a3 = part[(kc + 3) * cstride];
+        v += a0;
+        v += a1;
+        v += a2;
+        v += a3;
+      }
+      for (; kc < nkc; ++kc) v += part[kc * cstride];
+    }
+    xs[row][i][j] = v;
+  }
+}
+
+// v + scale * xa . B[col] for pair i of the LoRA epilogue, rounded to bf16:
+// the dot runs in j order with fma -- the arithmetic of the separate LoRA
+// passes.
+__device__ float lora_apply(const GemvArgs &p, const float *xs, int i, int col, float v) {
+  const int r = p.lora_r[i];
+  if (r == 0) return v;
+  auto xa = [&](int j) { return xs[j]; };
+  const uint4 *bc = (const uint4 *)(p.lora_b[i] + (size_t)col * r);
+  float d = 0.f;
+  for (int j8 = 0; j8 < (r >> 3); ++j8) {
+    const uint4 bv = bc[j8];
+    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      d = fmaf(xa(8 * j8 + 2 * q), __builtin_bit_cast(float, bw[q] << 16), d);
+      d = fmaf(xa(8 * j8 + 2 * q + 1), __builtin_bit_cast(float, bw[q] & 0xFFFF0000u), d);
+    }
+  }
+  return (float)(__bf16)(v + p.lora_scale[i] * d);
+}
 
 __device__ __forceinline__ bf16x2 u32_as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
@@ -116,6 +169,7 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
   }
 
   __shared__ float red[kMaxKW][kCB][M];
+  __shared__ float lxs[M][2][kMaxRank];  // LoRA epilogue: xa per row and pair
 
   // weight rows of batch b: 8 code granules and their scale pairs per lane
   auto load_batch = [&](int b, uint4 (&cw)[kCB][G], uint32_t (&sw)[kCB][G]) {
@@ -220,16 +274,20 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
       if (r >= p.m) break;
       if constexpr (NMAT == 1) {
         const int c = lane >> 3;
-        if ((lane & 7) == 0 && c < ncols)
-          ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = (__bf16)(tot[r] * p.ts0);
+        if ((lane & 7) == 0 && c < ncols) {
+          __bf16 o = (__bf16)(tot[r] * p.ts0);
+          if (p.lora_xa) o = (__bf16)lora_apply(p, lxs[r][0], 0, c0 + c, (float)o);
+          ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = o;
+        }
       } else {
         const float up = xor_shfl<8>(tot[r]);  // entry 2c+1 (up) next to 2c (gate)
         const int c = lane >> 4;
         if ((lane & 15) == 0 && c < ncols) {
           const size_t o = (size_t)r * p.n + c0 + c;
-          if (p.y2) {  // gate and up kept apart (an overlay adds to each before silu)
-            ((__bf16 *)p.y)[o] = (__bf16)(tot[r] * p.ts0);
-            ((__bf16 *)p.y2)[o] = (__bf16)(up * p.ts1);
+          if (p.lora_xa) {  // deltas on the bf16 gate and up, then silu_mul
+            const float gb = lora_apply(p, lxs[r][0], 0, c0 + c, (float)(__bf16)(tot[r] * p.ts0));
+            const float ub = lora_apply(p, lxs[r][1], 1, c0 + c, (float)(__bf16)(up * p.ts1));
+            ((__bf16 *)p.y)[o] = (__bf16)(silu_f32(gb) * ub);
           } else {
             ((__bf16 *)p.y)[o] = swiglu_bf16(tot[r] * p.ts0, up * p.ts1);
           }
@@ -244,6 +302,10 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
   uint32_t swA[kCB][G], swB[kCB][G];
   int b = blockIdx.x;
   load_batch(b, cwA, swA);
+  if (p.lora_xa) {  // while the first batch's weights are in flight
+    lora_gather<M>(p, lxs);
+    __syncthreads();
+  }
   for (; b < p.nbatch; b += 2 * gridDim.x) {
     const int b1 = b + gridDim.x;
     load_batch(b1, cwB, swB);
@@ -320,7 +382,7 @@ bool gemv_eligible(int m, int k) {
 }
 
 hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat, const MatRef *w, void *y,
-                       hipStream_t stream, void *y2) {
+                       hipStream_t stream, const GemvLora *lora) {
   GemvArgs p{};
   p.x = x;
   p.m = m;
@@ -333,8 +395,17 @@ hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat, const MatRe
   p.scales1 = nmat > 1 ? w[1].scales : nullptr;
   p.ts1 = nmat > 1 ? w[1].ts : 0.f;
   p.y = y;
-  p.y2 = nmat > 1 ? y2 : nullptr;
   p.nbatch = cdiv(n, kCB / nmat);
+  if (lora) {
+    p.lora_xa = lora->xa;
+    p.lora_nkc = lora->nkc;
+    p.lora_rmax = lora->rmax;
+    for (int i = 0; i < 2; ++i) {
+      p.lora_b[i] = (const uint16_t *)lora->b[i];
+      p.lora_r[i] = i < nmat ? lora->r[i] : 0;
+      p.lora_scale[i] = lora->scale[i];
+    }
+  }
   const GemvShape s = gemv_shape(m, k);
   return nmat == 1 ? launch_n<1>(p, s, stream) : launch_n<2>(p, s, stream);
 }

@@ -182,6 +182,14 @@ hipError_t launch_xa(const void *x, int m, int k, const void *a0, int r0, const 
 
 }  // namespace
 
+int lora_chunks(int k) { return chunks(k); }
+
+hipError_t launch_lora_xa_pair(const void *x, int m, int k, const LoraRef &lg, const LoraRef &lu, float *xa,
+                               hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  return launch_xa(x, m, k, lg.a, lg.r, lu.a, lu.r, xa, stream);
+}
+
 size_t lora_xa_floats(int m, int k, int npairs) { return (size_t)npairs * chunks(k) * m * kMaxRank; }
 
 hipError_t launch_lora_delta(const void *x, int m, int k, const void *a, const void *b, int r, int n,

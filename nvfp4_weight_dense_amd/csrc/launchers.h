@@ -103,7 +103,7 @@ hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat,
                           hipStream_t stream);
 
 // Vector-ALU projection for 1..4 rows (bf16 activations), nmat as above;
-// with nmat 2 and y2 set, gate goes to y and up to y2 (no silu).
+// with a GemvLora, the LoRA deltas are added in the epilogue.
 // Eligible when K splits into at most 4 waves of register-resident granules.
 // LoRA delta: base[m][n] (bf16, in place) += scale * (x . A^T) . B^T with
 // A bf16 [r][k], B bf16 [n][r]; xa is fp32 scratch of lora_xa_floats(m, k,
@@ -121,11 +121,28 @@ hipError_t launch_lora_delta(const void *x, int m, int k, const void *a, const v
 // receives act = bf16(silu(bf16(g + dg)) * bf16(u + du)).
 hipError_t launch_lora_gate_up_silu(const void *x, int m, int k, const LoraRef &lg, const LoraRef &lu,
                                     int n, void *g, const void *u, float *xa, hipStream_t stream);
+// x . A^T partials alone (one or two pairs; lg.r or lu.r may be 0), for a
+// GEMV that adds the deltas in its epilogue; lora_chunks(k) K chunks.
+hipError_t launch_lora_xa_pair(const void *x, int m, int k, const LoraRef &lg, const LoraRef &lu, float *xa,
+                               hipStream_t stream);
+int lora_chunks(int k);
 
 bool gemv_eligible(int m, int k);
+// LoRA epilogue of the GEMV: matrix i's bf16 value v becomes
+// bf16(v + scale[i] * xa_i . B_i[c]) before the silu (nmat 2) or as the
+// output (nmat 1), with xa_i the fp32 partials of x . A_i^T written by
+// launch_lora_xa_pair ([pair][nkc][m][rmax], summed in chunk order) -- the
+// arithmetic of launch_lora_gate_up_silu / launch_lora_delta.
+struct GemvLora {
+  const float *xa;
+  int nkc, rmax;
+  const void *b[2];  // B_i bf16 [n][r_i]
+  int r[2];          // 0: no pair
+  float scale[2];
+};
 hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat,
                        const MatRef *w, void *y, hipStream_t stream,
-                       void *y2 = nullptr);
+                       const GemvLora *lora = nullptr);
 
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out,
                            int64_t count, hipStream_t stream);

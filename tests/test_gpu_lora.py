@@ -92,6 +92,29 @@ def test_dense_ffn_lora_single_pair(which):
     assert np.max(np.abs(got - ye) / bound) <= 1.0
 
 
+@pytest.mark.parametrize("m", [1, 3])
+def test_dense_ffn_lora_fused_epilogue_equals_composition(m):
+    """Up to four rows the GEMVs add the LoRA deltas in their epilogues; the
+    result must equal, bit for bit, the same FFN composed from the separate
+    entry points (gate and up GEMMs, LoRA deltas into the bf16 buffers,
+    silu_mul, down GEMM, down delta): the same roundings in the same order."""
+    _say(f"ffn lora fused vs composed m={m}")
+    x, wg, wu, wd = si.workload("tiny", m=m)
+    hidden, inter = x.shape[1], wg.n
+    pg, _ = _pair(inter, hidden, 16, 0, 2.0)
+    pu, _ = _pair(inter, hidden, 8, 1, -1.5)
+    pd, _ = _pair(hidden, inter, 24, 2, 0.5)
+    xd = x.cuda()
+    Wg, Wu, Wd = g_weight(wg), g_weight(wu), g_weight(wd)
+    y = nv.dense_ffn_forward_lora(xd, Wg, Wu, Wd, pg, pu, pd)
+    g = nv.nvfp4_lora_delta(xd, pg, nv.nvfp4_gemm_w4a16(xd, Wg))
+    u = nv.nvfp4_lora_delta(xd, pu, nv.nvfp4_gemm_w4a16(xd, Wu))
+    act = nv.silu_mul(g, u)
+    y2 = nv.nvfp4_lora_delta(act, pd, nv.nvfp4_gemm_w4a16(act, Wd))
+    sync()
+    assert np.array_equal(bits(y), bits(y2))
+
+
 def test_dense_ffn_lora_without_pairs_is_dense_ffn():
     _say("ffn lora, no pairs")
     x, wg, wu, wd = si.workload("tiny", m=6)
