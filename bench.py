@@ -290,7 +290,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              "(this build runs the FFN on a single MI355X)", file=sys.stderr)
+              "(the FFN runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
     import torch

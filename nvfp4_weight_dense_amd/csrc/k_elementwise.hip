@@ -7,7 +7,8 @@
 
 // The quantizer's codes must equal the CPU definition bit for bit: every
 // float operation below is one IEEE fp32 operation in the written order
-// (no FMA contraction; fp32 division is correctly rounded in this build).
+// (no FMA contraction; fp32 division is correctly rounded: the library is
+// compiled with -fhip-fp32-correctly-rounded-divide-sqrt).
 #pragma clang fp contract(off)
 
 namespace nvfp4 {
