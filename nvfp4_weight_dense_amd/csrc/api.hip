@@ -69,7 +69,7 @@ const char *path_name(Path p) {
 }
 
 // weight-streaming kernel for this many rows: plain up to 16; from 17 to 64
-// the LDS-DMA weight ring when k % 256 == 0, else LDS-shared activations
+// the LDS-DMA weight ring when k % 64 == 0, else LDS-shared activations
 Path stream_kind(int m, int k) {
   if (m <= 16) return Path::Stream;
   return smallm_eligible(m, k) ? Path::Small : Path::StreamLds;

@@ -31,7 +31,12 @@
 // Lane (c = lane%32, h = lane/32) holds for weight row col+c the 32 codes at
 // K offset 32h of a step; MFMA j sums K offsets {8j..8j+7} U
 // {32+8j..32+8j+7}, and the A fragment of row tile mt is read at LDS row
-// 32mt+c at the same offsets.  Requires k % 256 == 0.
+// 32mt+c at the same offsets.  Requires k % 64 == 0 (whole steps).  When
+// k % 256 != 0 the last weight group of the last split is partial: the
+// steps it lacks are never run (the code bytes its requests bring from
+// beyond each row's end are never read), and the scales come a dword (one
+// step) at a time, since the scale rows are then only 4-byte aligned and a
+// 16-byte load could straddle the end of the last row.
 #include <algorithm>
 #include <type_traits>
 
@@ -155,9 +160,17 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
   uint4 sc[kRing][kNB];
   auto load_scales = [&](int G, uint4 (&sv)[kNB]) {
     const uint32_t goff = (uint32_t)(s_begin + kGroup * G) * 4u;
-    const bool ok = kGroup * G < len;
+    const int nst = len - kGroup * G;  // steps of this group that run (uniform)
+    if (nst >= kGroup && (kb16 & 15u) == 0) {
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) sv[i] = ld16(ws[i], ok ? (uint32_t)c32 * kb16 + goff : kOOB);
+      for (int i = 0; i < kNB; ++i) sv[i] = ld16(ws[i], (uint32_t)c32 * kb16 + goff);
+    } else {
+      const uint32_t o = (uint32_t)c32 * kb16 + goff;
+#pragma unroll
+      for (int i = 0; i < kNB; ++i)
+        sv[i] = uint4{ld4(ws[i], nst > 0 ? o : kOOB), ld4(ws[i], nst > 1 ? o + 4u : kOOB),
+                      ld4(ws[i], nst > 2 ? o + 8u : kOOB), ld4(ws[i], nst > 3 ? o + 12u : kOOB)};
+    }
   };
   auto dequant_j = [&](const uint4 (&w)[kNB], const uint32_t (&s)[kNB], int j, bf16x8 (&out)[kNB]) {
 #pragma unroll
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(256) void k_smallm_reduce(const float *__restrict__
 
 }  // namespace
 
-bool smallm_eligible(int m, int k) { return m >= 17 && m <= 64 && k % 256 == 0; }
+bool smallm_eligible(int m, int k) { return m >= 17 && m <= 64 && k % 64 == 0; }
 
 SmallPlan smallm_plan(int m, int n, int k, int nmat) {
   SmallPlan pl;

@@ -63,7 +63,7 @@ hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat,
                              unsigned *counters, const LdsPlan &pl,
                              hipStream_t stream);
 
-// Weight-streaming projection for 17..64 rows (bf16 activations, k % 256
+// Weight-streaming projection for 17..64 rows (bf16 activations, k % 64
 // == 0): two-wave workgroups of 64 (nmat 2, gate+up+silu fused) or 128
 // (nmat 1) columns, K split over blockIdx.y with the in-kernel fixup;
 // `partial` holds smallm_partial_floats(...) floats and `counters` tiles

@@ -57,6 +57,9 @@ SHAPES = [
     (1, 16, 32), (1, 50, 96), (2, 200, 160), (4, 64, 4096), (15, 33, 128), (16, 64, 256),
     (9, 70, 224), (6, 20, 96),
     (17, 80, 384), (33, 33, 512), (48, 100, 640), (64, 130, 1024),
+    # 17..64 rows: k % 64 == 0 with a partial last weight group (LDS-DMA
+    # ring), and k % 64 != 0 (LDS-shared activations)
+    (40, 70, 2176), (20, 64, 160), (64, 48, 96),
     (65, 130, 1024), (130, 300, 416), (257, 129, 96), (200, 64, 2048),
     # many-row kernel with tiles split over workgroups by K steps (stream-K)
     (600, 520, 2048), (300, 1000, 1024),
