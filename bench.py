@@ -16,7 +16,7 @@ launches on, around exactly K back-to-back steps after W warm-up steps,
 bracketed by device synchronizations.
 
 roofline: the dominant kernel is the fused gate+up+silu single-row kernel
-k_gemv<1, 2, 1> (two thirds of the decode FFN's bytes); its average launch duration
+k_gemv<1, 2, 1, false> (two thirds of the decode FFN's bytes); its average launch duration
 comes from K back-to-back launches of nvfp4_gate_up_silu_w4a16 (one kernel
 per call at this shape) between events on the same stream.  Algorithmic
 bytes per launch = both weight matrices (codes + E4M3 scales) + x + act.
@@ -44,7 +44,7 @@ FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 REPLICA_BYTES = 1 << 30
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 DOMINANT_KERNEL_SRC = os.path.join(ROOT, "nvfp4_weight_dense_amd", "csrc", "k_gemv.hip")
-DOMINANT_KERNEL = "k_gemv<1, 2, 1>"
+DOMINANT_KERNEL = "k_gemv<1, 2, 1, false>"
 TRAFFIC_FILE = os.path.join(PROFILE_DIR, "k_gemv_gate_up_silu_decode_traffic.txt")
 COPY_BYTES = 1 << 28
 
