@@ -81,15 +81,17 @@ __device__ void lora_gather(const GemvArgs &p, float (&xs)[M][2][kMaxRank]) {
 
 // v + scale * xa . B[col] for pair i of the LoRA epilogue, rounded to bf16:
 // the dot runs in j order with fma -- the arithmetic of the separate LoRA
-// passes.
-__device__ float lora_apply(const GemvArgs &p, const float *xs, int i, int col, float v) {
+// passes.  Ranks up to kLoraPre take B[col] from pre (loaded with the
+// batch's weights), larger ranks load it here.
+constexpr int kLoraPre = 16;
+__device__ float lora_apply(const GemvArgs &p, const float *xs, int i, int col, float v, const uint4 (&pre)[2]) {
   const int r = p.lora_r[i];
   if (r == 0) return v;
   auto xa = [&](int j) { return xs[j]; };
   const uint4 *bc = (const uint4 *)(p.lora_b[i] + (size_t)col * r);
   float d = 0.f;
   for (int j8 = 0; j8 < (r >> 3); ++j8) {
-    const uint4 bv = bc[j8];
+    const uint4 bv = r <= kLoraPre ? (j8 == 0 ? pre[0] : pre[1]) : bc[j8];
     const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -175,7 +177,10 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
   __shared__ float lxs[LORA ? M : 1][2][LORA ? kMaxRank : 1];  // LoRA epilogue: xa per row and pair
 
   // weight rows of batch b: 8 code granules and their scale pairs per lane
-  auto load_batch = [&](int b, uint4 (&cw)[kCB][G], uint32_t (&sw)[kCB][G]) {
+  // LORA: the B rows of this lane's epilogue column (ranks up to kLoraPre),
+  // loaded with the batch's weights so that the epilogue waits on nothing
+  // issued after them (loads complete in order)
+  auto load_batch = [&](int b, uint4 (&cw)[kCB][G], uint32_t (&sw)[kCB][G], uint4 (&lb)[2][2]) {
     const int c0 = b * NC;
     const int ncols = b < p.nbatch ? min(NC, p.n - c0) : 0;
     __amdgpu_buffer_rsrc_t wres[NMAT], sres[NMAT];
@@ -195,9 +200,24 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
         sw[i][g] = ld2_nt(sres[mat], jok[g] ? col * kb16 + jg[g] * 2u : kOOB);
       }
     }
+    if constexpr (LORA) {
+      // the epilogue lane of column c of the batch (see compute_batch)
+      const int c = NMAT == 2 ? (lane >> 4) : (lane >> 3);
+      const bool epi = NMAT == 2 ? (lane & 15) == 0 : (lane & 7) == 0;
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i) {
+        const int r = p.lora_r[i];
+        const bool pre = epi && r > 0 && r <= kLoraPre;
+        const __amdgpu_buffer_rsrc_t bres = rsrc(p.lora_b[i] + (size_t)c0 * r, (size_t)ncols * r * 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          lb[i][h] = ld16(bres, (pre && 8 * h < r) ? (uint32_t)(c * r * 2 + 16 * h) : kOOB);
+      }
+    }
   };
 
-  auto compute_batch = [&](int b, const uint4 (&cw)[kCB][G], const uint32_t (&sw)[kCB][G]) {
+  auto compute_batch = [&](int b, const uint4 (&cw)[kCB][G], const uint32_t (&sw)[kCB][G],
+                           const uint4 (&lb)[2][2]) {
     const int c0 = b * NC;
     const int ncols = min(NC, p.n - c0);
     float v[kCB][M];
@@ -279,7 +299,7 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
         const int c = lane >> 3;
         if ((lane & 7) == 0 && c < ncols) {
           __bf16 o = (__bf16)(tot[r] * p.ts0);
-          if constexpr (LORA) o = (__bf16)lora_apply(p, lxs[r][0], 0, c0 + c, (float)o);
+          if constexpr (LORA) o = (__bf16)lora_apply(p, lxs[r][0], 0, c0 + c, (float)o, lb[0]);
           ((__bf16 *)p.y)[(size_t)r * p.n + c0 + c] = o;
         }
       } else {
@@ -288,8 +308,8 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
         if ((lane & 15) == 0 && c < ncols) {
           const size_t o = (size_t)r * p.n + c0 + c;
           if constexpr (LORA) {  // deltas on the bf16 gate and up, then silu_mul
-            const float gb = lora_apply(p, lxs[r][0], 0, c0 + c, (float)(__bf16)(tot[r] * p.ts0));
-            const float ub = lora_apply(p, lxs[r][1], 1, c0 + c, (float)(__bf16)(up * p.ts1));
+            const float gb = lora_apply(p, lxs[r][0], 0, c0 + c, (float)(__bf16)(tot[r] * p.ts0), lb[0]);
+            const float ub = lora_apply(p, lxs[r][1], 1, c0 + c, (float)(__bf16)(up * p.ts1), lb[1]);
             ((__bf16 *)p.y)[o] = (__bf16)(silu_f32(gb) * ub);
           } else {
             ((__bf16 *)p.y)[o] = swiglu_bf16(tot[r] * p.ts0, up * p.ts1);
@@ -304,19 +324,20 @@ __global__ __launch_bounds__(kMaxKW * 64) void k_gemv(GemvArgs p) {
   uint4 cwA[kCB][G], cwB[kCB][G];
   uint32_t swA[kCB][G], swB[kCB][G];
   int b = blockIdx.x;
-  load_batch(b, cwA, swA);
+  uint4 lbA[2][2] = {}, lbB[2][2] = {};
+  load_batch(b, cwA, swA, lbA);
   if constexpr (LORA) {  // while the first batch's weights are in flight
     lora_gather<M>(p, lxs);
     __syncthreads();
   }
   for (; b < p.nbatch; b += 2 * gridDim.x) {
     const int b1 = b + gridDim.x;
-    load_batch(b1, cwB, swB);
-    compute_batch(b, cwA, swA);
+    load_batch(b1, cwB, swB, lbB);
+    compute_batch(b, cwA, swA, lbA);
     if (b1 >= p.nbatch) break;
     const int b2 = b1 + gridDim.x;
-    load_batch(b2, cwA, swA);
-    compute_batch(b1, cwB, swB);
+    load_batch(b2, cwA, swA, lbA);
+    compute_batch(b1, cwB, swB, lbB);
   }
 }
 
