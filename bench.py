@@ -9,20 +9,31 @@ and the packed-Q2 weights are measured in the same run and reported under
 
 Cold weights: every weight set fits in the 256 MB Infinity Cache, so each
 step reads the next of R replicas with R x size >= 1 GiB; the reported
-weight GB/s is HBM traffic, not cache hits.
+weight GB/s is HBM traffic, not cache hits.  "warm" entries (one replica,
+cache-resident) are measured separately and labelled as such.
 
 Timing: hipEvents (torch.cuda.Event) recorded on the stream the library
 launches on, around exactly K back-to-back steps after W warm-up steps,
-bracketed by device synchronizations.
+bracketed by device synchronizations.  Before the W warm-up steps of each
+workload the same call runs untimed for RAMP_S seconds of wall time: after
+an idle gap (weight replicas being built on the host) the first tens of
+milliseconds of GPU work run up to 20% slower, and a warm-up counted in
+calls would time that ramp instead of the kernels.
 
 roofline: the dominant kernel is the fused gate+up+silu single-row kernel
-k_gemv<1, 2, 1, false> (two thirds of the decode FFN's bytes); its average launch duration
-comes from K back-to-back launches of nvfp4_gate_up_silu_w4a16 (one kernel
-per call at this shape) between events on the same stream.  Algorithmic
-bytes per launch = both weight matrices (codes + E4M3 scales) + x + act.
+k_gemv<1, 2, 1, false> (two thirds of the decode FFN's bytes); its average
+launch duration comes from K back-to-back launches of
+nvfp4_gate_up_silu_w4a16 (one kernel per call at this shape) between events
+on the same stream.  Algorithmic bytes per launch = both weight matrices
+(codes + E4M3 scales) + x + act.
+
+mfma_peak: the bf16 matrix throughput a register-only MFMA loop reaches on
+this part (nvfp4_probe_mfma_bf16), beside the 2.5 PFLOP/s specification.
 
 cpu_baseline: the CPU oracle (fp64, plain loops) on the same decode
-workload, repeated for about 10 s on 16 host threads.
+workload, repeated for about 10 s on the host's cores; per_config: the
+oracle on a few sampled rows of every workload (its time scaled to the
+workload's rows, and the GPU rows' max |err| / rms against it).
 """
 
 from __future__ import annotations
@@ -42,6 +53,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 REPLICA_BYTES = 1 << 30
+RAMP_S = 0.15                   # untimed calls before the counted warm-up, per workload
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 DOMINANT_KERNEL_SRC = os.path.join(ROOT, "nvfp4_weight_dense_amd", "csrc", "k_gemv.hip")
 DOMINANT_KERNEL = "k_gemv<1, 2, 1, false>"
@@ -71,8 +83,22 @@ def _replicas(ws, count, device):
     return out
 
 
-def _time_loop(fn, reps, steps, warmup, stream):
+def _ramp(fn, reps, seconds):
+    """Untimed calls for `seconds` of wall time (GPU clock ramp)."""
     import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn(reps[i % len(reps)])
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def _time_loop(fn, reps, steps, warmup, stream, ramp_s=RAMP_S):
+    import torch
+    _ramp(fn, reps, ramp_s)
     for i in range(warmup):
         fn(reps[i % len(reps)])
     torch.cuda.synchronize()
@@ -86,8 +112,18 @@ def _time_loop(fn, reps, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def _label(name, m, hidden, inter, w4a4=False, w8a8=False, q2=False, fused=False, lora_rank=0,
+           warm=False):
+    return (f"{name} m={m} hidden={hidden} inter={inter}" + (" w4a4" if w4a4 else "")
+            + (" (block-scaled FP8 weights, per-row FP8 activations)" if w8a8 else "")
+            + (" (packed-Q2 weights, group 128, bf16 activations)" if q2 else "")
+            + (" fused gate+up weight" if fused else "")
+            + (f" + LoRA rank {lora_rank} on gate, up, down" if lora_rank else "")
+            + (" [warm: one weight replica, cache-resident]" if warm else ""))
+
+
 def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=0, w8a8=False,
-                q2=False):
+                q2=False, warm=False):
     import torch
 
     import nvfp4_weight_dense_amd as nv
@@ -99,10 +135,11 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
     m, hidden = x.shape
     inter = wg.n
     wbytes = weight_bytes(wg) + weight_bytes(wu) + weight_bytes(wd)
-    nrep = max(1, math.ceil(REPLICA_BYTES / wbytes))
+    nrep = 1 if warm else max(1, math.ceil(REPLICA_BYTES / wbytes))
     xd = x.to(dev)
     out = torch.empty((m, hidden), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+    lp = None
     if lora_rank:
         # rank-r pairs on gate, up and down (small: shared by every replica)
         def pair(n, k, which, scale):
@@ -125,13 +162,12 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
         reps = _replicas((wg, wu, wd), nrep, dev)
         fn = nv.dense_ffn_forward_w4a4 if w4a4 else nv.dense_ffn_forward
     ms = _time_loop(lambda r: fn(xd, *r, out=out, stream=stream), reps, steps, warmup, stream)
+    # one more call on the first replica, kept for the oracle comparison
+    fn(xd, *reps[0], out=out, stream=stream)
+    torch.cuda.synchronize()
     flops = 6.0 * m * hidden * inter
     res = {
-        "workload": f"{name} m={m} hidden={hidden} inter={inter}" + (" w4a4" if w4a4 else "")
-                    + (" (block-scaled FP8 weights, per-row FP8 activations)" if w8a8 else "")
-                    + (" (packed-Q2 weights, group 128, bf16 activations)" if q2 else "")
-                    + (" fused gate+up weight" if fused else "")
-                    + (f" + LoRA rank {lora_rank} on gate, up, down" if lora_rank else ""),
+        "workload": _label(name, m, hidden, inter, w4a4, w8a8, q2, fused, lora_rank, warm),
         "m": m, "hidden": hidden, "inter": inter,
         "ms_per_step": ms,
         "tflops": flops / (ms * 1e-3) / 1e12,
@@ -141,7 +177,9 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
     }
     res["hbm_frac"] = res["weight_gbs"] / HBM_PEAK_GBS
     res["mfma_frac"] = res["tflops"] / (FP8_PEAK_TFLOPS if w8a8 else BF16_PEAK_TFLOPS)
-    ctx = dict(x=xd, weights=reps, out=out, stream=stream, wbytes=wbytes)
+    check = dict(name=name, x=x, weights=(wg, wu, wd), y=out.cpu(), w4a4=w4a4, w8a8=w8a8, q2=q2,
+                 lora=lora_rank, ms=ms, m=m)
+    ctx = dict(x=xd, weights=reps, out=out, stream=stream, wbytes=wbytes, check=check)
     return res, ctx
 
 
@@ -173,6 +211,38 @@ def measure_dominant_kernel(ctx, steps, warmup):
     }
 
 
+def measure_mfma_peak():
+    """Best of three runs of the register-only bf16 MFMA loop."""
+    import torch
+
+    import nvfp4_weight_dense_amd as nv
+
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs, iters = 2 * cus, 20000
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    nv.nvfp4_probe_mfma_bf16(wgs, 2000, sink, stream)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        nv.nvfp4_probe_mfma_bf16(wgs, iters, sink, stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        best = ms if best is None else min(best, ms)
+    flops = float(wgs) * 4 * iters * 4 * 32768
+    return {
+        "measured_tflops": flops / (best * 1e-3) / 1e12,
+        "spec_tflops": BF16_PEAK_TFLOPS,
+        "kernel": "v_mfma_f32_32x32x16_bf16, register operands, 4 independent chains per wave",
+        "workgroups": wgs, "waves_per_workgroup": 4, "iters": iters, "ms": best,
+    }
+
+
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in (DOMINANT_KERNEL_SRC,
@@ -199,39 +269,47 @@ def _traffic_per_launch():
         return None
 
 
+# launch patterns for the rocprofv3 counter passes: (workload, extra measure_ffn args)
+KERNEL_RUNS = {
+    "w4a4": ("w4a4", dict(m=1, w4a4=True)),
+    "w8a8": ("w8a8", dict(m=1, w8a8=True)),
+    "q2": ("decode", dict(m=1, q2=True)),
+    "smallm": ("smallm", {}),
+    "prefill": ("prefill", {}),
+    "w4a4_512": ("w4a4", dict(m=512, w4a4=True)),
+    "w8a8_512": ("w8a8", dict(m=512, w8a8=True)),
+    "q2_prefill": ("prefill", dict(q2=True)),
+}
+
+
 def traffic_run(steps, what="gemv"):
-    """Launch pattern for the rocprofv3 FETCH_SIZE / WRITE_SIZE passes: `steps`
-    launches of the dominant kernel over rotating cold replicas (what="gemv"),
-    or `steps` whole decode FFNs in the W4A4 or W8A8 ("w4a4", "w8a8": m=1,
-    hidden 4096, inter 14336) or packed-Q2 ("q2", m=1, hidden 4096, inter
-    12288) formats, then
-    `steps` plain device copies of COPY_BYTES, whose counter readings
-    calibrate the counters against a transfer of known size."""
+    """Launch pattern for the rocprofv3 counter passes: `steps` launches of
+    the dominant kernel over rotating cold replicas (what="gemv"), or
+    `steps` whole FFNs of one workload (KERNEL_RUNS), then `steps` plain
+    device copies of COPY_BYTES, whose counter readings calibrate the
+    counters against a transfer of known size."""
     import torch
 
     import nvfp4_weight_dense_amd as nv
 
     if what == "gemv":
         _, ctx = measure_ffn("decode", 1, 1)
-    elif what == "w4a4":
-        _, ctx = measure_ffn("w4a4", 1, 1, m=1, w4a4=True)
     else:
-        _, ctx = measure_ffn("w8a8" if what == "w8a8" else "decode", 1, 1, m=1,
-                             w8a8=what == "w8a8", q2=what == "q2")
-    xd, reps, stream = ctx["x"], ctx["weights"], ctx["stream"]
+        name, kw = KERNEL_RUNS[what]
+        _, ctx = measure_ffn(name, 1, 1, **kw)
+    xd, reps, stream, out = ctx["x"], ctx["weights"], ctx["stream"], ctx["out"]
+    chk = ctx["check"]
     act = torch.empty((xd.shape[0], reps[0][0].codes.shape[0]), dtype=torch.bfloat16,
                       device=xd.device)
-    out = ctx["out"]
+    fn = (nv.dense_ffn_forward_w8a8 if chk["w8a8"] else nv.dense_ffn_forward_q2 if chk["q2"]
+          else nv.dense_ffn_forward_w4a4 if chk["w4a4"] else nv.dense_ffn_forward)
+    torch.cuda.synchronize()
     for i in range(steps):
         r = reps[i % len(reps)]
         if what == "gemv":
             nv.nvfp4_gate_up_silu_w4a16(xd, r[0], r[1], act=act, stream=stream)
-        elif what == "w8a8":
-            nv.dense_ffn_forward_w8a8(xd, *r, out=out, stream=stream)
-        elif what == "w4a4":
-            nv.dense_ffn_forward_w4a4(xd, *r, out=out, stream=stream)
         else:
-            nv.dense_ffn_forward_q2(xd, *r, out=out, stream=stream)
+            fn(xd, *r, out=out, stream=stream)
     torch.cuda.synchronize()
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=xd.device)
     dst = torch.empty_like(src)
@@ -243,16 +321,94 @@ def traffic_run(steps, what="gemv"):
           flush=True)
 
 
-def cpu_baseline(seconds=10.0, threads=16):
+def _host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_count": os.cpu_count(), "usable_cores": usable, "model": model}
+
+
+def _oracle_weights(check):
+    import numpy as np
+    import torch
+
+    import oracle
+    wg, wu, wd = check["weights"]
+    if check["w8a8"]:
+        return [oracle.Fp8Weight(w.codes.numpy(), w.scales.numpy()) for w in (wg, wu, wd)]
+    if check["q2"]:
+        return [oracle.Q2Weight(w.codes.numpy(), w.scales.view(torch.int16).numpy().view(np.uint16),
+                                w.group) for w in (wg, wu, wd)]
+    return [oracle.Weight(w.codes.numpy(), w.scales.numpy(), w.ts) for w in (wg, wu, wd)]
+
+
+def oracle_check(check, threads, max_rows=2):
+    """The oracle on a few rows of one workload: its time per row scaled to
+    the workload's rows, and max |gpu - oracle| / rms(oracle) on those rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synthetic_inputs as si
+
+    m = check["m"]
+    rows = np.unique(np.array([0, m - 1][:max_rows]))
+    xb = check["x"].view(torch.int16).numpy().view(np.uint16)[rows]
+    ow = _oracle_weights(check)
+    t0 = time.perf_counter()
+    if check["w8a8"]:
+        _, ye = oracle.dense_ffn_w8a8(xb, *ow, nthreads=threads)
+    elif check["q2"]:
+        _, ye = oracle.dense_ffn_q2(xb, *ow, nthreads=threads)
+    elif check["lora"]:
+        wg, wu, wd = check["weights"]
+        inter, hidden = wg.n, wg.k
+        pairs = []
+        for n, k, which, scale in ((inter, hidden, 0, 2.0), (inter, hidden, 1, -1.5),
+                                   (hidden, inter, 2, 0.5)):
+            a, b = si.lora_pair(n, k, check["lora"], which=which)
+            pairs.append(oracle.Lora(a.view(torch.int16).numpy().view(np.uint16),
+                                     b.view(torch.int16).numpy().view(np.uint16), scale))
+        _, ye = oracle.dense_ffn_lora(xb, *ow, *pairs, nthreads=threads)
+    else:
+        _, ye = oracle.dense_ffn(xb, *ow, w4a4=check["w4a4"], nthreads=threads)
+    el = time.perf_counter() - t0
+    got = check["y"][rows].double().numpy()
+    rms = float(np.sqrt(np.mean(ye ** 2)))
+    err = float(np.max(np.abs(got - ye))) / max(rms, 1e-300)
+    est_s = el / len(rows) * m
+    return {
+        "oracle_rows": int(len(rows)),
+        "oracle_s_per_ffn_est": est_s,
+        "gpu_ms_per_ffn": check["ms"],
+        "speedup_vs_oracle": est_s / (check["ms"] * 1e-3),
+        "max_err_over_rms": err,
+        "within_2e-2": bool(err <= 2e-2),
+    }
+
+
+def cpu_baseline(seconds=10.0, threads=None):
     import numpy as np
 
     import oracle
     import synthetic_inputs as si
 
+    host = _host_cpu()
+    if threads is None:
+        threads = host["usable_cores"]
     x, wg, wu, wd = si.workload("decode")
     ow = [oracle.Weight(w.codes.numpy(), w.scales.numpy(), w.ts) for w in (wg, wu, wd)]
     xb = x.view(__import__("torch").int16).numpy().view(np.uint16)
-    threads = max(1, min(threads, os.cpu_count() or 1))
     wbytes = sum(weight_bytes(w) for w in (wg, wu, wd))
     reps = 0
     t0 = time.perf_counter()
@@ -266,26 +422,58 @@ def cpu_baseline(seconds=10.0, threads=16):
         "value": wbytes * reps / el / 1e9,
         "unit": "GB/s",
         "cores": threads,
+        "threads": threads,
+        "usable_cores": host["usable_cores"],
+        "cpu_count": host["cpu_count"],
+        "cpu_model": host["model"],
         "kind": "oracle",
-        "sample": f"{reps} full decode FFNs (m=1, hidden=4096, inter=12288) in {el:.1f} s",
+        "sample": f"{reps} full decode FFNs (m=1, hidden=4096, inter=12288) in {el:.1f} s "
+                  f"on {threads} threads",
         "ms_per_step": el / reps * 1e3,
     }
+
+
+WORKLOAD_TABLE = (
+    # name, steps divisor, w4a4, m, fused, lora rank, w8a8, q2, warm
+    ("decode", 1, False, None, False, 0, False, True, False),
+    ("smallm", 2, False, None, False, 0, False, True, False),
+    ("prefill", 20, False, None, False, 0, False, True, False),
+    ("decode", 1, False, None, True, 0, False, False, False),
+    ("decode", 1, False, None, False, 16, False, False, False),
+    ("smallm", 2, False, None, False, 0, False, False, False),
+    ("prefill", 20, False, None, False, 0, False, False, False),
+    ("decode", 1, False, None, False, 0, False, False, True),
+    ("smallm", 2, False, None, False, 0, False, False, True),
+    ("prefill", 20, False, None, False, 0, False, False, True),
+    ("decode_tp8", 1, False, None, False, 0, False, False, False),
+    ("prefill_tp8", 20, False, None, False, 0, False, False, False),
+    ("w4a4", 2, True, 1, False, 0, False, False, False),
+    ("w4a4", 2, True, 8, False, 0, False, False, False),
+    ("w4a4", 2, True, 64, False, 0, False, False, False),
+    ("w4a4", 20, True, 512, False, 0, False, False, False),
+    ("w8a8", 2, False, 1, False, 0, True, False, False),
+    ("w8a8", 2, False, 8, False, 0, True, False, False),
+    ("w8a8", 2, False, 64, False, 0, True, False, False),
+    ("w8a8", 20, False, 512, False, 0, True, False, False),
+)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=500,
-                    help="untimed calls before the timed ones (about 10 ms of decode work: "
-                         "kernels in the first ~40 ms of a process run slower)")
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed calls before the timed ones (each workload first runs "
+                         f"{RAMP_S} s of untimed calls for the GPU clock ramp)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true",
                     help="time only the decode workload (for profiling runs)")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated workload names to time besides the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--traffic-run", nargs="?", const="gemv", default=None,
-                    choices=("gemv", "w4a4", "w8a8", "q2"),
-                    help="only launch the dominant kernel (or a W8A8 / packed-Q2 decode FFN) "
+                    choices=("gemv",) + tuple(KERNEL_RUNS),
+                    help="only launch the dominant kernel (or whole FFNs of one workload) "
                          "and a calibration copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -306,40 +494,49 @@ def main():
         return
 
     head, ctx = measure_ffn("decode", args.steps, args.warmup)
+    checks = [(head, ctx["check"])]
     roof = measure_dominant_kernel(ctx, args.steps, args.warmup)
     del ctx
+    mfma = measure_mfma_peak()
     workloads = []
+    only = None if args.only is None else set(args.only.split(","))
+    invariance = {}
     if not args.only_headline:
-        for name, steps, w4a4, m, fused, rank, q2 in (
-                ("decode", args.steps, False, None, False, 0, True),
-                ("smallm", max(20, args.steps // 2), False, None, False, 0, True),
-                ("prefill", max(5, args.steps // 20), False, None, False, 0, True)):
-            r, c = measure_ffn(name, steps, max(3, args.warmup // 2), q2=q2)
+        for name, div, w4a4, m, fused, rank, w8a8, q2, warm in WORKLOAD_TABLE:
+            if only is not None and name not in only:
+                continue
+            steps = max(5 if div >= 20 else 20, args.steps // div)
+            r, c = measure_ffn(name, steps, args.warmup, w4a4=w4a4, m=m, fused=fused,
+                               lora_rank=rank, w8a8=w8a8, q2=q2, warm=warm)
+            if r["m"] >= 512 or name in ("prefill", "prefill_tp8"):
+                r["mfma_frac_measured_peak"] = r["tflops"] / mfma["measured_tflops"]
+            if w4a4 or w8a8:
+                invariance.setdefault("w4a4" if w4a4 else "w8a8", {})[r["m"]] = c["check"]["y"]
+            checks.append((r, c["check"]))
             del c
             torch.cuda.empty_cache()
             workloads.append(r)
-        for name, steps, w4a4, m, fused, rank in (
-                ("decode", args.steps, False, None, True, 0),
-                ("decode", args.steps, False, None, False, 16),
-                ("smallm", max(20, args.steps // 2), False, None, False, 0),
-                ("prefill", max(5, args.steps // 20), False, None, False, 0),
-                ("decode_tp8", args.steps, False, None, False, 0),
-                ("prefill_tp8", max(5, args.steps // 20), False, None, False, 0),
-                ("w4a4", max(20, args.steps // 2), True, 1, False, 0),
-                ("w4a4", max(20, args.steps // 2), True, 8, False, 0),
-                ("w4a4", max(20, args.steps // 2), True, 64, False, 0),
-                ("w4a4", max(5, args.steps // 20), True, 512, False, 0),
-                ("w8a8", max(20, args.steps // 2), False, 1, False, 0),
-                ("w8a8", max(20, args.steps // 2), False, 8, False, 0),
-                ("w8a8", max(20, args.steps // 2), False, 64, False, 0),
-                ("w8a8", max(5, args.steps // 20), False, 512, False, 0)):
-            r, c = measure_ffn(name, steps, max(3, args.warmup // 2), w4a4=w4a4, m=m, fused=fused,
-                               lora_rank=rank, w8a8=name == "w8a8")
-            del c
-            torch.cuda.empty_cache()
-            workloads.append(r)
+    # fixed formats: rows 0..m-1 at m < 512 equal the m = 512 run's rows bit for bit
+    for fmt, ys in invariance.items():
+        if 512 not in ys:
+            continue
+        for r in workloads:
+            fmt_of = "w4a4" if r["workload"].endswith("w4a4") else ("w8a8" if "FP8" in r["workload"]
+                                                                    else None)
+            if fmt_of == fmt and r["m"] < 512:
+                r["rows_bit_identical_to_m512"] = bool(torch.equal(
+                    ys[r["m"]].view(torch.int16), ys[512][: r["m"]].view(torch.int16)))
     nv.nvfp4_release()
-    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args.cpu_seconds)
+        per = []
+        for r, chk in checks:
+            rows = 1 if chk["m"] == 1 else 2
+            entry = {"workload": r["workload"]}
+            entry.update(oracle_check(chk, cpu["threads"], max_rows=rows))
+            per.append(entry)
+        cpu["per_config"] = per
 
     line = {
         "metric": "dense FFN TFLOP/s + weight HBM GB/s (% roofline) at m=1/64/2048, 1 MI355X",
@@ -360,10 +557,12 @@ def main():
             "weights": "NVFP4 (E2M1 + E4M3/16 + fp32 tensor scale)",
             "accumulate": "fp32",
             "cold_weight_replicas": head["replicas"],
+            "ramp_s_before_warmup": RAMP_S,
         },
         "tflops": head["tflops"],
         "hbm_frac": head["hbm_frac"],
         "roofline": roof,
+        "mfma_peak": mfma,
         "cpu_baseline": cpu,
         "workloads": workloads,
     }

@@ -89,7 +89,10 @@ int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w,
                     void *y, void *stream);
 
 /* Per-row NVFP4 activation quantizer (the activation half of the W4A4
- * projection).  x: bf16 [m][k], k % 32 == 0.  Outputs: codes uint8
+ * projection: page layers/dense_ffn_fixed.rs, module doc and the W4A4 arm
+ * of `forward_fixed`, where the projection takes the bf16 input and
+ * quantizes it to NVFP4 itself; the pages give no recipe, so the one below
+ * is this library's reading).  x: bf16 [m][k], k % 32 == 0.  Outputs: codes uint8
  * [m][k/2] (packing as in nvfp4_weight), scales uint8 [m][k/16] (E4M3FN),
  * row_scale fp32 [m].  Per row, in fp32 with IEEE rounding:
  *   s_row = amax/2688 (1 for an all-zero row);
@@ -202,8 +205,8 @@ int dense_ffn_forward_lora(const void *x, int32_t m, int32_t hidden,
  * The other fixed activation format of the pages (page
  * layers/dense_ffn_fixed.rs, `Fixed::W8a8`: the declared W8A8 layer, per-row
  * FP8 activations at every row count) on block-scaled FP8 weights (page
- * layers/dense_ffn_overlays.rs, `set_fp8_weights`: "native block-scaled FP8"
- * weights with a scale grid).  The pages fix neither the block shape nor the
+ * layers/dense_ffn_overlays.rs, `set_fp8_weights`: FP8 weights that carry
+ * their own per-block scale grid).  The pages fix neither the block shape nor the
  * activation recipe; the readings taken here: one fp32 scale per 128 x 128
  * weight block, and one fp32 scale per activation row with amax mapped to
  * 448, the largest E4M3 magnitude. */
@@ -232,9 +235,11 @@ int fp8_quantize_rows(const void *x, int32_t m, int32_t k, uint8_t *codes,
 /* W8A8 projection: x is quantized per row (fp8_quantize_rows), then
  * y[r][c] = bf16( s_row[r] * sum_b scales[c/128][b] *
  *                 sum_{k in block b} e4m3(xq[r][k]) * e4m3(wq[c][k]) ),
- * fp32 accumulation, FP8 matrix cores.  Row r's bits are the same for
- * every m: one kernel and one K order (fixed by n and k) serve every row
- * count.  x: bf16 [m][k]; y: bf16 [m][n]. */
+ * fp32 accumulation.  Both E4M3 operands are converted exactly to fp16 and
+ * multiplied on the f16 matrix cores (exact products; gfx950's FP8 matrix
+ * forms drop low-order products inside a group, so they are not used).
+ * Row r's bits are the same for every m: one kernel and one K order (fixed
+ * by n and k) serve every row count.  x: bf16 [m][k]; y: bf16 [m][n]. */
 int fp8_gemm_w8a8(const void *x, int32_t m, const fp8_weight *w, void *y,
                   void *stream);
 
@@ -281,12 +286,32 @@ int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden,
                          const q2_weight *wu, const q2_weight *wd, void *out,
                          void *stream);
 
-/* The calling thread's last error message ("" if none). */
+/* The calling thread's last error message ("" if none).  The pages' ops
+ * return an error value whose message names the failed check (page
+ * layers/dense_ffn_fixed.rs, the `ensure!`/`bail!` checks of
+ * `forward_fixed`); a C caller gets the status code from the call and the
+ * message from here.  The string stays valid until the thread's next
+ * call into the library. */
 const char *nvfp4_last_error(void);
 
-/* Frees the scratch arena of every device.  The caller must have
- * synchronized all streams that used the library. */
+/* Frees the scratch arena of every device (and the packed-Q2 library
+ * handles).  The pages keep per-layer scratch buffers for the FFN's
+ * intermediates (page layers/dense_ffn_fixed.rs, the scratch buffers of
+ * `forward_fixed`); here they are one arena per device, which this call
+ * gives back.  The caller must have synchronized all streams that used the
+ * library; the next call grows the arena again. */
 void nvfp4_release(void);
+
+/* Measurement aid, not a step of the FFN: enqueues `workgroups` workgroups
+ * of four waves, each wave running iters x 4 independent
+ * v_mfma_f32_32x32x16_bf16 on register operands (32768 flops each, so
+ * workgroups * 4 * iters * 4 * 32768 flops in all).  Timing it with events
+ * gives the bf16 matrix throughput the part reaches, which benchmarks print
+ * beside the specification's peak.  sink: device fp32 [256], never written
+ * in practice (it keeps the loop from being optimized away).  NVFP4_EINVAL
+ * for a null sink or a non-positive count. */
+int nvfp4_probe_mfma_bf16(int32_t workgroups, int32_t iters, float *sink,
+                          void *stream);
 
 /* ABI version of this header (bumped on incompatible change). */
 int32_t nvfp4_abi_version(void);

@@ -39,6 +39,7 @@ __all__ = [
     "dense_ffn_forward_lora", "FP8Weight", "fp8_quantize_rows", "fp8_gemm_w8a8",
     "dense_ffn_forward_w8a8", "Q2Weight", "q2_gemm_w2a16", "dense_ffn_forward_q2",
     "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
+    "nvfp4_probe_mfma_bf16",
 ]
 
 
@@ -163,6 +164,8 @@ def load_library(path: str = LIB_PATH):
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    L.nvfp4_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    L.nvfp4_probe_mfma_bf16.restype = ctypes.c_int
     L.nvfp4_last_error.argtypes = []
     L.nvfp4_last_error.restype = ctypes.c_char_p
     L.nvfp4_release.argtypes = []
@@ -192,12 +195,34 @@ def _check(rc: int):
         raise Nvfp4Error(rc, nvfp4_last_error())
 
 
-def _act(t: torch.Tensor, name: str) -> torch.Tensor:
-    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+def _act(t: torch.Tensor, name: str, k: int | None = None) -> torch.Tensor:
+    """A bf16 [rows, cols] activation; with k, cols must equal k."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2 \
+            or not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous 2-D bfloat16 tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name}: expected a GPU tensor")
+    if k is not None and t.shape[1] != k:
+        raise ValueError(f"{name}: has {t.shape[1]} columns, the weight has k={k}")
     return t
+
+
+def _out(t: torch.Tensor | None, m: int, n: int, like: torch.Tensor, name: str) -> torch.Tensor:
+    """A caller's bf16 [m, n] output (checked), or a new one on like's device."""
+    if t is None:
+        return torch.empty((m, n), dtype=torch.bfloat16, device=like.device)
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2 \
+            or tuple(t.shape) != (m, n) or not t.is_contiguous():
+        got = tuple(t.shape) if isinstance(t, torch.Tensor) else type(t).__name__
+        raise ValueError(f"{name}: expected a contiguous bfloat16 [{m}, {n}] tensor, got {got}")
+    return t
+
+
+def _gpu(first: torch.Tensor, *rest):
+    """Every tensor on the GPU, on first's device (checked after the shapes)."""
+    if not first.is_cuda:
+        raise ValueError("expected GPU tensors")
+    for t in rest:
+        if t is not None and t.device != first.device:
+            raise ValueError(f"tensors on {t.device} and {first.device}: expected one device")
 
 
 def _cweight(w) -> _CWeight:
@@ -206,10 +231,18 @@ def _cweight(w) -> _CWeight:
     if ts is None:
         ts = w.ts
     for t, nm in ((codes, "codes"), (scales, "scales")):
-        if t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"weight {nm}: expected a contiguous uint8 GPU tensor")
+        if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"weight {nm}: expected a contiguous 2-D uint8 tensor")
     n, half_k = codes.shape
+    if tuple(scales.shape) != (n, (2 * half_k) // 16):
+        raise ValueError(f"weight scales: expected [n={n}, k/16={(2 * half_k) // 16}], "
+                         f"got {tuple(scales.shape)}")
     return _CWeight(codes.data_ptr(), scales.data_ptr(), float(ts), int(n), int(half_k * 2))
+
+
+def _wt(w):
+    """The weight's tensors (for the device check)."""
+    return (w.codes, w.scales)
 
 
 # ---- C ABI, same names --------------------------------------------------------
@@ -226,13 +259,23 @@ def nvfp4_release() -> None:
     load_library().nvfp4_release()
 
 
+def nvfp4_probe_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue the register-only bf16 MFMA loop (a measurement aid):
+    workgroups * 4 * iters * 4 * 32768 flops; sink is a float32 GPU tensor of
+    at least 256 elements."""
+    L = load_library()
+    if sink.dtype != torch.float32 or sink.numel() < 256 or not sink.is_cuda:
+        raise ValueError("sink: expected a float32 GPU tensor of at least 256 elements")
+    _check(L.nvfp4_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _stream(stream)))
+
+
 def nvfp4_gemm_w4a16(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
     """y = bf16(x . W^T); x [m, k] bf16 -> y [m, n] bf16."""
     L = load_library()
-    x = _act(x, "x")
     cw = _cweight(w)
-    if y is None:
-        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    x = _act(x, "x", cw.k)
+    y = _out(y, x.shape[0], cw.n, x, "y")
+    _gpu(x, y, *_wt(w))
     _check(L.nvfp4_gemm_w4a16(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
     return y
 
@@ -240,10 +283,10 @@ def nvfp4_gemm_w4a16(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=N
 def nvfp4_gemm_w4a4(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
     """W4A4 projection: x quantized per row to NVFP4, then x_q . W^T."""
     L = load_library()
-    x = _act(x, "x")
     cw = _cweight(w)
-    if y is None:
-        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    x = _act(x, "x", cw.k)
+    y = _out(y, x.shape[0], cw.n, x, "y")
+    _gpu(x, y, *_wt(w))
     _check(L.nvfp4_gemm_w4a4(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
     return y
 
@@ -252,6 +295,7 @@ def nvfp4_quantize_rows(x: torch.Tensor, stream=None):
     """Per-row NVFP4 quantizer -> (codes [m, k/2], scales [m, k/16], row_scale [m])."""
     L = load_library()
     x = _act(x, "x")
+    _gpu(x)
     m, k = x.shape
     codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
@@ -264,12 +308,17 @@ def nvfp4_quantize_rows(x: torch.Tensor, stream=None):
 def silu_mul(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None, stream=None):
     """out = bf16(silu(gate) * up); out may be gate."""
     L = load_library()
-    if gate.shape != up.shape or gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
-        raise ValueError("silu_mul: gate and up must be bf16 tensors of one shape")
-    if not (gate.is_contiguous() and up.is_contiguous() and gate.is_cuda and up.is_cuda):
-        raise ValueError("silu_mul: expected contiguous GPU tensors")
+    for t, nm in ((gate, "gate"), (up, "up")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"silu_mul: {nm} must be a contiguous bf16 tensor")
+    if gate.shape != up.shape:
+        raise ValueError("silu_mul: gate and up must have one shape")
     if out is None:
         out = torch.empty_like(gate)
+    elif not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16 or \
+            out.shape != gate.shape or not out.is_contiguous():
+        raise ValueError("silu_mul: out must be a contiguous bf16 tensor of gate's shape")
+    _gpu(gate, up, out)
     _check(L.silu_mul(_ptr(gate), _ptr(up), _ptr(out), gate.numel(), _stream(stream)))
     return out
 
@@ -278,22 +327,33 @@ def nvfp4_gate_up_silu_w4a16(x: torch.Tensor, wg, wu, act: torch.Tensor | None =
                              stream=None):
     """act = bf16(silu(bf16(x.Wg^T)) * bf16(x.Wu^T))."""
     L = load_library()
-    x = _act(x, "x")
     cg, cu = _cweight(wg), _cweight(wu)
-    if act is None:
-        act = torch.empty((x.shape[0], cg.n), dtype=torch.bfloat16, device=x.device)
+    if (cg.n, cg.k) != (cu.n, cu.k):
+        raise ValueError(f"wg [{cg.n}, {cg.k}] and wu [{cu.n}, {cu.k}] differ")
+    x = _act(x, "x", cg.k)
+    act = _out(act, x.shape[0], cg.n, x, "act")
+    _gpu(x, act, *_wt(wg), *_wt(wu))
     _check(L.nvfp4_gate_up_silu_w4a16(_ptr(x), x.shape[0], ctypes.byref(cg), ctypes.byref(cu),
                                       _ptr(act), _stream(stream)))
     return act
 
 
+def _ffn_shapes(x, g, u, d, out):
+    """Check x [m, hidden], wg/wu [inter, hidden], wd [hidden, inter] and out
+    [m, hidden]; returns (x, out, m, hidden, inter)."""
+    inter, hidden = g
+    if u != (inter, hidden) or d != (hidden, inter):
+        raise ValueError(f"wg {list(g)}, wu {list(u)}, wd {list(d)}: expected wg/wu "
+                         f"[inter, hidden] and wd [hidden, inter]")
+    x = _act(x, "x", hidden)
+    out = _out(out, x.shape[0], hidden, x, "out")
+    return x, out, x.shape[0], hidden, inter
+
+
 def _ffn(fn, x, wg, wu, wd, out, stream):
-    x = _act(x, "x")
     cg, cu, cd = _cweight(wg), _cweight(wu), _cweight(wd)
-    m, hidden = x.shape
-    inter = cg.n
-    if out is None:
-        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
+    x, out, m, hidden, inter = _ffn_shapes(x, (cg.n, cg.k), (cu.n, cu.k), (cd.n, cd.k), out)
+    _gpu(x, out, *_wt(wg), *_wt(wu), *_wt(wd))
     _check(fn(_ptr(x), m, hidden, inter, ctypes.byref(cg), ctypes.byref(cu), ctypes.byref(cd),
               _ptr(out), _stream(stream)))
     return out
@@ -331,26 +391,34 @@ def dense_ffn_forward_fused(x: torch.Tensor, wgu, wd, out: torch.Tensor | None =
                             stream=None):
     """W4A16 dense SwiGLU FFN on a fused gate+up weight [2*inter, hidden]."""
     L = load_library()
-    x = _act(x, "x")
     cgu, cd = _cweight(wgu), _cweight(wd)
-    m, hidden = x.shape
+    if cgu.n % 2:
+        raise ValueError(f"wgu: {cgu.n} rows, expected 2*inter")
     inter = cgu.n // 2
-    if out is None:
-        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
+    x, out, m, hidden, _ = _ffn_shapes(x, (inter, cgu.k), (inter, cgu.k), (cd.n, cd.k), out)
+    _gpu(x, out, *_wt(wgu), *_wt(wd))
     _check(L.dense_ffn_forward_fused(_ptr(x), m, hidden, inter, ctypes.byref(cgu), ctypes.byref(cd),
                                      _ptr(out), _stream(stream)))
     return out
 
 
-def _clora_pair(p: LoraPair | None) -> _CLoraPair:
+def _clora_pair(p: LoraPair | None, k: int, n: int, name: str) -> _CLoraPair:
+    """A LoRA pair for a delta on an [m, n] output from a [m, k] input."""
     if p is None:
         return _CLoraPair(None, None, 0, 0.0)
     for t, nm in ((p.a, "a"), (p.b, "b")):
-        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"lora {nm}: expected a contiguous 2-D bfloat16 GPU tensor")
-    if p.a.shape[0] != p.b.shape[1]:
-        raise ValueError("lora: a is [rank, k] and b is [n, rank]")
-    return _CLoraPair(p.a.data_ptr(), p.b.data_ptr(), int(p.a.shape[0]), float(p.scale))
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2 \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} {nm}: expected a contiguous 2-D bfloat16 tensor")
+    r = p.a.shape[0]
+    if tuple(p.a.shape) != (r, k) or tuple(p.b.shape) != (n, r):
+        raise ValueError(f"{name}: a is [rank, k={k}] and b is [n={n}, rank], got a "
+                         f"{list(p.a.shape)} and b {list(p.b.shape)}")
+    return _CLoraPair(p.a.data_ptr(), p.b.data_ptr(), int(r), float(p.scale))
+
+
+def _lora_t(p: LoraPair | None):
+    return () if p is None else (p.a, p.b)
 
 
 def nvfp4_lora_delta(x: torch.Tensor, pair: LoraPair, base: torch.Tensor, stream=None):
@@ -358,8 +426,14 @@ def nvfp4_lora_delta(x: torch.Tensor, pair: LoraPair, base: torch.Tensor, stream
     L = load_library()
     x = _act(x, "x")
     base = _act(base, "base")
-    cp = _clora_pair(pair)
-    _check(L.nvfp4_lora_delta(_ptr(x), x.shape[0], x.shape[1], ctypes.byref(cp), base.shape[1],
+    m, k = x.shape
+    if base.shape[0] != m:
+        raise ValueError(f"base: {base.shape[0]} rows, x has {m}")
+    if pair is None:
+        raise ValueError("lora_delta: pair is None")
+    cp = _clora_pair(pair, k, base.shape[1], "lora pair")
+    _gpu(x, base, *_lora_t(pair))
+    _check(L.nvfp4_lora_delta(_ptr(x), m, k, ctypes.byref(cp), base.shape[1],
                               _ptr(base), _stream(stream)))
     return base
 
@@ -369,13 +443,12 @@ def dense_ffn_forward_lora(x: torch.Tensor, wg, wu, wd, gate: LoraPair | None = 
                            out: torch.Tensor | None = None, stream=None):
     """W4A16 dense SwiGLU FFN with a LoRA overlay on gate, up and down."""
     L = load_library()
-    x = _act(x, "x")
     cg, cu, cd = _cweight(wg), _cweight(wu), _cweight(wd)
-    m, hidden = x.shape
-    if out is None:
-        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
-    cl = _CLora(_clora_pair(gate), _clora_pair(up), _clora_pair(down))
-    _check(L.dense_ffn_forward_lora(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
+    x, out, m, hidden, inter = _ffn_shapes(x, (cg.n, cg.k), (cu.n, cu.k), (cd.n, cd.k), out)
+    cl = _CLora(_clora_pair(gate, hidden, inter, "lora gate"), _clora_pair(up, hidden, inter, "lora up"),
+                _clora_pair(down, inter, hidden, "lora down"))
+    _gpu(x, out, *_wt(wg), *_wt(wu), *_wt(wd), *_lora_t(gate), *_lora_t(up), *_lora_t(down))
+    _check(L.dense_ffn_forward_lora(_ptr(x), m, hidden, inter, ctypes.byref(cg), ctypes.byref(cu),
                                     ctypes.byref(cd), ctypes.byref(cl), _ptr(out), _stream(stream)))
     return out
 
@@ -383,10 +456,10 @@ def dense_ffn_forward_lora(x: torch.Tensor, wg, wu, wd, gate: LoraPair | None = 
 # ---- W8A8 fixed format ----------------------------------------------------------
 
 def _cfp8(w) -> _CFp8Weight:
-    if w.codes.dtype != torch.uint8 or not w.codes.is_contiguous() or not w.codes.is_cuda:
-        raise ValueError("fp8 weight codes: expected a contiguous uint8 GPU tensor")
-    if w.scales.dtype != torch.float32 or not w.scales.is_contiguous() or not w.scales.is_cuda:
-        raise ValueError("fp8 weight scales: expected a contiguous float32 GPU tensor")
+    if w.codes.dtype != torch.uint8 or w.codes.dim() != 2 or not w.codes.is_contiguous():
+        raise ValueError("fp8 weight codes: expected a contiguous 2-D uint8 tensor")
+    if w.scales.dtype != torch.float32 or not w.scales.is_contiguous():
+        raise ValueError("fp8 weight scales: expected a contiguous float32 tensor")
     n, k = w.codes.shape
     if tuple(w.scales.shape) != ((n + 127) // 128, (k + 127) // 128):
         raise ValueError("fp8 weight scales: expected [ceil(n/128), ceil(k/128)]")
@@ -397,6 +470,7 @@ def fp8_quantize_rows(x: torch.Tensor, stream=None):
     """Per-row FP8 quantizer -> (codes uint8 [m, k] E4M3, row_scale float32 [m])."""
     L = load_library()
     x = _act(x, "x")
+    _gpu(x)
     m, k = x.shape
     codes = torch.empty((m, k), dtype=torch.uint8, device=x.device)
     rs = torch.empty((m,), dtype=torch.float32, device=x.device)
@@ -407,10 +481,10 @@ def fp8_quantize_rows(x: torch.Tensor, stream=None):
 def fp8_gemm_w8a8(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
     """W8A8 projection: x quantized per row to FP8, then x_q . W^T (block-scaled W)."""
     L = load_library()
-    x = _act(x, "x")
     cw = _cfp8(w)
-    if y is None:
-        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    x = _act(x, "x", cw.k)
+    y = _out(y, x.shape[0], cw.n, x, "y")
+    _gpu(x, y, *_wt(w))
     _check(L.fp8_gemm_w8a8(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
     return y
 
@@ -419,12 +493,10 @@ def dense_ffn_forward_w8a8(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None
                            stream=None):
     """Fixed-format W8A8 FFN (FP8 activations per row, block-scaled FP8 weights)."""
     L = load_library()
-    x = _act(x, "x")
     cg, cu, cd = _cfp8(wg), _cfp8(wu), _cfp8(wd)
-    m, hidden = x.shape
-    if out is None:
-        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
-    _check(L.dense_ffn_forward_w8a8(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
+    x, out, m, hidden, inter = _ffn_shapes(x, (cg.n, cg.k), (cu.n, cu.k), (cd.n, cd.k), out)
+    _gpu(x, out, *_wt(wg), *_wt(wu), *_wt(wd))
+    _check(L.dense_ffn_forward_w8a8(_ptr(x), m, hidden, inter, ctypes.byref(cg), ctypes.byref(cu),
                                     ctypes.byref(cd), _ptr(out), _stream(stream)))
     return out
 
@@ -432,12 +504,12 @@ def dense_ffn_forward_w8a8(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None
 # ---- packed-Q2 weights ------------------------------------------------------------
 
 def _cq2(w) -> _CQ2Weight:
-    if w.codes.dtype != torch.uint8 or not w.codes.is_contiguous() or not w.codes.is_cuda:
-        raise ValueError("q2 weight codes: expected a contiguous uint8 GPU tensor")
-    if w.scales.element_size() != 2 or not w.scales.is_contiguous() or not w.scales.is_cuda:
-        raise ValueError("q2 weight scales: expected a contiguous 16-bit GPU tensor of fp16 bits")
+    if w.codes.dtype != torch.uint8 or w.codes.dim() != 2 or not w.codes.is_contiguous():
+        raise ValueError("q2 weight codes: expected a contiguous 2-D uint8 tensor")
+    if w.scales.element_size() != 2 or not w.scales.is_contiguous():
+        raise ValueError("q2 weight scales: expected a contiguous 16-bit tensor of fp16 bits")
     n, k4 = w.codes.shape
-    if tuple(w.scales.shape) != (n, (4 * k4) // int(w.group)):
+    if int(w.group) <= 0 or tuple(w.scales.shape) != (n, (4 * k4) // int(w.group)):
         raise ValueError("q2 weight scales: expected [n, k/group]")
     return _CQ2Weight(w.codes.data_ptr(), w.scales.data_ptr(), int(w.group), int(n), int(4 * k4))
 
@@ -445,10 +517,10 @@ def _cq2(w) -> _CQ2Weight:
 def q2_gemm_w2a16(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):
     """y = bf16(x . W^T) with W = bf16((q - 2) * d) from a packed-Q2 weight."""
     L = load_library()
-    x = _act(x, "x")
     cw = _cq2(w)
-    if y is None:
-        y = torch.empty((x.shape[0], cw.n), dtype=torch.bfloat16, device=x.device)
+    x = _act(x, "x", cw.k)
+    y = _out(y, x.shape[0], cw.n, x, "y")
+    _gpu(x, y, *_wt(w))
     _check(L.q2_gemm_w2a16(_ptr(x), x.shape[0], ctypes.byref(cw), _ptr(y), _stream(stream)))
     return y
 
@@ -457,11 +529,9 @@ def dense_ffn_forward_q2(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None =
                          stream=None):
     """Dense SwiGLU FFN on packed-Q2 weights (bf16 activations)."""
     L = load_library()
-    x = _act(x, "x")
     cg, cu, cd = _cq2(wg), _cq2(wu), _cq2(wd)
-    m, hidden = x.shape
-    if out is None:
-        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=x.device)
-    _check(L.dense_ffn_forward_q2(_ptr(x), m, hidden, cg.n, ctypes.byref(cg), ctypes.byref(cu),
+    x, out, m, hidden, inter = _ffn_shapes(x, (cg.n, cg.k), (cu.n, cu.k), (cd.n, cd.k), out)
+    _gpu(x, out, *_wt(wg), *_wt(wu), *_wt(wd))
+    _check(L.dense_ffn_forward_q2(_ptr(x), m, hidden, inter, ctypes.byref(cg), ctypes.byref(cu),
                                   ctypes.byref(cd), _ptr(out), _stream(stream)))
     return out

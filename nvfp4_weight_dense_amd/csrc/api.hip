@@ -81,6 +81,7 @@ struct Config {
   bool profile = false;
   bool log = false;
   size_t arena_cap = 0;  // 0: no cap
+  int splitk_min_k = 0;  // 0: K may be split at any length
 };
 
 const Config &cfg() {
@@ -95,6 +96,7 @@ const Config &cfg() {
     if (const char *v = getenv("NVFP4_PROFILE")) c.profile = !strcmp(v, "1");
     if (const char *v = getenv("NVFP4_LOG")) c.log = !strcmp(v, "1");
     if (const char *v = getenv("NVFP4_ARENA_MAX_BYTES")) c.arena_cap = strtoull(v, nullptr, 10);
+    if (const char *v = getenv("NVFP4_SPLITK_MIN_K")) c.splitk_min_k = atoi(v);
     return c;
   }();
   return c;
@@ -275,8 +277,24 @@ size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
   return 0;  // many-row kernel: no scratch
 }
 
+// split-K arrival counters a projection needs (zero on entry, left zero)
+size_t proj_counter_words(int m, int n, int k, int nmat, Path path) {
+  if (path == Path::Small) {
+    const SmallPlan pl = smallm_plan(m, n, k, nmat);
+    return pl.ksplit > 1 ? (size_t)pl.tiles : 0;
+  }
+  if (path == Path::StreamLds) {
+    const LdsPlan pl = stream_lds_plan(m, n, k, nmat);
+    return pl.ksplit > 1 ? stream_lds_counter_words(pl) : 0;
+  }
+  if (path == Path::Stream) return stream_counter_words(stream_plan(n, k), m);
+  return 0;
+}
+
+// `counters`: null to take them from the library's counter buffer, else a
+// caller region of at least proj_counter_words(...) zero words
 int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, void *y,
-             void *scratch, Path path, hipStream_t s) {
+             void *scratch, Path path, hipStream_t s, unsigned *counters_in = nullptr) {
   if (path == Path::Gemv)
     return hip_status(launch_gemv(a.x_bf16, m, k, n, nmat, w, y, s), "gemv projection launch");
   if (path == Path::Prefill)
@@ -284,8 +302,8 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
                       "many-row projection launch");
   if (path == Path::Small) {
     SmallPlan pl = smallm_plan(m, n, k, nmat);
-    unsigned *counters = nullptr;
-    if (pl.ksplit > 1) {
+    unsigned *counters = counters_in;
+    if (pl.ksplit > 1 && !counters) {
       int rc = counters_get((size_t)pl.tiles, &counters);
       if (rc) return rc;
     }
@@ -294,8 +312,8 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
   }
   if (path == Path::StreamLds) {
     LdsPlan pl = stream_lds_plan(m, n, k, nmat);
-    unsigned *counters = nullptr;
-    if (pl.ksplit > 1) {
+    unsigned *counters = counters_in;
+    if (pl.ksplit > 1 && !counters) {
       int rc = counters_get(stream_lds_counter_words(pl), &counters);
       if (rc) return rc;
     }
@@ -304,9 +322,11 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
   }
   if (path == Path::Stream) {
     StreamPlan pl = stream_plan(n, k);
-    unsigned *counters = nullptr;
-    int rc = counters_get(stream_counter_words(pl, m), &counters);
-    if (rc) return rc;
+    unsigned *counters = counters_in;
+    if (!counters) {
+      int rc = counters_get(stream_counter_words(pl, m), &counters);
+      if (rc) return rc;
+    }
     return hip_status(launch_stream(a, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),
                       "weight-streaming projection launch");
   }
@@ -479,11 +499,21 @@ int run_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2Mat
 
 }  // namespace
 
+// (declared in launchers.h: the plans of the split-K kernels read it)
+int nvfp4::splitk_min_k() { return cfg().splitk_min_k; }
+
 // ---- C ABI ---------------------------------------------------------------------------
 
 extern "C" {
 
 int32_t nvfp4_abi_version(void) { return 1; }
+
+int nvfp4_probe_mfma_bf16(int32_t workgroups, int32_t iters, float *sink, void *stream) {
+  g_err.clear();
+  if (workgroups <= 0 || iters <= 0) return fail(NVFP4_EINVAL, "probe: workgroups and iters must be positive");
+  if (!sink) return fail(NVFP4_EINVAL, "probe: null sink");
+  return hip_status(launch_mfma_probe(workgroups, iters, sink, (hipStream_t)stream), "probe launch");
+}
 
 const char *nvfp4_last_error(void) { return g_err.c_str(); }
 

@@ -243,7 +243,20 @@ QuantShape quant_shape(int m, int k) {
   return q;
 }
 
+// words[i] = 0 for i < count (a plain store kernel: safe to record in a
+// graph, unlike a memset node)
+__global__ __launch_bounds__(256) void k_zero_words(unsigned *__restrict__ words, int count) {
+  const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (i < count) words[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_words(unsigned *words, int count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_words, dim3((count + 255) / 256), dim3(256), 0, stream, words, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes, float *row_scale,
                                     hipStream_t stream) {

@@ -396,6 +396,7 @@ SmallPlan smallm_plan(int m, int n, int k, int nmat) {
   const int slots = 3 * 256;
   int ksplit = std::max(1, slots / pl.tiles);
   ksplit = std::min(ksplit, std::max(1, nsteps / 8));
+  if (k < splitk_min_k()) ksplit = 1;
   pl.steps_per_split = cdiv(cdiv(nsteps, ksplit), kGroup) * kGroup;
   pl.ksplit = cdiv(nsteps, pl.steps_per_split);
   (void)m;

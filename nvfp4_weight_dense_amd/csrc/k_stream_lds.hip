@@ -308,6 +308,7 @@ LdsPlan stream_lds_plan(int m, int n, int k, int nmat) {
   const int cap = nsteps / 4 > 0 ? nsteps / 4 : 1;  // at least four steps per split
   if (ksplit > cap) ksplit = cap;
   if (ksplit < 1) ksplit = 1;
+  if (k < splitk_min_k()) ksplit = 1;
   pl.steps_per_split = cdiv(nsteps, ksplit);
   pl.ksplit = cdiv(nsteps, pl.steps_per_split);
   pl.rotate = pl.row_blocks == 1;

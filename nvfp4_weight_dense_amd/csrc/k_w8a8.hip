@@ -341,6 +341,7 @@ StreamPlan w8a8_plan(int n, int k) {
     if (ksplit < 1) ksplit = 1;
   }
   StreamPlan pl;
+  if (k < splitk_min_k()) ksplit = 1;
   pl.steps_per_split = cdiv(nsteps, ksplit);
   pl.ksplit = cdiv(nsteps, pl.steps_per_split);
   pl.tiles = tiles;

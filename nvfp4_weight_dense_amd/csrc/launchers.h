@@ -28,6 +28,12 @@ struct ActRef {
 // `partial` must hold stream_partial_floats(...) floats and `counters`
 // stream_counter_words(...) words that are zero on entry (the kernel leaves
 // them zero).  The plan depends on (n, k) only.
+// Reduction length below which no projection splits K over workgroups
+// (NVFP4_SPLITK_MIN_K, read once; 0 = split wherever the plan wants).
+// Every split plan below honours it; it depends on k only, so the W4A4 and
+// W8A8 plans still depend on (n, k) only.
+int splitk_min_k();
+
 struct StreamPlan {
   int ksplit;           // workgroups along K
   int steps_per_split;  // 128-element K steps per split
@@ -43,8 +49,9 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat,
 
 // LDS-shared projection (bf16 activations): a workgroup owns 32*mt rows
 // and 128 columns; its four waves share each 64-element activation chunk
-// through LDS.  Serves 17..64 rows (mt 1 or 2, one row block) and the
-// many-row regime (mt 8).  Partial/counter rules as above, with
+// through LDS.  Serves projections whose k is not a multiple of 64 (the
+// LDS-DMA kernels need whole 64-K steps): 17..64 rows (mt 1 or 2, one row
+// block) and more rows (mt 8, 256-row blocks).  Partial/counter rules as above, with
 // stream_lds_counter_words(...) counters.
 struct LdsPlan {
   int mt;               // 32-row tiles per workgroup
@@ -144,6 +151,9 @@ hipError_t launch_gemv(const void *x, int m, int k, int n, int nmat,
                        const MatRef *w, void *y, hipStream_t stream,
                        const GemvLora *lora = nullptr);
 
+// words[0..count) = 0 with a store kernel on `stream`.
+hipError_t launch_zero_words(unsigned *words, int count, hipStream_t stream);
+
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out,
                            int64_t count, hipStream_t stream);
 
@@ -195,5 +205,10 @@ hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat,
                        const Fp8MatRef *w, void *y, float *partial,
                        unsigned *counters, const StreamPlan &pl,
                        hipStream_t stream);
+
+// Register-only bf16 MFMA loop (a measurement aid): `workgroups` groups of
+// four waves, each wave iters x 4 v_mfma_f32_32x32x16_bf16.  sink: 256
+// floats, never written in practice.
+hipError_t launch_mfma_probe(int workgroups, int iters, float *sink, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -228,3 +228,64 @@ def test_binding_refuses_cpu_tensors():
     w = nv.NVFP4Weight(torch.zeros((8, 32), dtype=torch.uint8), torch.zeros((8, 4), dtype=torch.uint8))
     with pytest.raises(ValueError):
         nv.nvfp4_gemm_w4a16(x, w)
+
+
+def _match(fn, *a, msg, **kw):
+    with pytest.raises(ValueError, match=msg):
+        fn(*a, **kw)
+
+
+def test_binding_checks_shapes_before_any_launch():
+    """Every shape the C ABI cannot see (tensor extents behind raw pointers)
+    is checked by the binding and raises ValueError before the library is
+    called.  CPU tensors: the shape checks run before the device check, so
+    a wrong shape is reported as such."""
+    import torch
+    _lib()
+    bf = torch.bfloat16
+    u8 = torch.uint8
+    W = lambda n, k, sk=None: nv.NVFP4Weight(torch.zeros((n, k // 2), dtype=u8),
+                                             torch.zeros((n, sk if sk is not None else k // 16), dtype=u8))
+    x = torch.zeros((2, 64), dtype=bf)
+    # scales not [n, k/16]
+    _match(nv.nvfp4_gemm_w4a16, x, W(8, 64, sk=3), msg="weight scales")
+    # x columns != weight k
+    _match(nv.nvfp4_gemm_w4a16, x, W(8, 128), msg="columns")
+    _match(nv.nvfp4_gemm_w4a4, x, W(8, 128), msg="columns")
+    # caller's output of the wrong shape, dtype or layout
+    _match(nv.nvfp4_gemm_w4a16, x, W(8, 64), y=torch.zeros((2, 9), dtype=bf), msg=r"\[2, 8\]")
+    _match(nv.nvfp4_gemm_w4a16, x, W(8, 64), y=torch.zeros((2, 8), dtype=torch.float32), msg="y:")
+    _match(nv.nvfp4_gemm_w4a16, x, W(8, 64), y=torch.zeros((8, 2), dtype=bf).t(), msg="y:")
+    # gate+up: weights of different shapes, act of the wrong shape
+    _match(nv.nvfp4_gate_up_silu_w4a16, x, W(8, 64), W(16, 64), msg="differ")
+    _match(nv.nvfp4_gate_up_silu_w4a16, x, W(8, 64), W(8, 64), act=torch.zeros((3, 8), dtype=bf),
+           msg="act:")
+    # FFN: wd not [hidden, inter], out of the wrong shape
+    for fn in (nv.dense_ffn_forward, nv.dense_ffn_forward_w4a4):
+        _match(fn, x, W(96, 64), W(96, 64), W(96, 64), msg="wd")
+        _match(fn, x, W(96, 64), W(96, 64), W(64, 96), out=torch.zeros((2, 96), dtype=bf),
+               msg="out:")
+        _match(fn, torch.zeros((2, 32), dtype=bf), W(96, 64), W(96, 64), W(64, 96), msg="columns")
+    # fused gate+up weight: odd rows, wd mismatch
+    _match(nv.dense_ffn_forward_fused, x, W(97, 64), W(64, 48), msg="2\\*inter")
+    _match(nv.dense_ffn_forward_fused, x, W(96, 64), W(64, 96), msg="wd")
+    # LoRA: a not [rank, k], b not [n, rank], base rows != x rows
+    P = lambda r, k, n: nv.LoraPair(torch.zeros((r, k), dtype=bf), torch.zeros((n, r), dtype=bf))
+    base = torch.zeros((2, 8), dtype=bf)
+    _match(nv.nvfp4_lora_delta, x, P(16, 32, 8), base, msg="lora pair")
+    _match(nv.nvfp4_lora_delta, x, P(16, 64, 9), base, msg="lora pair")
+    _match(nv.nvfp4_lora_delta, x, P(16, 64, 8), torch.zeros((3, 8), dtype=bf), msg="base")
+    _match(nv.dense_ffn_forward_lora, x, W(96, 64), W(96, 64), W(64, 96), down=P(16, 64, 64),
+           msg="lora down")
+    # W8A8 and packed Q2: x columns and output shapes
+    f8 = nv.FP8Weight(torch.zeros((8, 128), dtype=u8), torch.zeros((1, 1), dtype=torch.float32))
+    _match(nv.fp8_gemm_w8a8, x, f8, msg="columns")
+    q2 = nv.Q2Weight(torch.zeros((8, 32), dtype=u8), torch.zeros((8, 1), dtype=torch.int16), 128)
+    _match(nv.q2_gemm_w2a16, x, q2, msg="columns")
+    _match(nv.q2_gemm_w2a16, torch.zeros((2, 128), dtype=bf), q2,
+           y=torch.zeros((2, 7), dtype=bf), msg="y:")
+    # silu_mul: out of another shape
+    g = torch.zeros((2, 8), dtype=bf)
+    _match(nv.silu_mul, g, g, out=torch.zeros((2, 9), dtype=bf), msg="out")
+    # shapes right, tensors on the CPU: refused as well
+    _match(nv.nvfp4_gemm_w4a16, x, W(8, 64), msg="GPU")

@@ -53,13 +53,19 @@ def test_dense_ffn_w4a16_row_counts(m):
     assert_close(bits(y), ye, f"ffn tiny m={m}")
 
 
-@pytest.mark.parametrize("name,m,nrows", [("tiny", 4, 4), ("w4a4", 64, 4), ("w4a4", 512, 4)])
+def _block_rows(m, block=64):
+    """The first and last row of every `block`-row block."""
+    return np.array(sorted({r for b in range(0, m, block) for r in (b, min(m, b + block) - 1)}))
+
+
+@pytest.mark.parametrize("name,m,nrows", [("tiny", 4, 4), ("w4a4", 64, 4), ("w4a4", 512, None)])
 def test_dense_ffn_w4a4_matches_oracle(name, m, nrows):
     _say(f"ffn w4a4 {name} m={m}")
     x, wg, wu, wd = si.workload(name, m=m)
     y = nv.dense_ffn_forward_w4a4(x.cuda(), g_weight(wg), g_weight(wu), g_weight(wd))
     sync()
-    rows = _rows(m, nrows, seed=2)
+    # m = 512: one row at each end of every 64-row block
+    rows = _block_rows(m) if nrows is None else _rows(m, nrows, seed=2)
     _, ye = oracle.dense_ffn(bits(x)[rows], o_weight(wg), o_weight(wu), o_weight(wd), w4a4=True)
     assert_close(bits(y)[rows], ye, f"ffn w4a4 {name} m={m}")
 

@@ -61,7 +61,7 @@ SHAPES = [
     # ring), and k % 64 != 0 (LDS-shared activations)
     (40, 70, 2176), (20, 64, 160), (64, 48, 96),
     (65, 130, 1024), (130, 300, 416), (257, 129, 96), (200, 64, 2048),
-    # many-row kernel with tiles split over workgroups by K steps (stream-K)
+    # many-row kernel with several tile rounds per persistent workgroup
     (600, 520, 2048), (300, 1000, 1024),
     # many-row kernel with k % 256 != 0: a partial last weight group of 1, 2
     # or 3 steps, scale rows only 4-byte aligned
@@ -259,7 +259,64 @@ def test_rows_beyond_m_untouched_and_errors_leave_output():
     assert torch.all(out[m:] == 7.0)
     before = out.clone()
     bad = nv.NVFP4Weight(g_weight(wd).codes, g_weight(wd).scales, 1.0)  # transposed role
-    with pytest.raises(nv.Nvfp4Error):
+    # the binding refuses it before calling the library ...
+    with pytest.raises(ValueError):
         nv.dense_ffn_forward(x.cuda(), g_weight(wg), bad, g_weight(wd), out=out[:m])
+    # ... and so does the C ABI itself, before enqueuing anything
+    import ctypes
+    L = nv.load_library()
+    xd = x.cuda()
+    cg, cb, cd = nv._cweight(g_weight(wg)), nv._cweight(bad), nv._cweight(g_weight(wd))
+    rc = L.dense_ffn_forward(ctypes.c_void_p(xd.data_ptr()), m, hidden, cg.n, ctypes.byref(cg),
+                             ctypes.byref(cb), ctypes.byref(cd), ctypes.c_void_p(out.data_ptr()),
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == nv.NVFP4_ESHAPE
     sync()
     assert torch.equal(out, before)
+
+
+# ---- every row of the many-row kernel -----------------------------------------------------------
+
+def _spread_cols(n, count, tail, seed):
+    """`count` columns spread over [0, n) plus `tail` from the last 1024
+    (where the many-row kernel's second column launch works) and n - 1."""
+    rng = np.random.default_rng(seed)
+    cols = set(rng.choice(n, count, replace=False).tolist())
+    cols |= set(rng.choice(np.arange(max(0, n - 1024), n), tail, replace=False).tolist())
+    cols |= {0, n - 1}
+    return np.array(sorted(cols))
+
+
+@pytest.mark.parametrize("name,m,n,k", [("prefill down", 2048, 5120, 17408),
+                                        ("prefill gate", 2048, 17408, 5120)])
+def test_exact_case_every_row_many_row_kernel(name, m, n, k):
+    """All 2048 rows (every row tile, the partial last row block included)
+    for columns of every column range, bit for bit on exact inputs."""
+    _say(f"exact case, every row: {name}")
+    x, w = si.exact_case(m, n, k, seed=4)
+    y = nv.nvfp4_gemm_w4a16(x.cuda(), g_weight(w))
+    sync()
+    cols = _spread_cols(n, 48, 16, seed=6)
+    yo, _ = oracle.gemm_w4a16(bits(x), o_weight(w, cols))
+    assert np.array_equal(bits(y)[:, cols], yo)
+
+
+def test_exact_case_every_row_gate_up_silu_many_rows():
+    """The fused gate+up+silu launch at the prefill shape: every row, and
+    columns of both of its column launches.  gate and up are exact, so act
+    must be the silu_mul of the oracle's gate and up within one bf16 ulp."""
+    m, hidden, inter = 2048, 5120, 17408
+    _say("exact case, every row: prefill gate+up+silu")
+    x, wg = si.exact_case(m, inter, hidden, seed=7)
+    _, wu = si.exact_case(1, inter, hidden, seed=8)
+    act = nv.nvfp4_gate_up_silu_w4a16(x.cuda(), g_weight(wg), g_weight(wu))
+    sync()
+    cols = _spread_cols(inter, 40, 24, seed=9)
+    go, _ = oracle.gemm_w4a16(bits(x), o_weight(wg, cols))
+    uo, _ = oracle.gemm_w4a16(bits(x), o_weight(wu, cols))
+    ref = oracle.silu_mul(go, uo)
+    got = bits(act)[:, cols]
+    d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    same_sign = (got & 0x8000) == (ref & 0x8000)
+    zero_pair = ((got & 0x7FFF) == 0) & ((ref & 0x7FFF) <= 1)
+    assert np.all((same_sign & (d <= 1)) | zero_pair)

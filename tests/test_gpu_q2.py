@@ -109,8 +109,8 @@ def test_q2_m_zero_and_errors_touch_nothing():
     x, wg, wu, wd = si.q2_workload("tiny", m=4)
     out = torch.full((4, 256), 7.0, dtype=torch.bfloat16, device="cuda")
     nv.dense_ffn_forward_q2(x[:0].cuda(), gq(wg), gq(wu), gq(wd), out=out[:0])
-    with pytest.raises(nv.Nvfp4Error):
-        nv.dense_ffn_forward_q2(x.cuda(), gq(wg), gq(wu), gq(wg), out=out)  # wd has the wrong shape
+    with pytest.raises(ValueError):
+        nv.dense_ffn_forward_q2(x.cuda(), gq(wg), gq(wu), gq(wg), out=out)  # wd's shape: refused by the binding
     bad = si.Q2Weight(wg.codes, wg.scales[:, :1].contiguous(), 256)  # group 256 on hidden 256: fine shape,
     with pytest.raises(nv.Nvfp4Error):                              # but gate and up groups differ
         nv.dense_ffn_forward_q2(x.cuda(), gq(bad), gq(wu), gq(wd), out=out)
