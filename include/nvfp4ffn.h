@@ -125,6 +125,23 @@ int dense_ffn_forward(const void *x, int32_t m, int32_t hidden, int32_t inter,
                       const nvfp4_weight *wg, const nvfp4_weight *wu,
                       const nvfp4_weight *wd, void *out, void *stream);
 
+/* dense_ffn_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, the same kernels and the same result
+ * bits, but act, the split-K partials and the arrival counters live in a
+ * fixed 32 MiB device array of the library (one copy per GPU, held until
+ * the process ends) instead of the arena.  The call itself allocates
+ * nothing.  The first call on a device looks up that array's address and
+ * clears its counter region with a kernel on `stream`.  Every call on a
+ * GPU shares the array: calls that overlap on one GPU (other streams,
+ * other threads) race.  A shape whose scratch exceeds the array (e.g.
+ * m * inter * 2 bytes of act beyond about 30 MiB) returns NVFP4_ENOMEM
+ * before anything is enqueued; other errors as dense_ffn_forward. */
+int dense_ffn_forward_noalloc(const void *x, int32_t m, int32_t hidden,
+                              int32_t inter, const nvfp4_weight *wg,
+                              const nvfp4_weight *wu, const nvfp4_weight *wd,
+                              void *out, void *stream);
+
 /* Dense SwiGLU FFN, fixed-format W4A4: x and act are quantized per row to
  * NVFP4 before each projection; row r's output bits do not depend on m
  * (page layers/dense_ffn_fixed.rs, `forward_fixed`, W4A4 arm). */

@@ -34,6 +34,7 @@ NVFP4_EHIP = -4
 __all__ = [
     "NVFP4Weight", "Nvfp4Error", "Nvfp4LibraryMissing",
     "nvfp4_gemm_w4a16", "nvfp4_gemm_w4a4", "nvfp4_quantize_rows", "silu_mul",
+    "dense_ffn_forward_noalloc",
     "nvfp4_gate_up_silu_w4a16", "dense_ffn_forward", "dense_ffn_forward_w4a4",
     "nvfp4_gate_up_views", "dense_ffn_forward_fused", "LoraPair", "nvfp4_lora_delta",
     "dense_ffn_forward_lora", "FP8Weight", "fp8_quantize_rows", "fp8_gemm_w8a8",
@@ -148,6 +149,7 @@ def load_library(path: str = LIB_PATH):
         "nvfp4_gate_up_silu_w4a16": [vp, i32, wp, wp, vp, vp],
         "dense_ffn_forward": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
         "dense_ffn_forward_w4a4": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
+        "dense_ffn_forward_noalloc": [vp, i32, i32, i32, wp, wp, wp, vp, vp],
         "nvfp4_gate_up_views": [wp, wp, wp],
         "dense_ffn_forward_fused": [vp, i32, i32, i32, wp, wp, vp, vp],
         "nvfp4_lora_delta": [vp, i32, i32, ctypes.POINTER(_CLoraPair), i32, vp, vp],
@@ -368,6 +370,15 @@ def dense_ffn_forward_w4a4(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None
                            stream=None):
     """Fixed-format W4A4 FFN (activations quantized per row before each projection)."""
     return _ffn(load_library().dense_ffn_forward_w4a4, x, wg, wu, wd, out, stream)
+
+
+def dense_ffn_forward_noalloc(x: torch.Tensor, wg, wu, wd, out: torch.Tensor | None = None,
+                              stream=None):
+    """dense_ffn_forward with the library's fixed device scratch instead of its
+    arena: the C call allocates nothing (out, when not given, is allocated
+    here by torch).  Shapes whose scratch does not fit raise Nvfp4Error
+    (NVFP4_ENOMEM)."""
+    return _ffn(load_library().dense_ffn_forward_noalloc, x, wg, wu, wd, out, stream)
 
 
 def nvfp4_gate_up_views(fused) -> tuple[NVFP4Weight, NVFP4Weight]:

@@ -41,6 +41,18 @@
 
 using namespace nvfp4;
 
+// ---- fixed device scratch of the allocation-free FFN ------------------------------
+// For callers that cannot allocate (graph capture, tight serving loops):
+// act, split-K partials and arrival counters of dense_ffn_forward_noalloc
+// live in this array, one copy per GPU, held until the process ends.  In
+// host code the name is only a stand-in for the symbol; the device address
+// comes from hipGetSymbolAddress, once per device (noalloc_scratch below),
+// and only that address is passed to kernels.  Calls that overlap on one
+// GPU share it and race.
+static constexpr size_t kNoAllocBytes = (size_t)32 << 20;
+static constexpr size_t kNoAllocCounterBytes = (size_t)64 << 10;  // first 64 KB: counters
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -497,6 +509,37 @@ int run_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2Mat
                     "packed-Q2 projection launch");
 }
 
+struct NoAllocDev {
+  bool ready = false;
+  void *ptr = nullptr;
+};
+std::mutex g_noalloc_mu;
+NoAllocDev g_noalloc[kMaxDevices];
+
+// This device's copy of `scratch`; on first use the symbol's address is
+// looked up and the counter region cleared (by a store kernel on `s`, so a
+// capture records no memset node).  Kernels leave the counters at zero.
+int noalloc_scratch(hipStream_t s, void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  NoAllocDev &d = g_noalloc[dev];
+  if (!d.ready) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(NVFP4_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    int rc = hip_status(launch_zero_words((unsigned *)ptr, (int)(kNoAllocCounterBytes / 4), s),
+                        "scratch counter clear");
+    if (rc) return rc;
+    d.ptr = ptr;
+    d.ready = true;
+  }
+  *out = d.ptr;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 // (declared in launchers.h: the plans of the split-K kernels read it)
@@ -635,6 +678,44 @@ int dense_ffn_forward(const void *x, int32_t m, int32_t hidden, int32_t inter,
   if ((rc = run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, hidden, inter, 2, w2, act, scr, p_up, s)))
     return rc;
   return run_proj(ActRef{act, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &wdm, out, scr, p_down, s);
+}
+
+int dense_ffn_forward_noalloc(const void *x, int32_t m, int32_t hidden, int32_t inter,
+                              const nvfp4_weight *wg, const nvfp4_weight *wu,
+                              const nvfp4_weight *wd, void *out, void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_ffn(x, m, hidden, inter, wg, wu, wd, out))) return rc;
+  if (m == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Path p_up, p_down;
+  if ((rc = path_or_fail(m, hidden, &p_up)) || (rc = path_or_fail(m, inter, &p_down))) return rc;
+  const size_t act_b = align256((size_t)2 * m * inter);
+  const size_t scr_b = std::max(proj_scratch_bytes(m, inter, hidden, 2, p_up),
+                                proj_scratch_bytes(m, hidden, inter, 1, p_down));
+  const size_t words = std::max(proj_counter_words(m, inter, hidden, 2, p_up),
+                                proj_counter_words(m, hidden, inter, 1, p_down));
+  const size_t need = kNoAllocCounterBytes + act_b + scr_b;
+  if (need > kNoAllocBytes || words * 4 > kNoAllocCounterBytes)
+    return fail(NVFP4_ENOMEM,
+                "dense_ffn_forward_noalloc: m=%d hidden=%d inter=%d needs %zu bytes of scratch "
+                "(%zu counter words); the fixed scratch holds %zu bytes (%zu words)",
+                m, hidden, inter, need, words, kNoAllocBytes, kNoAllocCounterBytes / 4);
+  log_path("dense_ffn_forward_noalloc gate+up", path_name(p_up), m, inter, hidden);
+  log_path("dense_ffn_forward_noalloc down", path_name(p_down), m, hidden, inter);
+  void *base = nullptr;
+  if ((rc = noalloc_scratch(s, &base))) return rc;
+  unsigned *counters = (unsigned *)base;
+  char *act = (char *)base + kNoAllocCounterBytes;
+  char *scr = act + act_b;
+  ProfileScope ps("dense_total noalloc", m, s);
+  MatRef w2[2] = {mat(wg), mat(wu)};
+  MatRef wdm = mat(wd);
+  if ((rc = run_proj(ActRef{x, nullptr, nullptr, nullptr}, m, hidden, inter, 2, w2, act, scr, p_up, s,
+                     counters)))
+    return rc;
+  return run_proj(ActRef{act, nullptr, nullptr, nullptr}, m, inter, hidden, 1, &wdm, out, scr, p_down, s,
+                  counters);
 }
 
 int nvfp4_gate_up_views(const nvfp4_weight *fused, nvfp4_weight *gate, nvfp4_weight *up) {
