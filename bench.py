@@ -123,7 +123,7 @@ def _label(name, m, hidden, inter, w4a4=False, w8a8=False, q2=False, fused=False
 
 
 def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=0, w8a8=False,
-                q2=False, warm=False):
+                q2=False, warm=False, ramp_s=RAMP_S):
     import torch
 
     import nvfp4_weight_dense_amd as nv
@@ -161,7 +161,8 @@ def measure_ffn(name, steps, warmup, w4a4=False, m=None, fused=False, lora_rank=
     else:
         reps = _replicas((wg, wu, wd), nrep, dev)
         fn = nv.dense_ffn_forward_w4a4 if w4a4 else nv.dense_ffn_forward
-    ms = _time_loop(lambda r: fn(xd, *r, out=out, stream=stream), reps, steps, warmup, stream)
+    ms = _time_loop(lambda r: fn(xd, *r, out=out, stream=stream), reps, steps, warmup, stream,
+                    ramp_s=ramp_s)
     # one more call on the first replica, kept for the oracle comparison
     fn(xd, *reps[0], out=out, stream=stream)
     torch.cuda.synchronize()
@@ -279,39 +280,49 @@ KERNEL_RUNS = {
     "w4a4_512": ("w4a4", dict(m=512, w4a4=True)),
     "w8a8_512": ("w8a8", dict(m=512, w8a8=True)),
     "q2_prefill": ("prefill", dict(q2=True)),
+    "q2_smallm": ("smallm", dict(q2=True)),
 }
 
 
 def traffic_run(steps, what="gemv"):
     """Launch pattern for the rocprofv3 counter passes: `steps` launches of
-    the dominant kernel over rotating cold replicas (what="gemv"), or
-    `steps` whole FFNs of one workload (KERNEL_RUNS), then `steps` plain
-    device copies of COPY_BYTES, whose counter readings calibrate the
-    counters against a transfer of known size."""
+    the dominant kernel over rotating cold replicas (what="gemv"), `steps`
+    whole FFNs of one workload (KERNEL_RUNS), or `steps` runs of the MFMA
+    probe (what="probe"); then `steps` plain device copies of COPY_BYTES,
+    whose counter readings calibrate the memory counters against a
+    transfer of known size.  No clock ramp: every dispatch is counted."""
     import torch
 
     import nvfp4_weight_dense_amd as nv
 
-    if what == "gemv":
-        _, ctx = measure_ffn("decode", 1, 1)
+    dev = torch.device("cuda:0")
+    if what == "probe":
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        sink = torch.zeros(256, dtype=torch.float32, device=dev)
+        for _ in range(steps):
+            nv.nvfp4_probe_mfma_bf16(2 * cus, 2000, sink)
+        torch.cuda.synchronize()
     else:
-        name, kw = KERNEL_RUNS[what]
-        _, ctx = measure_ffn(name, 1, 1, **kw)
-    xd, reps, stream, out = ctx["x"], ctx["weights"], ctx["stream"], ctx["out"]
-    chk = ctx["check"]
-    act = torch.empty((xd.shape[0], reps[0][0].codes.shape[0]), dtype=torch.bfloat16,
-                      device=xd.device)
-    fn = (nv.dense_ffn_forward_w8a8 if chk["w8a8"] else nv.dense_ffn_forward_q2 if chk["q2"]
-          else nv.dense_ffn_forward_w4a4 if chk["w4a4"] else nv.dense_ffn_forward)
-    torch.cuda.synchronize()
-    for i in range(steps):
-        r = reps[i % len(reps)]
         if what == "gemv":
-            nv.nvfp4_gate_up_silu_w4a16(xd, r[0], r[1], act=act, stream=stream)
+            _, ctx = measure_ffn("decode", 1, 0, ramp_s=0.0)
         else:
-            fn(xd, *r, out=out, stream=stream)
-    torch.cuda.synchronize()
-    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=xd.device)
+            name, kw = KERNEL_RUNS[what]
+            _, ctx = measure_ffn(name, 1, 0, ramp_s=0.0, **kw)
+        xd, reps, stream, out = ctx["x"], ctx["weights"], ctx["stream"], ctx["out"]
+        chk = ctx["check"]
+        act = torch.empty((xd.shape[0], reps[0][0].codes.shape[0]), dtype=torch.bfloat16,
+                          device=xd.device)
+        fn = (nv.dense_ffn_forward_w8a8 if chk["w8a8"] else nv.dense_ffn_forward_q2 if chk["q2"]
+              else nv.dense_ffn_forward_w4a4 if chk["w4a4"] else nv.dense_ffn_forward)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            r = reps[i % len(reps)]
+            if what == "gemv":
+                nv.nvfp4_gate_up_silu_w4a16(xd, r[0], r[1], act=act, stream=stream)
+            else:
+                fn(xd, *r, out=out, stream=stream)
+        torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(steps):
         dst.copy_(src)
@@ -472,7 +483,7 @@ def main():
                     help="comma-separated workload names to time besides the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--traffic-run", nargs="?", const="gemv", default=None,
-                    choices=("gemv",) + tuple(KERNEL_RUNS),
+                    choices=("gemv", "probe") + tuple(KERNEL_RUNS),
                     help="only launch the dominant kernel (or whole FFNs of one workload) "
                          "and a calibration copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()

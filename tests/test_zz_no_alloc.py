@@ -47,10 +47,10 @@ def test_noalloc_matches_dense_ffn_forward(calls):
 
 def test_noalloc_refuses_a_shape_beyond_its_scratch():
     _say("noalloc refusal")
-    x, wg, wu, wd = si.workload("prefill", m=1024)   # act alone is 34 MiB
+    x, wg, wu, wd = si.workload("prefill")   # m = 2048: act alone is 68 MiB
     xd = x.cuda()
     W = [g_weight(w) for w in (wg, wu, wd)]
-    out = torch.full((1024, 5120), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((2048, 5120), 7.0, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.dense_ffn_forward_noalloc(xd, *W, out=out)
     assert e.value.code == nv.NVFP4_ENOMEM
