@@ -38,10 +38,7 @@
  * Scratch: intermediates and split-K partials live in a per-device arena
  *   owned by the library (grown on first use of a larger shape, freed by
  *   nvfp4_release).  Calls that may run concurrently on different streams
- *   of one device race on it; calls on one stream are ordered.  The
- *   packed-Q2 calls above 64 rows also use one rocBLAS handle per device
- *   (created on first use, destroyed by nvfp4_release), which may allocate
- *   its own workspace.
+ *   of one device race on it; calls on one stream are ordered.
  */
 #ifndef NVFP4FFN_H
 #define NVFP4FFN_H
@@ -295,9 +292,11 @@ int q2_gemm_w2a16(const void *x, int32_t m, const q2_weight *w, void *y,
                   void *stream);
 
 /* Dense SwiGLU FFN on packed-Q2 weights: gate, up and silu_mul in one
- * launch, then down (page layers/dense_ffn_prefill.rs, `prefill_q2`).
- * wg, wu: [inter][hidden]; wd: [hidden][inter].  Errors as
- * dense_ffn_forward. */
+ * launch, then down (page layers/dense_ffn_prefill.rs, `prefill_q2`), at
+ * every row count: up to 64 rows the weight-streaming kernel, more rows the
+ * many-row kernel (the streaming kernel in 64-row blocks when hidden or
+ * inter is not a multiple of 64).  wg, wu: [inter][hidden]; wd:
+ * [hidden][inter].  Errors as dense_ffn_forward. */
 int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden,
                          int32_t inter, const q2_weight *wg,
                          const q2_weight *wu, const q2_weight *wd, void *out,
@@ -311,8 +310,7 @@ int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden,
  * call into the library. */
 const char *nvfp4_last_error(void);
 
-/* Frees the scratch arena of every device (and the packed-Q2 library
- * handles).  The pages keep per-layer scratch buffers for the FFN's
+/* Frees the scratch arena of every device.  The pages keep per-layer scratch buffers for the FFN's
  * intermediates (page layers/dense_ffn_fixed.rs, the scratch buffers of
  * `forward_fixed`); here they are one arena per device, which this call
  * gives back.  The caller must have synchronized all streams that used the

@@ -16,8 +16,9 @@
 //          layers/dense_ffn_fixed.rs, `Fixed::W8a8`).
 //   Q2:    packed-Q2 weights, bf16 activations (page layers/dense_ffn_prefill.rs,
 //          `prefill_q2`): up to NVFP4_SMALLM_MAX_M rows the weight-streaming
-//          kernel (gate+up+silu fused, then down); more rows dequantize each
-//          weight to bf16 and run a rocBLAS bf16 GEMM, silu_mul over gate.
+//          kernel, more rows the many-row kernel when k % 64 == 0 (gate+up+
+//          silu fused, then down; the weights dequantized in registers, never
+//          copied to bf16), else the streaming kernel with 64-row blocks.
 // Every check runs before the first launch; a forced path that cannot serve a
 // shape is an error, never a silent fallback (the pages refuse to start with
 // a requested but missing variant: page layers/mod.rs, `w4a16_v2_kernel`).
@@ -32,8 +33,6 @@
 #include <set>
 #include <string>
 #include <tuple>
-
-#include <rocblas/rocblas.h>
 
 #include "launchers.h"
 #include "nvfp4_common.h"
@@ -459,45 +458,12 @@ size_t q2_scratch_bytes(int m, int n, int k, int nmat) {
   return align256(4 * q2_partial_floats(q2_plan(m, n, k), nmat, m, n));
 }
 
-// ---- many rows on packed-Q2 weights: dequantize to bf16, then a library GEMM ------
-// (page layers/dense_ffn_prefill.rs, `prefill_q2`: the default leg dequantizes
-// each projection to BF16 into one shared scratch and runs the BF16 GEMM; the
-// projections run in order on the stream, so one scratch serves all three).
-// One rocBLAS handle per device, created on first use; calls on a device are
-// serialized by a mutex because the handle's stream is per call.
-std::mutex g_blas_mu;
-rocblas_handle g_blas[kMaxDevices];
+// ---- many rows on packed-Q2 weights: the many-row kernel --------------------------
+// (page layers/dense_ffn_prefill.rs, `prefill_q2`: the default leg runs a BF16
+// GEMM on the dequantized weight; here the many-row kernel dequantizes each
+// weight fragment in registers, so no bf16 copy of the weight exists).
+bool q2_tiled(int m, int k) { return m > cfg().smallm_max_m && k % 64 == 0; }
 
-int blas_gemm_bf16(const void *x, int m, int k, const void *wbf16, int n, void *y, hipStream_t s) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return fail(NVFP4_EHIP, "hipGetDevice failed");
-  std::lock_guard<std::mutex> lk(g_blas_mu);
-  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
-    g_blas[dev] = nullptr;
-    return fail(NVFP4_EHIP, "rocblas_create_handle failed");
-  }
-  rocblas_handle h = g_blas[dev];
-  if (rocblas_set_stream(h, s) != rocblas_status_success) return fail(NVFP4_EHIP, "rocblas_set_stream failed");
-  // row-major y[m][n] = x[m][k] . W[n][k]^T is column-major y^T = W^T' x^T':
-  // A = W seen as column-major [k][n] (transposed), B = x as column-major [k][m]
-  const float alpha = 1.0f, beta = 0.0f;
-  const rocblas_status st = rocblas_gemm_ex(
-      h, rocblas_operation_transpose, rocblas_operation_none, n, m, k, &alpha, wbf16,
-      rocblas_datatype_bf16_r, k, x, rocblas_datatype_bf16_r, k, &beta, y, rocblas_datatype_bf16_r, n, y,
-      rocblas_datatype_bf16_r, n, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  if (st != rocblas_status_success) return fail(NVFP4_EHIP, "rocblas_gemm_ex failed (status %d)", (int)st);
-  return NVFP4_OK;
-}
-
-int q2_gemm_many_rows(const void *x, int m, int k, int n, int gshift, const Q2MatRef &w, void *y,
-                      void *wbf16, hipStream_t s) {
-  int rc;
-  if ((rc = hip_status(launch_dequant_q2_bf16(w, n, k, gshift, wbf16, s), "Q2 dequant launch"))) return rc;
-  return blas_gemm_bf16(x, m, k, wbf16, n, y, s);
-}
-
-bool q2_many_rows(int m) { return m > cfg().smallm_max_m; }
 
 int run_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w, void *y,
            void *scratch, hipStream_t s) {
@@ -561,18 +527,6 @@ int nvfp4_probe_mfma_bf16(int32_t workgroups, int32_t iters, float *sink, void *
 const char *nvfp4_last_error(void) { return g_err.c_str(); }
 
 void nvfp4_release(void) {
-  {
-    std::lock_guard<std::mutex> lb(g_blas_mu);
-    int cur = 0;
-    (void)hipGetDevice(&cur);
-    for (int d = 0; d < kMaxDevices; ++d)
-      if (g_blas[d]) {
-        (void)hipSetDevice(d);
-        (void)rocblas_destroy_handle(g_blas[d]);
-        g_blas[d] = nullptr;
-      }
-    (void)hipSetDevice(cur);
-  }
   std::lock_guard<std::mutex> lk(g_arena_mu);
   int cur = 0;
   (void)hipGetDevice(&cur);
@@ -997,12 +951,11 @@ int q2_gemm_w2a16(const void *x, int32_t m, const q2_weight *w, void *y, void *s
   if (m == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
   Q2MatRef wm = q2_mat(w);
-  if (q2_many_rows(m)) {
-    log_path("gemm_q2", "dequant+gemm", m, w->n, w->k);
-    void *wb = nullptr;
-    if ((rc = arena_get(align256((size_t)2 * w->n * w->k), &wb))) return rc;
+  if (q2_tiled(m, w->k)) {
+    log_path("gemm_q2", "prefill", m, w->n, w->k);
     ProfileScope ps("gemm_q2", m, s);
-    return q2_gemm_many_rows(x, m, w->k, w->n, gs, wm, y, wb, s);
+    return hip_status(launch_prefill_q2(x, m, w->k, w->n, gs, 1, &wm, y, prefill_plan(m, w->n, w->k, 1), s),
+                      "packed-Q2 many-row projection launch");
   }
   log_path("gemm_q2", "q2", m, w->n, w->k);
   const size_t part = q2_scratch_bytes(m, w->n, w->k, 1);
@@ -1033,21 +986,31 @@ int dense_ffn_forward_q2(const void *x, int32_t m, int32_t hidden, int32_t inter
   if (m == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
   Q2MatRef mg = q2_mat(wg), mu = q2_mat(wu), md = q2_mat(wd);
-  if (q2_many_rows(m)) {
-    // gate and up into [m][inter] bf16 buffers, silu_mul over gate, down;
-    // one bf16 weight scratch shared by the three projections in turn
-    log_path("dense_ffn_forward_q2", "dequant+gemm", m, inter, hidden);
-    const size_t gu_b = align256((size_t)2 * m * inter);
-    const size_t wb_b = align256((size_t)2 * inter * hidden);
+  const bool up_tiled = q2_tiled(m, hidden), down_tiled = q2_tiled(m, inter);
+  if (up_tiled || down_tiled) {
+    // gate+up+silu in one launch, then down; the many-row kernel where
+    // k % 64 == 0, else the streaming kernel with 64-row blocks
+    log_path("dense_ffn_forward_q2 gate+up", up_tiled ? "prefill" : "q2", m, inter, hidden);
+    log_path("dense_ffn_forward_q2 down", down_tiled ? "prefill" : "q2", m, hidden, inter);
+    const size_t act_b = align256((size_t)2 * m * inter);
+    const size_t part = std::max(up_tiled ? 0 : q2_scratch_bytes(m, inter, hidden, 2),
+                                 down_tiled ? 0 : q2_scratch_bytes(m, hidden, inter, 1));
     void *base = nullptr;
-    if ((rc = arena_get(2 * gu_b + wb_b, &base))) return rc;
-    char *g = (char *)base, *u = g + gu_b, *wb = u + gu_b;
+    if ((rc = arena_get(act_b + part, &base))) return rc;
+    char *act = (char *)base;
+    char *scr = act + act_b;
     ProfileScope ps("dense_total q2", m, s);
-    if ((rc = q2_gemm_many_rows(x, m, hidden, inter, gsg, mg, g, wb, s)) ||
-        (rc = q2_gemm_many_rows(x, m, hidden, inter, gsu, mu, u, wb, s)))
-      return rc;
-    if ((rc = hip_status(launch_silu_mul(g, u, g, (int64_t)m * inter, s), "silu_mul launch"))) return rc;
-    return q2_gemm_many_rows(g, m, inter, hidden, gsd, md, out, wb, s);
+    Q2MatRef w2[2] = {mg, mu};
+    if (up_tiled)
+      rc = hip_status(launch_prefill_q2(x, m, hidden, inter, gsg, 2, w2, act, prefill_plan(m, inter, hidden, 2), s),
+                      "packed-Q2 many-row projection launch");
+    else
+      rc = run_q2(x, m, hidden, inter, gsg, 2, w2, act, scr, s);
+    if (rc) return rc;
+    if (down_tiled)
+      return hip_status(launch_prefill_q2(act, m, inter, hidden, gsd, 1, &md, out, prefill_plan(m, hidden, inter, 1), s),
+                        "packed-Q2 many-row projection launch");
+    return run_q2(act, m, inter, hidden, gsd, 1, &md, out, scr, s);
   }
   log_path("dense_ffn_forward_q2", "q2", m, inter, hidden);
   const size_t act_b = align256((size_t)2 * m * inter);

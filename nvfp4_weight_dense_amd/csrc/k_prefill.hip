@@ -77,19 +77,59 @@ struct PrefillArgs {
   const uint8_t *codes0, *scales0;  // gate (SWIGLU) or the matrix
   const uint8_t *codes1, *scales1;  // up (SWIGLU) or unused
   float ts0, ts1;
+  int gshift;              // packed-Q2 weights: scale group = 1 << gshift
   void *y;
   int ldy;                 // row stride of y in elements (>= n)
   int row_blocks, groups;  // tile = column group * row_blocks + row block
   int nwg;                 // persistent workgroups (gridDim.x)
 };
 
+// Packed-Q2 weights (page layers/dense_ffn_prefill.rs, `prefill_q2`: Q2_0
+// weights with a group size, dequantized to BF16 for the BF16 GEMM; the code
+// is this library's reading): a 2-bit code q per element, four per byte from
+// the low bits, one fp16 scale d per row and group of K; the value is
+// bf16((q - 2) * d).  A lane's 32 K values of a step lie in one group
+// (group >= 32), so the four values it can meet form a table, T_q =
+// bf16(fma(q, d, -2d)) -- exact in fp32 and rounded once, the bits of the
+// dequantized BF16 weight -- packed two per dword: lo = T0 | T1 << 16,
+// hi = T2 | T3 << 16.
+__device__ __forceinline__ void q2_table(uint32_t d_bits16, uint32_t &lo, uint32_t &hi) {
+  const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)d_bits16);
+  const float m2d = -2.0f * d;
+  const bf16x2 t01 = {(__bf16)__builtin_fmaf(0.0f, d, m2d), (__bf16)__builtin_fmaf(1.0f, d, m2d)};
+  const bf16x2 t23 = {(__bf16)__builtin_fmaf(2.0f, d, m2d), (__bf16)__builtin_fmaf(3.0f, d, m2d)};
+  lo = __builtin_bit_cast(uint32_t, t01);
+  hi = __builtin_bit_cast(uint32_t, t23);
+}
+
+// Eight codes (16 bits, element e in bits 2e..2e+1) -> their eight table
+// values.  z = cw | cw << 14 puts the codes of elements 2i and 2i+1 at bits
+// 4i and 4i+16, so (z >> 4i) & 0x30003 = q_2i + q_2i+1 << 16; times 0x0202
+// plus 0x01000100 that is the byte selector {2q, 2q+1} of each half for
+// v_perm_b32 over the 8-byte table {hi, lo} (bytes 0-3 lo, 4-7 hi).
+__device__ __forceinline__ bf16x8 q2_dequant8(uint32_t cw, uint32_t lo, uint32_t hi) {
+  const uint32_t z = cw | (cw << 14);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t y = (z >> (4 * i)) & 0x00030003u;
+    o[i] = __builtin_amdgcn_perm(hi, lo, y * 0x0202u + 0x01000100u);
+  }
+  return __builtin_bit_cast(bf16x8, uint4{o[0], o[1], o[2], o[3]});
+}
+
 // MT: 32-row tiles per workgroup; NBC: 32-column tiles per wave and matrix
-// (gate and up each with SWIGLU); NB = B tiles per wave.
-template <int MT, int NBC, bool SWIGLU>
+// (gate and up each with SWIGLU); NB = B tiles per wave.  Q2: packed-Q2
+// weights instead of NVFP4 (q2_table above).
+template <int MT, int NBC, bool SWIGLU, bool Q2>
 __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
   constexpr int kMT = MT;
   constexpr int kRows = 32 * MT;
   constexpr int kNB = SWIGLU ? 2 * NBC : NBC;
+  // steps per weight group: a group is 128 code bytes of a row either way
+  // (4 steps of NVFP4 at 32 bytes, 8 steps of packed Q2 at 16 bytes)
+  constexpr int kGroup = Q2 ? 8 : 4;
+  constexpr uint32_t kStepBytes = Q2 ? 16u : 32u;  // code bytes of a row per step
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kRows * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kRows * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wb0[kWaves * kNB * 32 * 32 * 4];
@@ -118,7 +158,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
   const int c32 = lane & 31;
   const int h = lane >> 5;
   const int k = k_v;
-  const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
+  // bytes per weight row: codes, and scales (E4M3 per 16 K; fp16 per group)
+  const uint32_t kb2 = Q2 ? (uint32_t)k >> 2 : (uint32_t)k >> 1;
+  const uint32_t kb16 = Q2 ? ((uint32_t)k >> p.gshift) * 2u : (uint32_t)k >> 4;
   const int cg = tile / p.row_blocks;
   const int rb = tile - cg * p.row_blocks;
   const int row0 = rb * kRows;
@@ -167,18 +209,21 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
   };
 
   // weight groups: codes through the LDS ring, scales through registers
-  constexpr int kGroup = 4;                    // steps per group
   // DMA lane mapping: instruction g moves rows 8g..8g+7; lane l loads row
   // 8g + l/8, chunk (l%8) ^ (l/8), and lands at 16 l
   const uint32_t drow = (uint32_t)lane >> 3, dchunk = ((uint32_t)lane & 7) ^ drow;
-  // read side: row c32 = 8g + a sits in instruction g, lane 8a + (x ^ a)
+  // read side: row c32 = 8g + a sits in instruction g, lane 8a + (x ^ a);
+  // step q of the group is chunk x = 2q + h (NVFP4: 16 bytes per lane) or
+  // chunk q, bytes 8h.. (packed Q2: 8 bytes per lane)
   const uint32_t ra = (uint32_t)c32 & 7;
   uint32_t coff[kGroup];
 #pragma unroll
   for (int q = 0; q < kGroup; ++q)
-    coff[q] = (uint32_t)(wave * kNB * 4 + (c32 >> 3)) * 1024u + 16u * (8u * ra + ((2u * q + h) ^ ra));
+    coff[q] = (uint32_t)(wave * kNB * 4 + (c32 >> 3)) * 1024u +
+              (Q2 ? 16u * (8u * ra + ((uint32_t)q ^ ra)) + 8u * (uint32_t)h
+                  : 16u * (8u * ra + ((2u * q + h) ^ ra)));
   auto load_group = [&](int G, uint8_t *slot) {
-    const uint32_t goff = (uint32_t)(s_begin + kGroup * G) * 32u;
+    const uint32_t goff = (uint32_t)(s_begin + kGroup * G) * kStepBytes;
     const bool ok = kGroup * G < len;
 #pragma unroll
     for (int i = 0; i < kNB; ++i)
@@ -187,8 +232,19 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
         dma16(wc[i], slot + ((wave * kNB + i) * 4 + g) * 1024,
               ok ? (8u * g + drow) * kb2 + goff + 16u * dchunk : kOOB);
   };
+  // packed Q2: lane (c32, h) needs one fp16 scale per step, that of K
+  // 64 t + 32 h (a lane's 32 K values lie in one group, group >= 32); step t's
+  // scales are loaded two steps ahead into slot t % 4
+  uint32_t qs[4][kNB];
+  auto load_q2_scales = [&](int tl, uint32_t (&sv)[kNB]) {
+    const uint32_t kk = (uint32_t)(s_begin + tl) * 64u + 32u * (uint32_t)h;
+    const uint32_t o = tl < len ? (uint32_t)c32 * kb16 + (kk >> p.gshift) * 2u : kOOB;
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) sv[i] = ld2(ws[i], o);
+  };
   uint4 sc[2][kNB];
   auto load_scales = [&](int G, uint4 (&sv)[kNB]) {
+    if constexpr (Q2) return;
     const uint32_t goff = (uint32_t)(s_begin + kGroup * G) * 4u;
     const int nst = len - kGroup * G;  // steps of this group that run (uniform)
     if (nst >= kGroup && (kb16 & 15u) == 0) {
@@ -204,12 +260,19 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
                       ld4(ws[i], nst > 2 ? o + 8u : kOOB), ld4(ws[i], nst > 3 ? o + 12u : kOOB)};
     }
   };
-  auto dequant_j = [&](const uint4 (&w)[kNB], const uint32_t (&s)[kNB], int j, bf16x8 (&out)[kNB]) {
+  // NVFP4: w holds the step's 32 codes of the lane, s its two scale bytes.
+  // Packed Q2: w.xy holds the 32 two-bit codes, s the two table dwords.
+  auto dequant_j = [&](const uint4 (&w)[kNB], const uint32_t (&s)[kNB][2], int j, bf16x8 (&out)[kNB]) {
 #pragma unroll
     for (int i = 0; i < kNB; ++i) {
-      const float sc_ = j < 2 ? e4m3_to_f32_sel<0>(s[i]) : e4m3_to_f32_sel<1>(s[i]);
-      const uint32_t word = j == 0 ? w[i].x : j == 1 ? w[i].y : j == 2 ? w[i].z : w[i].w;
-      out[i] = dequant8(word, sc_);
+      if constexpr (Q2) {
+        const uint32_t word = j < 2 ? w[i].x : w[i].y;
+        out[i] = q2_dequant8((j & 1) ? word >> 16 : word & 0xFFFFu, s[i][0], s[i][1]);
+      } else {
+        const float sc_ = j < 2 ? e4m3_to_f32_sel<0>(s[i][0]) : e4m3_to_f32_sel<1>(s[i][0]);
+        const uint32_t word = j == 0 ? w[i].x : j == 1 ? w[i].y : j == 2 ? w[i].z : w[i].w;
+        out[i] = dequant8(word, sc_);
+      }
     }
   };
 
@@ -226,6 +289,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
   lds_barrier();
   load_group(0, wb0);
   load_scales(0, sc[0]);
+  if constexpr (Q2) {
+    load_q2_scales(0, qs[0]);
+    load_q2_scales(1, qs[1]);
+  }
   load_a(0);
   store_a(lds0);
   load_a(1);
@@ -237,8 +304,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
       af[mt] = as_bf16x8(*(const uint4 *)&slot[(mt * 32 + c32) * kRowBytes + 2 * (32 * h + 8 * j)]);
   };
 
-  // one step; slot_c = t % 8 fixes at compile time the A slot (t % 2), the
-  // weight-ring slot (t / 4 % 2) and the step within its group (t % 4)
+  // one step; slot_c = t % (2 kGroup) fixes at compile time the A slot
+  // (t % 2), the weight-ring slot (t / kGroup % 2), the step within its
+  // group (t % kGroup) and, for packed Q2, the scale slot (t % 4)
   auto step = [&](int tl, auto slot_c) {
     constexpr int s8 = decltype(slot_c)::value;
     constexpr int q = s8 % kGroup, bsl = (s8 / kGroup) % 2;
@@ -246,13 +314,20 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
     uint8_t *nxt = (s8 % 2) ? lds0 : lds1;
     const uint8_t *bcur = bsl ? wb1 : wb0;
     uint4 w[kNB];
-    uint32_t sw[kNB];
+    uint32_t sw[kNB][2];
 #pragma unroll
     for (int i = 0; i < kNB; ++i) {
-      w[i] = *(const uint4 *)&bcur[coff[q] + i * 4 * 1024];
-      const uint32_t d = q == 0 ? sc[bsl][i].x : q == 1 ? sc[bsl][i].y : q == 2 ? sc[bsl][i].z : sc[bsl][i].w;
-      sw[i] = d >> (16u * h);
+      if constexpr (Q2) {
+        const uint2 c2 = *(const uint2 *)&bcur[coff[q] + i * 4 * 1024];
+        w[i] = uint4{c2.x, c2.y, 0u, 0u};
+        q2_table(qs[s8 % 4][i], sw[i][0], sw[i][1]);
+      } else {
+        w[i] = *(const uint4 *)&bcur[coff[q] + i * 4 * 1024];
+        const uint32_t d = q == 0 ? sc[bsl][i].x : q == 1 ? sc[bsl][i].y : q == 2 ? sc[bsl][i].z : sc[bsl][i].w;
+        sw[i][0] = d >> (16u * h);
+      }
     }
+    if constexpr (Q2) load_q2_scales(tl + 2, qs[(s8 + 2) % 4]);
     if constexpr (q == 1) {
       // second step of a group: request the next group into the other slot
       // (last read before the previous barrier), three steps ahead of use.
@@ -299,7 +374,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
     __builtin_amdgcn_sched_group_barrier(0x200, kPerThread, 0);
     lds_barrier();
   };
-  for (int tl = 0; tl < len; tl += 8) {
+  for (int tl = 0; tl < len; tl += 2 * kGroup) {
     step(tl, std::integral_constant<int, 0>{});
     if (tl + 1 < len) step(tl + 1, std::integral_constant<int, 1>{});
     if (tl + 2 < len) step(tl + 2, std::integral_constant<int, 2>{});
@@ -308,6 +383,16 @@ __global__ __launch_bounds__(kWaves * 64) void k_prefill(PrefillArgs p) {
     if (tl + 5 < len) step(tl + 5, std::integral_constant<int, 5>{});
     if (tl + 6 < len) step(tl + 6, std::integral_constant<int, 6>{});
     if (tl + 7 < len) step(tl + 7, std::integral_constant<int, 7>{});
+    if constexpr (Q2) {
+      if (tl + 8 < len) step(tl + 8, std::integral_constant<int, 8>{});
+      if (tl + 9 < len) step(tl + 9, std::integral_constant<int, 9>{});
+      if (tl + 10 < len) step(tl + 10, std::integral_constant<int, 10>{});
+      if (tl + 11 < len) step(tl + 11, std::integral_constant<int, 11>{});
+      if (tl + 12 < len) step(tl + 12, std::integral_constant<int, 12>{});
+      if (tl + 13 < len) step(tl + 13, std::integral_constant<int, 13>{});
+      if (tl + 14 < len) step(tl + 14, std::integral_constant<int, 14>{});
+      if (tl + 15 < len) step(tl + 15, std::integral_constant<int, 15>{});
+    }
   }
   // the last group request may still be in flight; the LDS it targets is not
   // read again, but it must land before the workgroup's LDS is released
@@ -436,22 +521,47 @@ PrefillPlan prefill_plan(int m, int n, int k, int nmat) {
 
 namespace {
 
+template <bool Q2>
 hipError_t launch_part(PrefillArgs p, int nmat, int mt, hipStream_t stream) {
   dim3 grid(p.nwg), block(kWaves * 64);
   switch ((nmat == 2 ? 100 : 0) + mt) {
-    case 108: hipLaunchKernelGGL((k_prefill<8, 1, true>), grid, block, 0, stream, p); break;
-    case 106: hipLaunchKernelGGL((k_prefill<6, 1, true>), grid, block, 0, stream, p); break;
-    case 105: hipLaunchKernelGGL((k_prefill<5, 1, true>), grid, block, 0, stream, p); break;
-    case 104: hipLaunchKernelGGL((k_prefill<4, 1, true>), grid, block, 0, stream, p); break;
-    case 102: hipLaunchKernelGGL((k_prefill<2, 1, true>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((k_prefill<8, 2, false>), grid, block, 0, stream, p); break;
-    case 6: hipLaunchKernelGGL((k_prefill<6, 2, false>), grid, block, 0, stream, p); break;
-    case 5: hipLaunchKernelGGL((k_prefill<5, 2, false>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((k_prefill<4, 2, false>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((k_prefill<2, 2, false>), grid, block, 0, stream, p); break;
+    case 108: hipLaunchKernelGGL((k_prefill<8, 1, true, Q2>), grid, block, 0, stream, p); break;
+    case 106: hipLaunchKernelGGL((k_prefill<6, 1, true, Q2>), grid, block, 0, stream, p); break;
+    case 105: hipLaunchKernelGGL((k_prefill<5, 1, true, Q2>), grid, block, 0, stream, p); break;
+    case 104: hipLaunchKernelGGL((k_prefill<4, 1, true, Q2>), grid, block, 0, stream, p); break;
+    case 102: hipLaunchKernelGGL((k_prefill<2, 1, true, Q2>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((k_prefill<8, 2, false, Q2>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((k_prefill<6, 2, false, Q2>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((k_prefill<5, 2, false, Q2>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_prefill<4, 2, false, Q2>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_prefill<2, 2, false, Q2>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Both launches of a plan; codes/scales of matrix i start at w_codes[i] /
+// w_scales[i], with code and scale bytes per weight row cb and sb.
+template <bool Q2>
+hipError_t launch_plan(PrefillArgs p, int n, int nmat, const uint8_t *const *w_codes,
+                       const uint8_t *const *w_scales, size_t cb, size_t sb, void *y,
+                       const PrefillPlan &pl, hipStream_t stream) {
+  // columns [c0, c0 + cols) of every matrix and of y
+  auto part = [&](int c0, int cols, int mt, int rb, int groups, int nwg) {
+    p.n = cols;
+    p.codes0 = w_codes[0] + (size_t)c0 * cb;
+    p.scales0 = w_scales[0] + (size_t)c0 * sb;
+    p.codes1 = nmat > 1 ? w_codes[1] + (size_t)c0 * cb : nullptr;
+    p.scales1 = nmat > 1 ? w_scales[1] + (size_t)c0 * sb : nullptr;
+    p.y = (uint8_t *)y + (size_t)c0 * 2;
+    p.row_blocks = rb;
+    p.groups = groups;
+    p.nwg = nwg;
+    return launch_part<Q2>(p, nmat, mt, stream);
+  };
+  hipError_t e = part(0, pl.n_bulk, pl.mt, pl.row_blocks, pl.groups, pl.nwg);
+  if (e != hipSuccess || pl.n_bulk >= n) return e;
+  return part(pl.n_bulk, n - pl.n_bulk, pl.mt2, pl.row_blocks2, pl.groups2, pl.nwg2);
 }
 
 }  // namespace
@@ -465,23 +575,25 @@ hipError_t launch_prefill(const void *x, int m, int k, int n, int nmat, const Ma
   p.ldy = n;
   p.ts0 = w[0].ts;
   p.ts1 = nmat > 1 ? w[1].ts : 0.f;
-  // columns [c0, c0 + cols) of every matrix and of y
-  auto part = [&](int c0, int cols, int mt, int rb, int groups, int nwg) {
-    const size_t cb = (size_t)c0 * (size_t)(k / 2), sb = (size_t)c0 * (size_t)(k / 16);
-    p.n = cols;
-    p.codes0 = w[0].codes + cb;
-    p.scales0 = w[0].scales + sb;
-    p.codes1 = nmat > 1 ? w[1].codes + cb : nullptr;
-    p.scales1 = nmat > 1 ? w[1].scales + sb : nullptr;
-    p.y = (uint8_t *)y + (size_t)c0 * 2;
-    p.row_blocks = rb;
-    p.groups = groups;
-    p.nwg = nwg;
-    return launch_part(p, nmat, mt, stream);
-  };
-  hipError_t e = part(0, pl.n_bulk, pl.mt, pl.row_blocks, pl.groups, pl.nwg);
-  if (e != hipSuccess || pl.n_bulk >= n) return e;
-  return part(pl.n_bulk, n - pl.n_bulk, pl.mt2, pl.row_blocks2, pl.groups2, pl.nwg2);
+  const uint8_t *codes[2] = {w[0].codes, nmat > 1 ? w[1].codes : nullptr};
+  const uint8_t *scales[2] = {w[0].scales, nmat > 1 ? w[1].scales : nullptr};
+  return launch_plan<false>(p, n, nmat, codes, scales, (size_t)(k / 2), (size_t)(k / 16), y, pl, stream);
+}
+
+hipError_t launch_prefill_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w,
+                             void *y, const PrefillPlan &pl, hipStream_t stream) {
+  PrefillArgs p{};
+  p.x = x;
+  p.m = m;
+  p.k = k;
+  p.ldy = n;
+  p.ts0 = 1.0f;
+  p.ts1 = 1.0f;
+  p.gshift = gshift;
+  const uint8_t *codes[2] = {w[0].codes, nmat > 1 ? w[1].codes : nullptr};
+  const uint8_t *scales[2] = {(const uint8_t *)w[0].scales, nmat > 1 ? (const uint8_t *)w[1].scales : nullptr};
+  return launch_plan<true>(p, n, nmat, codes, scales, (size_t)(k / 4), (size_t)(k >> gshift) * 2, y, pl,
+                           stream);
 }
 
 }  // namespace nvfp4

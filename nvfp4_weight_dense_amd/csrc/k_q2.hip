@@ -294,29 +294,6 @@ hipError_t launch_mt(const Q2Args &p, int mt, dim3 grid, hipStream_t s) {
   }
 }
 
-// Many rows: the weight is dequantized once into a bf16 [n][k] buffer for a
-// library GEMM (the pages' default packed-Q2 leg: dequant to BF16, then the
-// BF16 GEMM).  One thread per 16 weights (one 32-bit code word), the same
-// per-element arithmetic as the streaming kernel.
-__global__ __launch_bounds__(256) void k_dequant_q2_bf16(const uint32_t *__restrict__ codes,
-                                                        const uint16_t *__restrict__ scales, int n,
-                                                        int k, int gshift, uint4 *__restrict__ out) {
-  const int words = k >> 4;  // code words per row
-  const int64_t total = (int64_t)n * words;
-  const int ngroups = k >> gshift;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int row = (int)(i / words);
-    const int w16 = (int)(i - (int64_t)row * words);
-    const uint32_t c = codes[i];
-    const float d = fp16_bits_to_f32(scales[(size_t)row * ngroups + ((w16 << 4) >> gshift)]);
-    const float m2d = -2.0f * d;
-    const bf16x8 lo = dequant_q2x8(c & 0xFFFFu, d, m2d);
-    const bf16x8 hi = dequant_q2x8(c >> 16, d, m2d);
-    out[2 * i] = __builtin_bit_cast(uint4, lo);
-    out[2 * i + 1] = __builtin_bit_cast(uint4, hi);
-  }
-}
-
 }  // namespace
 
 // Column tiles per workgroup: with more than 16 rows each activation
@@ -353,16 +330,6 @@ size_t q2_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
   return pl.ksplit > 1
              ? (size_t)pl.tiles * cdiv(m, 64) * nmat * pl.ksplit * q2_ctw(m, n) * 16 * mt * 16
              : 0;
-}
-
-hipError_t launch_dequant_q2_bf16(const Q2MatRef &w, int n, int k, int gshift, void *out,
-                                  hipStream_t stream) {
-  const int64_t total = (int64_t)n * (k >> 4);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(k_dequant_q2_bf16, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint32_t *)w.codes, w.scales, n, k, gshift, (uint4 *)out);
-  return hipGetLastError();
 }
 
 hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w,

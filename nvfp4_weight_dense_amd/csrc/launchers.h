@@ -191,9 +191,12 @@ hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat,
                      unsigned *counters, const StreamPlan &pl,
                      hipStream_t stream);
 
-// W -> bf16 [n][k] (out 16-byte aligned), for the many-row library GEMM.
-hipError_t launch_dequant_q2_bf16(const Q2MatRef &w, int n, int k, int gshift,
-                                  void *out, hipStream_t stream);
+// Many-row projection on packed-Q2 weights (k % 64 == 0): the many-row
+// kernel of launch_prefill with the weights' codes dequantized in registers
+// as bf16((q - 2) * d); plan prefill_plan, no scratch.
+hipError_t launch_prefill_q2(const void *x, int m, int k, int n, int gshift, int nmat,
+                             const Q2MatRef *w, void *y, const PrefillPlan &pl,
+                             hipStream_t stream);
 
 // FP8 projection, nmat 1 or 2 (gate+up+silu) as launch_stream, with its own
 // plan (w8a8_plan: depends on n and k only) and partial size

@@ -48,7 +48,12 @@ def oq(w: si.Q2Weight) -> oracle.Q2Weight:
                                          (3, 16400, 256, 128), (64, 1000, 2048, 128),
                                          (2, 40, 512, 256), (130, 96, 768, 256),
                                          # up to 16 rows with a ragged last 128-K step
-                                         (4, 72, 160, 32), (9, 33, 96, 32), (1, 16, 224, 32)])
+                                         (4, 72, 160, 32), (9, 33, 96, 32), (1, 16, 224, 32),
+                                         # many rows: a partial last 512-K weight group (k % 512
+                                         # != 0), 32-element groups, two column launches; k % 64
+                                         # != 0 takes the streaming kernel with 64-row blocks
+                                         (300, 200, 2176, 128), (257, 96, 320, 32), (65, 40, 64, 32),
+                                         (600, 1100, 1024, 128), (100, 72, 96, 32)])
 def test_q2_gemm_matches_oracle(m, n, k, group):
     _say(f"q2 gemm m={m} n={n} k={k} group={group}")
     x = si.activations(m, k, seed=n, outliers=True)
@@ -56,11 +61,19 @@ def test_q2_gemm_matches_oracle(m, n, k, group):
     y = nv.q2_gemm_w2a16(x.cuda(), gq(w))
     sync()
     _, ye = oracle.gemm_q2(bits(x), oq(w))
-    assert_close(bits(y), ye, f"q2 gemm m={m} n={n} k={k}")
+    # outlier activations make some outputs heavy-tailed: rounding v to bf16
+    # moves it by up to 2^-8 |v| (half an ulp at the bottom of a binade), so
+    # with outputs beyond 2e-2 / 2^-8 = 5.12 x rms(ref) even the correctly
+    # rounded result can miss 2e-2 rms; the element-wise bound (one bf16 ulp
+    # more) always applies, the plain one where it is attainable
+    assert_close_elem(bits(y), ye, f"q2 gemm m={m} n={n} k={k}")
+    if np.max(np.abs(ye)) <= 5.12 * np.sqrt(np.mean(ye ** 2)):
+        assert_close(bits(y), ye, f"q2 gemm m={m} n={n} k={k}")
 
 
-# m = 130 takes the many-row leg (dequantize to bf16, library GEMM)
-@pytest.mark.parametrize("m,n,k", [(2, 12288, 4096), (33, 4096, 12288), (130, 4096, 12288)])
+# m = 130 and 2048 take the many-row kernel (k = 2176: a partial last weight group)
+@pytest.mark.parametrize("m,n,k", [(2, 12288, 4096), (33, 4096, 12288), (130, 4096, 12288),
+                                   (2048, 512, 2176)])
 def test_q2_gemm_exact_case_bit_exact(m, n, k):
     _say(f"q2 gemm exact m={m} n={n} k={k}")
     g = torch.Generator().manual_seed(n)
