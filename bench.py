@@ -277,7 +277,9 @@ KERNEL_RUNS = {
     "q2": ("decode", dict(m=1, q2=True)),
     "smallm": ("smallm", {}),
     "prefill": ("prefill", {}),
+    "w4a4_64": ("w4a4", dict(m=64, w4a4=True)),
     "w4a4_512": ("w4a4", dict(m=512, w4a4=True)),
+    "w8a8_64": ("w8a8", dict(m=64, w8a8=True)),
     "w8a8_512": ("w8a8", dict(m=512, w8a8=True)),
     "q2_prefill": ("prefill", dict(q2=True)),
     "q2_smallm": ("smallm", dict(q2=True)),

@@ -35,6 +35,12 @@
 //     the W4A4 arm needs.
 //   * Up to 64 rows (MT tiles of 16) share each dequantized weight fragment;
 //     more rows use more row blocks (grid.z).
+//   * NVFP4 activations from 17 rows on take k_stream_tall: the same
+//     per-output schedule, fed by a two-stage load pipeline, with two column
+//     tiles per workgroup (four for a single matrix beyond 64 rows) and an
+//     XCD-aware workgroup order.  Since every output sees the same steps,
+//     waves, MFMA sequence and reduction order, the fixed format's rows keep
+//     their bits at every row count.
 #include <type_traits>
 
 #include "launchers.h"
@@ -46,6 +52,13 @@ namespace {
 
 constexpr int kNW = 4;  // waves per workgroup (K split inside it)
 constexpr int kTargetBlocks = 512;
+// k_stream_tall: column tiles per workgroup (two; four for one matrix
+// beyond 64 rows, so every wave holds 4 x 4 accumulator tiles and each
+// dequantized fragment feeds four MFMAs) and row tiles per block beyond 64 rows
+constexpr int kTallCtw = 2;
+constexpr int kTallCtwWide = 4;
+constexpr int kTallRowTiles = 4;
+constexpr int kTallMinRows = 17;  // NVFP4 activations with this many rows take k_stream_tall
 
 struct StreamArgs {
   const void *x;          // bf16 [m][k] (W4A16)
@@ -58,7 +71,7 @@ struct StreamArgs {
   float ts0, ts1;
   void *y;
   float *partial;         // [nmat][ksplit][m][n]
-  unsigned *counters;     // [gridDim.z][gridDim.x], zero between calls
+  unsigned *counters;     // [row blocks][column blocks], zero between calls
   int ksplit, steps_per_split;
 };
 
@@ -69,147 +82,15 @@ struct Cfg {
   static constexpr int U = kRegsPerStep * 8 <= 128 ? 8 : (kRegsPerStep * 4 <= 128 ? 4 : 2);
 };
 
+// The workgroup's end: reduce the waves' accumulators in wave order, with
+// ksplit > 1 hand the tile to the last-arriving split (partials summed in
+// split order), then the epilogue.  Shared by both kernels below, so a tile's
+// result depends only on its accumulators, never on which kernel made them.
 template <int MT, int NMAT, int CTW, bool AFP4>
-__global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
-  constexpr int U = Cfg<MT, NMAT, CTW, AFP4>::U;
-  // MFMA operand type: fp16 when both operands are NVFP4 (exact either way,
-  // half the conversion work), bf16 for bf16 activations
-  using Frag = std::conditional_t<AFP4, f16x8, bf16x8>;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void stream_finish(const StreamArgs &p, f32x4 (&acc)[NMAT][CTW][MT], int lane,
+                                              int wave, int col0, int row0, int tile, int split) {
   const int c16 = lane & 15;
   const int g = lane >> 4;
-  const int src_addr = load_layout_src_addr(lane);
-  const uint32_t lrow = (uint32_t)(lane >> 2), lpiece = (uint32_t)(lane & 3);  // load layout
-  const int k = p.k;
-  const int col0 = blockIdx.x * (16 * CTW);
-  const int row0 = blockIdx.z * 64;
-  const int nsteps = (k + 127) >> 7;
-  const int s_begin = blockIdx.y * p.steps_per_split;
-  const int s_end = min(nsteps, s_begin + p.steps_per_split);
-  const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
-
-  // resources cover exactly this workgroup's weight rows and activation rows
-  const int ncols = min(16 * CTW, p.n - col0);
-  const int nrows = min(64, p.m - row0);
-  __amdgpu_buffer_rsrc_t wc[NMAT], ws[NMAT];
-  wc[0] = rsrc(p.codes0 + (size_t)col0 * kb2, (size_t)ncols * kb2);
-  ws[0] = rsrc(p.scales0 + (size_t)col0 * kb16, (size_t)ncols * kb16);
-  if constexpr (NMAT > 1) {
-    wc[1] = rsrc(p.codes1 + (size_t)col0 * kb2, (size_t)ncols * kb2);
-    ws[1] = rsrc(p.scales1 + (size_t)col0 * kb16, (size_t)ncols * kb16);
-  }
-  __amdgpu_buffer_rsrc_t ax, axs;
-  if constexpr (AFP4) {
-    ax = rsrc(p.xc + (size_t)row0 * kb2, (size_t)nrows * kb2);
-    axs = rsrc(p.xs + (size_t)row0 * kb16, (size_t)nrows * kb16);
-  } else {
-    ax = rsrc((const uint16_t *)p.x + (size_t)row0 * k, (size_t)nrows * k * 2);
-    axs = ax;
-  }
-
-  f32x4 acc[NMAT][CTW][MT];
-#pragma unroll
-  for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-    for (int ct = 0; ct < CTW; ++ct)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int base = s_begin + wave; base < s_end; base += kNW * U) {
-    uint4 bw[U][NMAT][CTW];
-    uint32_t bsc[U][NMAT][CTW];
-    uint4 aw[U][MT][AFP4 ? 1 : 4];
-    uint32_t asc[U][MT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = base + u * kNW;
-      const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
-      const bool ok = t < s_end && kk < (uint32_t)k;
-      const uint32_t kl = (uint32_t)t * 128u + 32u * lpiece;  // K of this lane's weight load
-      const bool okl = t < s_end && kl < (uint32_t)k;
-#pragma unroll
-      for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) {
-          const uint32_t row = (uint32_t)(ct * 16) + lrow;
-          bw[u][i][ct] = ld16(wc[i], okl ? row * kb2 + (kl >> 1) : kOOB);
-          bsc[u][i][ct] = ld2(ws[i], okl ? row * kb16 + (kl >> 4) : kOOB);
-        }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t r = (uint32_t)(mt * 16 + c16);
-        if constexpr (AFP4) {
-          aw[u][mt][0] = ld16(ax, ok ? r * kb2 + (kk >> 1) : kOOB);
-          asc[u][mt] = ld2(axs, ok ? r * kb16 + (kk >> 4) : kOOB);
-        } else {
-          const uint32_t off = ok ? (r * (uint32_t)k + kk) * 2u : kOOB;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) aw[u][mt][q] = ld16(ax, off + 16u * q);
-          asc[u][mt] = 0;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Frag bf[NMAT][CTW][4];
-#pragma unroll
-      for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) {
-          const uint4 w = from_load_layout(bw[u][i][ct], src_addr);
-          const uint32_t sc = from_load_layout(bsc[u][i][ct], src_addr);
-          const float s0 = e4m3_to_f32_sel<0>(sc);
-          const float s1 = e4m3_to_f32_sel<1>(sc);
-          if constexpr (AFP4) {
-            const f16x2 m0 = scale_mantissa_f16x2(s0), m1 = scale_mantissa_f16x2(s1);
-            bf[i][ct][0] = dequant8_f16(w.x, s0, m0);
-            bf[i][ct][1] = dequant8_f16(w.y, s0, m0);
-            bf[i][ct][2] = dequant8_f16(w.z, s1, m1);
-            bf[i][ct][3] = dequant8_f16(w.w, s1, m1);
-          } else {
-            bf[i][ct][0] = dequant8(w.x, s0);
-            bf[i][ct][1] = dequant8(w.y, s0);
-            bf[i][ct][2] = dequant8(w.z, s1);
-            bf[i][ct][3] = dequant8(w.w, s1);
-          }
-        }
-      Frag afr[MT][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        Frag (&af)[4] = afr[mt];
-        if constexpr (AFP4) {
-          const float s0 = e4m3_to_f32_sel<0>(asc[u][mt]);
-          const float s1 = e4m3_to_f32_sel<1>(asc[u][mt]);
-          const f16x2 m0 = scale_mantissa_f16x2(s0), m1 = scale_mantissa_f16x2(s1);
-          af[0] = dequant8_f16(aw[u][mt][0].x, s0, m0);
-          af[1] = dequant8_f16(aw[u][mt][0].y, s0, m0);
-          af[2] = dequant8_f16(aw[u][mt][0].z, s1, m1);
-          af[3] = dequant8_f16(aw[u][mt][0].w, s1, m1);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) af[q] = as_bf16x8(aw[u][mt][q]);
-        }
-      }
-      // K sub-step outermost: consecutive MFMAs update different accumulators
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-            for (int ct = 0; ct < CTW; ++ct) {
-              if constexpr (AFP4)
-                acc[i][ct][mt] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[mt][j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
-              else
-                acc[i][ct][mt] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][j], bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
-            }
-    }
-  }
-
   // fixed-order reduction over the workgroup's waves, one (matrix, tile)
   // pair at a time to bound LDS
   __shared__ float red[kNW - 1][MT][4][64];
@@ -242,7 +123,7 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
   if (p.ksplit > 1) {
     // this workgroup's partial tiles: [NMAT][ksplit][CTW][16*MT rows][16 columns]
     constexpr int kTile = 16 * MT * 16;
-    const size_t wg = (size_t)blockIdx.z * gridDim.x + blockIdx.x;
+    const size_t wg = (size_t)tile;
     const __amdgpu_buffer_rsrc_t pres = rsrc(p.partial + wg * NMAT * p.ksplit * CTW * kTile,
                                              (size_t)NMAT * p.ksplit * CTW * kTile * 4);
     auto poff = [&](int i, int sp, int ct, int mt, int e) -> uint32_t {
@@ -257,7 +138,7 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int i = 0; i < NMAT; ++i)
-            st_coherent(pres, poff(i, blockIdx.y, ct, mt, e), acc[i][ct][mt][e]);
+            st_coherent(pres, poff(i, split, ct, mt, e), acc[i][ct][mt][e]);
     unsigned *cnt = p.counters + wg;
     wait_all_memory();
     unsigned old = 0;
@@ -326,6 +207,318 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
 }
 
 template <int MT, int NMAT, int CTW, bool AFP4>
+__global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
+  constexpr int U = Cfg<MT, NMAT, CTW, AFP4>::U;
+  // MFMA operand type: fp16 when both operands are NVFP4 (exact either way,
+  // half the conversion work), bf16 for bf16 activations
+  using Frag = std::conditional_t<AFP4, f16x8, bf16x8>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+  const int src_addr = load_layout_src_addr(lane);
+  const uint32_t lrow = (uint32_t)(lane >> 2), lpiece = (uint32_t)(lane & 3);  // load layout
+  const int k = p.k;
+  const int col0 = blockIdx.x * (16 * CTW);
+  const int row0 = blockIdx.z * (16 * MT);  // row blocks of 16 MT rows
+  const int nsteps = (k + 127) >> 7;
+  const int s_begin = blockIdx.y * p.steps_per_split;
+  const int s_end = min(nsteps, s_begin + p.steps_per_split);
+  const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
+
+  // resources cover exactly this workgroup's weight rows and activation rows
+  const int ncols = min(16 * CTW, p.n - col0);
+  const int nrows = min(16 * MT, p.m - row0);
+  __amdgpu_buffer_rsrc_t wc[NMAT], ws[NMAT];
+  wc[0] = rsrc(p.codes0 + (size_t)col0 * kb2, (size_t)ncols * kb2);
+  ws[0] = rsrc(p.scales0 + (size_t)col0 * kb16, (size_t)ncols * kb16);
+  if constexpr (NMAT > 1) {
+    wc[1] = rsrc(p.codes1 + (size_t)col0 * kb2, (size_t)ncols * kb2);
+    ws[1] = rsrc(p.scales1 + (size_t)col0 * kb16, (size_t)ncols * kb16);
+  }
+  __amdgpu_buffer_rsrc_t ax, axs;
+  if constexpr (AFP4) {
+    ax = rsrc(p.xc + (size_t)row0 * kb2, (size_t)nrows * kb2);
+    axs = rsrc(p.xs + (size_t)row0 * kb16, (size_t)nrows * kb16);
+  } else {
+    ax = rsrc((const uint16_t *)p.x + (size_t)row0 * k, (size_t)nrows * k * 2);
+    axs = ax;
+  }
+
+  f32x4 acc[NMAT][CTW][MT];
+#pragma unroll
+  for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int base = s_begin + wave; base < s_end; base += kNW * U) {
+    uint4 bw[U][NMAT][CTW];
+    uint32_t bsc[U][NMAT][CTW];
+    uint4 aw[U][MT][AFP4 ? 1 : 4];
+    uint32_t asc[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = base + u * kNW;
+      const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
+      const bool ok = t < s_end && kk < (uint32_t)k;
+      const uint32_t kl = (uint32_t)t * 128u + 32u * lpiece;  // K of this lane's weight load
+      const bool okl = t < s_end && kl < (uint32_t)k;
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const uint32_t row = (uint32_t)(ct * 16) + lrow;
+          bw[u][i][ct] = ld16(wc[i], okl ? row * kb2 + (kl >> 1) : kOOB);
+          bsc[u][i][ct] = ld2(ws[i], okl ? row * kb16 + (kl >> 4) : kOOB);
+        }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t r = (uint32_t)(mt * 16 + c16);
+        if constexpr (AFP4) {
+          aw[u][mt][0] = ld16(ax, ok ? r * kb2 + (kk >> 1) : kOOB);
+          asc[u][mt] = ld2(axs, ok ? r * kb16 + (kk >> 4) : kOOB);
+        } else {
+          const uint32_t off = ok ? (r * (uint32_t)k + kk) * 2u : kOOB;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) aw[u][mt][q] = ld16(ax, off + 16u * q);
+          asc[u][mt] = 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Frag bf[NMAT][CTW][4];
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const uint4 w = from_load_layout(bw[u][i][ct], src_addr);
+          const uint32_t sc = from_load_layout(bsc[u][i][ct], src_addr);
+          if constexpr (AFP4) {
+            const f16x2 s01 = e4m3x2_to_f16x2(sc);
+            bf[i][ct][0] = dequant8_f16(w.x, s01[0]);
+            bf[i][ct][1] = dequant8_f16(w.y, s01[0]);
+            bf[i][ct][2] = dequant8_f16(w.z, s01[1]);
+            bf[i][ct][3] = dequant8_f16(w.w, s01[1]);
+          } else {
+            const float s0 = e4m3_to_f32_sel<0>(sc);
+            const float s1 = e4m3_to_f32_sel<1>(sc);
+            bf[i][ct][0] = dequant8(w.x, s0);
+            bf[i][ct][1] = dequant8(w.y, s0);
+            bf[i][ct][2] = dequant8(w.z, s1);
+            bf[i][ct][3] = dequant8(w.w, s1);
+          }
+        }
+      // K sub-step outermost: consecutive MFMAs update different
+      // accumulators.  An activation fragment is formed just before its
+      // MFMAs (NVFP4 rows dequantized exactly like the weight), so a tall row
+      // block does not hold all of a step's fragments at once; the MFMA
+      // sequence of every output is the same for every row-block height.
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          Frag af;
+          if constexpr (AFP4) {
+            const f16x2 sa = e4m3x2_to_f16x2(asc[u][mt]);
+            const uint32_t word = j == 0 ? aw[u][mt][0].x : j == 1 ? aw[u][mt][0].y
+                                : j == 2 ? aw[u][mt][0].z : aw[u][mt][0].w;
+            af = dequant8_f16(word, sa[j >> 1]);
+          } else {
+            af = as_bf16x8(aw[u][mt][j]);
+          }
+#pragma unroll
+          for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct) {
+              if constexpr (AFP4)
+                acc[i][ct][mt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
+              else
+                acc[i][ct][mt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[i][ct][j], acc[i][ct][mt], 0, 0, 0);
+            }
+        }
+    }
+  }
+
+  stream_finish<MT, NMAT, CTW, AFP4>(p, acc, lane, wave, col0, row0, blockIdx.z * gridDim.x + blockIdx.x,
+                                     blockIdx.y);
+}
+
+// Row-block variant for NVFP4 activations beyond 16 rows.  The same
+// workgroup shape, wave-to-step assignment, MFMA sequence per accumulator
+// and tail as k_stream<MT, NMAT, CTW, true>, so every output element gets the
+// same bits; what changes is how the steps are fed.  With up to 128 rows per
+// block a wave's registers cannot hold several steps in flight, so each wave
+// runs a two-stage pipeline: the loads of its next step are issued before the
+// current step is dequantized and multiplied, and only one step's raw bytes
+// wait in registers.  Activation fragments are formed one (row tile, K
+// sub-step) at a time and weight fragments one K sub-step at a time.
+template <int MT, int NMAT, int CTW>
+__global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+  const int src_addr = load_layout_src_addr(lane);
+  const uint32_t lrow = (uint32_t)(lane >> 2), lpiece = (uint32_t)(lane & 3);
+  const int k = p.k;
+  // One-dimensional grid over (row block, split, column block), row block
+  // fastest.  Workgroups go to the eight XCDs in turn (workgroup L to XCD
+  // L mod 8); each XCD gets one contiguous range of that order, so the row
+  // blocks that share a weight tile run together behind one L2.
+  const int nrb = cdiv(p.m, 16 * MT);
+  const int q = (int)(gridDim.x >> 3), rem = (int)(gridDim.x & 7), xcd = (int)(blockIdx.x & 7);
+  const int u = xcd * q + min(xcd, rem) + (int)(blockIdx.x >> 3);
+  const int rb = u % nrb;
+  const int split = (u / nrb) % p.ksplit;
+  const int cb = u / (nrb * p.ksplit);
+  const int col0 = cb * (16 * CTW);
+  const int row0 = rb * (16 * MT);
+  const int nsteps = (k + 127) >> 7;
+  const int s_begin = split * p.steps_per_split;
+  const int s_end = min(nsteps, s_begin + p.steps_per_split);
+  const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
+
+  const int ncols = min(16 * CTW, p.n - col0);
+  const int nrows = min(16 * MT, p.m - row0);
+  __amdgpu_buffer_rsrc_t wc[NMAT], ws[NMAT];
+  wc[0] = rsrc(p.codes0 + (size_t)col0 * kb2, (size_t)ncols * kb2);
+  ws[0] = rsrc(p.scales0 + (size_t)col0 * kb16, (size_t)ncols * kb16);
+  if constexpr (NMAT > 1) {
+    wc[1] = rsrc(p.codes1 + (size_t)col0 * kb2, (size_t)ncols * kb2);
+    ws[1] = rsrc(p.scales1 + (size_t)col0 * kb16, (size_t)ncols * kb16);
+  }
+  const __amdgpu_buffer_rsrc_t ax = rsrc(p.xc + (size_t)row0 * kb2, (size_t)nrows * kb2);
+  const __amdgpu_buffer_rsrc_t axs = rsrc(p.xs + (size_t)row0 * kb16, (size_t)nrows * kb16);
+
+  // one step's raw bytes: weights in the row-contiguous load layout,
+  // activations already in MFMA layout (lane (c, g): row c, 32 K at 32 g)
+  struct Step {
+    uint4 bw[NMAT][CTW];
+    uint32_t bsc[NMAT][CTW];
+    uint4 aw[MT];
+    uint32_t asc[MT];
+  };
+  auto load = [&](int t, Step &b) {
+    const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
+    const bool ok = t < s_end && kk < (uint32_t)k;
+    const uint32_t kl = (uint32_t)t * 128u + 32u * lpiece;
+    const bool okl = t < s_end && kl < (uint32_t)k;
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const uint32_t row = (uint32_t)(ct * 16) + lrow;
+        b.bw[i][ct] = ld16(wc[i], okl ? row * kb2 + (kl >> 1) : kOOB);
+        b.bsc[i][ct] = ld2(ws[i], okl ? row * kb16 + (kl >> 4) : kOOB);
+      }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t r = (uint32_t)(mt * 16 + c16);
+      b.aw[mt] = ld16(ax, ok ? r * kb2 + (kk >> 1) : kOOB);
+      b.asc[mt] = ld2(axs, ok ? r * kb16 + (kk >> 4) : kOOB);
+    }
+  };
+
+  f32x4 acc[NMAT][CTW][MT];
+#pragma unroll
+  for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Step &b) {
+    uint4 w[NMAT][CTW];
+    f16x2 wsc[NMAT][CTW];
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        w[i][ct] = from_load_layout(b.bw[i][ct], src_addr);
+        wsc[i][ct] = e4m3x2_to_f16x2(from_load_layout(b.bsc[i][ct], src_addr));
+      }
+    f16x2 asc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) asc[mt] = e4m3x2_to_f16x2(b.asc[mt]);
+    // K sub-step outermost, as in k_stream
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8 bf[NMAT][CTW];
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+          const uint32_t word = j == 0 ? w[i][ct].x : j == 1 ? w[i][ct].y : j == 2 ? w[i][ct].z : w[i][ct].w;
+          bf[i][ct] = dequant8_f16(word, wsc[i][ct][j >> 1]);
+        }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t word = j == 0 ? b.aw[mt].x : j == 1 ? b.aw[mt].y : j == 2 ? b.aw[mt].z : b.aw[mt].w;
+        const f16x8 af = dequant8_f16(word, asc[mt][j >> 1]);
+#pragma unroll
+        for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+          for (int ct = 0; ct < CTW; ++ct)
+            acc[i][ct][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[i][ct], acc[i][ct][mt], 0, 0, 0);
+      }
+    }
+  };
+
+  // wave w takes steps s_begin + w, s_begin + w + 4, ... in increasing
+  // order.  The loop body is one basic block (loads of the next step, then
+  // the current step's arithmetic, twice), so each step waits only for its
+  // own loads; loads past the wave's last step are out of range and fetch
+  // nothing.
+  const int first = s_begin + wave;
+  const int nmine = first < s_end ? (s_end - first + kNW - 1) / kNW : 0;
+  Step b0, b1;
+  load(first, b0);
+  int t = first;
+  for (int i = 0; i + 2 <= nmine; i += 2, t += 2 * kNW) {
+    // the barriers keep the scheduler from sinking a step's loads into the
+    // arithmetic that they are meant to overlap
+    load(t + kNW, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(t + 2 * kNW, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (nmine & 1) compute(b0);
+
+  stream_finish<MT, NMAT, CTW, true>(p, acc, lane, wave, col0, row0, rb * cdiv(p.n, 16 * CTW) + cb, split);
+}
+
+template <int MT, int NMAT, int CTW>
+hipError_t launch_tall(const StreamArgs &p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_stream_tall<MT, NMAT, CTW>), grid, dim3(kNW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+int tall_ctw(int nmat, int m) { return nmat == 1 && m > 64 ? kTallCtwWide : kTallCtw; }
+
+template <int NMAT>
+hipError_t launch_tall_mt(const StreamArgs &p, int mt, int ctw, dim3 grid, hipStream_t s) {
+  if (ctw == kTallCtwWide) {
+    if constexpr (NMAT == 1) return launch_tall<kTallRowTiles, 1, kTallCtwWide>(p, grid, s);
+    return hipErrorInvalidValue;
+  }
+  switch (mt) {
+    case 2: return launch_tall<2, NMAT, kTallCtw>(p, grid, s);
+    case 3: return launch_tall<3, NMAT, kTallCtw>(p, grid, s);
+    case 4: return launch_tall<4, NMAT, kTallCtw>(p, grid, s);
+    default: return launch_tall<kTallRowTiles, NMAT, kTallCtw>(p, grid, s);
+  }
+}
+
+template <int MT, int NMAT, int CTW, bool AFP4>
 hipError_t launch_one(const StreamArgs &p, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((k_stream<MT, NMAT, CTW, AFP4>), grid, dim3(kNW * 64), 0, s, p);
   return hipGetLastError();
@@ -366,14 +559,20 @@ StreamPlan stream_plan(int n, int k) {
 }
 
 size_t stream_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
-  // per workgroup: [nmat][ksplit][CTW][16*MT][16]
-  const int mt = m >= 64 ? 4 : cdiv(m, 16);
-  (void)n;
-  return pl.ksplit > 1
-             ? (size_t)pl.tiles * cdiv(m, 64) * nmat * pl.ksplit * stream_ctw(n) * 16 * mt * 16
-             : 0;
+  // per workgroup [nmat][ksplit][CTW][16*MT][16]: nmat*ksplit floats per
+  // element of the output padded to whole row blocks (16*MT rows) and whole
+  // workgroup columns, for either kernel
+  if (pl.ksplit <= 1) return 0;
+  const size_t rows_tall = (size_t)16 * kTallRowTiles * cdiv(m, 16 * kTallRowTiles);
+  const size_t rows = m <= 64 ? (size_t)16 * cdiv(m, 16)
+                              : (rows_tall > (size_t)64 * cdiv(m, 64) ? rows_tall : (size_t)64 * cdiv(m, 64));
+  const size_t cols_stream = (size_t)pl.tiles * 16 * stream_ctw(n);
+  const size_t cols_tall = (size_t)16 * kTallCtwWide * cdiv(n, 16 * kTallCtwWide);
+  return (size_t)nmat * pl.ksplit * rows * (cols_stream > cols_tall ? cols_stream : cols_tall);
 }
 
+// (also sizes the counters of the FP8 and Q2 streaming kernels; k_stream_tall
+// has no more row blocks and no more column blocks than k_stream)
 size_t stream_counter_words(const StreamPlan &pl, int m) {
   return pl.ksplit > 1 ? (size_t)pl.tiles * cdiv(m, 64) : 0;
 }
@@ -401,6 +600,12 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat, const M
   p.ksplit = pl.ksplit;
   p.steps_per_split = pl.steps_per_split;
   const bool afp4 = a.x_bf16 == nullptr;
+  if (afp4 && m >= kTallMinRows) {
+    const int mt = m > 64 ? kTallRowTiles : cdiv(m, 16);
+    const int ctw = tall_ctw(nmat, m);
+    dim3 grid(cdiv(n, 16 * ctw) * pl.ksplit * cdiv(m, 16 * mt));
+    return nmat == 1 ? launch_tall_mt<1>(p, mt, ctw, grid, stream) : launch_tall_mt<2>(p, mt, ctw, grid, stream);
+  }
   const int mt = m >= 64 ? 4 : cdiv(m, 16);
   const int ctw = stream_ctw(n);
   dim3 grid(pl.tiles, pl.ksplit, cdiv(m, 64));

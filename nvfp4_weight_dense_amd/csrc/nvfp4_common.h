@@ -59,21 +59,19 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
 // The same eight values as fp16, for operands that are NVFP4 on both sides.
 // An E2M1 value (at most 2 significant bits) times an E4M3 scale (at most
 // 4) needs at most 6 significant bits and lies in [2^-10, 2688], so it is
-// exact in fp16.  The hardware conversion applies the power-of-two part of
-// its scale operand (the scale itself is passed); the mantissa factor of
-// the scale, in [1, 2), follows as one packed fp16 multiply per pair.  A
-// zero scale gives zeros.
-__device__ __forceinline__ f16x2 scale_mantissa_f16x2(float s) {
-  const float mf =
-      __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, s) & 0x007FFFFFu) | 0x3F800000u);
-  const _Float16 h = (_Float16)mf;
-  return f16x2{h, h};
+// exact in fp16, and so is every E4M3 value.  The hardware conversions run
+// with a unit scale (fp4 -> the exact E2M1 values, fp8 -> the exact E4M3
+// values); the block scale then follows as one packed fp16 multiply per
+// pair, its operand selected from the scale pair by op_sel.
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t w) {  // bytes 0, 1 of w
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
 }
-__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float s, f16x2 mf) {
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0) * mf;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1) * mf;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * mf;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * mf;
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, _Float16 s) {
+  const f16x2 ss = {s, s};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 

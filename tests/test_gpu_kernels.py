@@ -173,8 +173,12 @@ def test_quantize_golden_rows_on_gpu():
 
 # ---- W4A4 projection ------------------------------------------------------------------------
 
+# beyond 64 rows the kernel takes 128-row blocks: 100 and 257 rows leave a
+# ragged last block, (130, 48, 4096) splits K over workgroups with it, and
+# n = 16400 takes two column tiles per workgroup
 @pytest.mark.parametrize("m,n,k", [(1, 16, 32), (3, 100, 160), (64, 130, 1024), (100, 64, 512),
-                                   (5, 40, 96), (12, 48, 352)])
+                                   (5, 40, 96), (12, 48, 352), (130, 48, 4096), (257, 200, 320),
+                                   (300, 16400, 160)])
 def test_gemm_w4a4_matches_oracle(m, n, k):
     _say(f"gemm_w4a4 m={m} n={n} k={k}")
     x = si.activations(m, k, seed=m + 2 * n)
@@ -195,6 +199,13 @@ def test_gemm_w4a4_rows_independent_of_m():
         y = nv.nvfp4_gemm_w4a4(x[:m].contiguous(), w)
         sync()
         assert torch.equal(y.view(torch.int16), ref[:m].view(torch.int16)), m
+    # K split over four workgroups; 65 and 130 rows: ragged 128-row blocks
+    w = g_weight(si.weight(64, hidden, seed=10, code_stream=1, scale_stream=2))
+    ref = nv.nvfp4_gemm_w4a4(x, w)
+    for m in (1, 8, 64, 65, 130, 300):
+        y = nv.nvfp4_gemm_w4a4(x[:m].contiguous(), w)
+        sync()
+        assert torch.equal(y.view(torch.int16), ref[:m].view(torch.int16)), ("split", m)
 
 
 # ---- gate+up+silu entry point -----------------------------------------------------------------
