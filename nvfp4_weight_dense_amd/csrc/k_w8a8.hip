@@ -63,7 +63,7 @@ struct W8Args {
   const float *scales0, *scales1;  // [ceil(n/128)][ceil(k/128)]
   void *y;
   float *partial;      // [tiles * row blocks][NMAT][ksplit][CTW][16*MT][16]
-  unsigned *counters;  // [gridDim.z][gridDim.x], zero between calls
+  unsigned *counters;  // [row blocks][column blocks], zero between calls
   int ksplit, steps_per_split;
 };
 
@@ -106,10 +106,22 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
   const int src_addr = load_layout_src_addr(lane);
   const uint32_t wrow = (uint32_t)(lane >> 2);    // weight row this lane loads
   const int k = p.k;
-  const int col0 = blockIdx.x * (16 * CTW);
-  const int row0 = blockIdx.z * 64;
+  // One-dimensional grid over (row block, split, column block), row block
+  // fastest.  Workgroups go to the eight XCDs in turn (workgroup L to XCD
+  // L mod 8); each XCD gets one contiguous range of that order, so the row
+  // blocks that read the same weight columns run together behind one L2
+  // and the weights leave HBM about once, not once per 64-row block.
+  const int nrb = cdiv(p.m, 64);
+  const int ncb = cdiv(p.n, 16 * CTW);
+  const int q = (int)(gridDim.x >> 3), rem = (int)(gridDim.x & 7), xcd = (int)(blockIdx.x & 7);
+  const int u = xcd * q + min(xcd, rem) + (int)(blockIdx.x >> 3);
+  const int rb = u % nrb;
+  const int split = (u / nrb) % p.ksplit;
+  const int cb = u / (nrb * p.ksplit);
+  const int col0 = cb * (16 * CTW);
+  const int row0 = rb * 64;
   const int nsteps = (k + 127) >> 7;  // = scale blocks along K
-  const int s_begin = blockIdx.y * p.steps_per_split;
+  const int s_begin = split * p.steps_per_split;
   const int s_end = min(nsteps, s_begin + p.steps_per_split);
   const int nbn = (p.n + 127) >> 7;   // scale blocks along N
 
@@ -134,72 +146,79 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
       for (int mt = 0; mt < MT; ++mt) acc[i][ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int base = s_begin + wave; base < s_end; base += kNW * U) {
-    uint4 bw[U][NMAT][CTW][2];
-    uint4 aw[U][MT][2];
-    float sc[U][NMAT][CTW];
+  // one step's bytes and block scales
+  struct Step {
+    uint4 bw[NMAT][CTW][2];
+    uint4 aw[MT][2];
+    float sc[NMAT][CTW];
+  };
+  auto load = [&](int t, Step &b) {
+    // K offsets of the 16-byte loads: weights (load layout), activations
+    // (operand layout); each is checked on its own (k is only a multiple
+    // of 32, so the second 64 bytes of the last step can lie past k)
+    const bool in_split = t < s_end;
+    const uint32_t kw = (uint32_t)t * 128u + 16u * (uint32_t)(lane & 3);
+    const uint32_t ka = (uint32_t)t * 128u + 16u * (uint32_t)g;
+    const bool okw0 = in_split && kw < (uint32_t)k, okw1 = in_split && kw + 64u < (uint32_t)k;
+    const bool oka0 = in_split && ka < (uint32_t)k, oka1 = in_split && ka + 64u < (uint32_t)k;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = base + u * kNW;
-      // K offsets of the 16-byte loads: weights (load layout), activations
-      // (operand layout); each is checked on its own (k is only a multiple
-      // of 32, so the second 64 bytes of the last step can lie past k)
-      const bool in_split = t < s_end;
-      const uint32_t kw = (uint32_t)t * 128u + 16u * (uint32_t)(lane & 3);
-      const uint32_t ka = (uint32_t)t * 128u + 16u * (uint32_t)g;
-      const bool okw0 = in_split && kw < (uint32_t)k, okw1 = in_split && kw + 64u < (uint32_t)k;
-      const bool oka0 = in_split && ka < (uint32_t)k, oka1 = in_split && ka + 64u < (uint32_t)k;
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct) {
+        const uint32_t roff = (uint32_t)(ct * 16) + wrow;
+        // cached loads: the non-temporal hint let lines go before every
+        // lane of a line had read it (FETCH_SIZE of the m=1 gate+up launch
+        // 1.35x its algorithmic bytes with the hint, 1.11x without)
+        b.bw[i][ct][0] = ld16(wc[i], okw0 ? roff * (uint32_t)k + kw : kOOB);
+        b.bw[i][ct][1] = ld16(wc[i], okw1 ? roff * (uint32_t)k + kw + 64u : kOOB);
+        // the tile's 16 columns share one scale row (col0 + 16 ct is a
+        // multiple of 16, blocks are 128 wide); steps past the end read
+        // block 0 and multiply zeros
+        const int tb = t < s_end ? t : 0;
+        const int cbs = min((col0 + ct * 16) >> 7, nbn - 1);  // a tile past n: any valid row
+        b.sc[i][ct] = wsc[i][(size_t)cbs * nsteps + tb];
+      }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t roff = (uint32_t)(mt * 16 + c16) * (uint32_t)k;
+      b.aw[mt][0] = ld16(ax, oka0 ? roff + ka : kOOB);
+      b.aw[mt][1] = ld16(ax, oka1 ? roff + ka + 64u : kOOB);
+    }
+  };
+  // P_b = the step's four MFMAs from zero, then acc = fma(scale_b, P_b, acc)
+  auto compute = [&](const Step &b) {
+    f16x8 bf[NMAT][CTW][4];
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CTW; ++ct)
+        fp8x32_to_f16(from_load_layout(b.bw[i][ct][0], src_addr), from_load_layout(b.bw[i][ct][1], src_addr),
+                      bf[i][ct]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f16x8 af[4];
+      fp8x32_to_f16(b.aw[mt][0], b.aw[mt][1], af);
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-          const uint32_t roff = (uint32_t)(ct * 16) + wrow;
-          // cached loads: the non-temporal hint let lines go before every
-          // lane of a line had read it (FETCH_SIZE of the m=1 gate+up launch
-          // 1.35x its algorithmic bytes with the hint, 1.11x without)
-          bw[u][i][ct][0] = ld16(wc[i], okw0 ? roff * (uint32_t)k + kw : kOOB);
-          bw[u][i][ct][1] = ld16(wc[i], okw1 ? roff * (uint32_t)k + kw + 64u : kOOB);
-          // the tile's 16 columns share one scale row (col0 + 16 ct is a
-          // multiple of 16, blocks are 128 wide); steps past the end read
-          // block 0 and multiply zeros
-          const int tb = t < s_end ? t : 0;
-          const int cb = min((col0 + ct * 16) >> 7, nbn - 1);  // a tile past n: any valid row
-          sc[u][i][ct] = wsc[i][(size_t)cb * nsteps + tb];
+          f32x4 pb = zero;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bf[i][ct][j], pb, 0, 0, 0);
+          const float sv = b.sc[i][ct];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][ct][mt][e] = __builtin_fmaf(sv, pb[e], acc[i][ct][mt][e]);
         }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t roff = (uint32_t)(mt * 16 + c16) * (uint32_t)k;
-        aw[u][mt][0] = ld16(ax, oka0 ? roff + ka : kOOB);
-        aw[u][mt][1] = ld16(ax, oka1 ? roff + ka + 64u : kOOB);
-      }
     }
+  };
+
+  for (int base = s_begin + wave; base < s_end; base += kNW * U) {
+    Step st[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      f16x8 bf[NMAT][CTW][4];
+    for (int u = 0; u < U; ++u) load(base + u * kNW, st[u]);
 #pragma unroll
-      for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-        for (int ct = 0; ct < CTW; ++ct)
-          fp8x32_to_f16(from_load_layout(bw[u][i][ct][0], src_addr), from_load_layout(bw[u][i][ct][1], src_addr),
-                        bf[i][ct]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f16x8 af[4];
-        fp8x32_to_f16(aw[u][mt][0], aw[u][mt][1], af);
-#pragma unroll
-        for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-          for (int ct = 0; ct < CTW; ++ct) {
-            f32x4 pb = zero;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bf[i][ct][j], pb, 0, 0, 0);
-            const float s = sc[u][i][ct];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][ct][mt][e] = __builtin_fmaf(s, pb[e], acc[i][ct][mt][e]);
-          }
-      }
-    }
+    for (int u = 0; u < U; ++u) compute(st[u]);
   }
 
   // fixed-order reduction over the workgroup's waves
@@ -232,7 +251,7 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
 
   if (p.ksplit > 1) {
     constexpr int kTile = 16 * MT * 16;
-    const size_t wg = (size_t)blockIdx.z * gridDim.x + blockIdx.x;
+    const size_t wg = (size_t)rb * ncb + cb;
     const __amdgpu_buffer_rsrc_t pres = rsrc(p.partial + wg * NMAT * p.ksplit * CTW * kTile,
                                              (size_t)NMAT * p.ksplit * CTW * kTile * 4);
     auto poff = [&](int i, int sp, int ct, int mt, int e) -> uint32_t {
@@ -247,7 +266,7 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int i = 0; i < NMAT; ++i)
-            st_coherent(pres, poff(i, blockIdx.y, ct, mt, e), acc[i][ct][mt][e]);
+            st_coherent(pres, poff(i, split, ct, mt, e), acc[i][ct][mt][e]);
     unsigned *cnt = p.counters + wg;
     wait_all_memory();
     unsigned old = 0;
@@ -314,6 +333,7 @@ hipError_t launch_one(const W8Args &p, dim3 grid, hipStream_t s) {
 
 template <int NMAT, int CTW>
 hipError_t launch_mt(const W8Args &p, int mt, dim3 grid, hipStream_t s) {
+  if constexpr (CTW == 4) return launch_one<4, NMAT, CTW>(p, grid, s);
   switch (mt) {
     case 1: return launch_one<1, NMAT, CTW>(p, grid, s);
     case 2: return launch_one<2, NMAT, CTW>(p, grid, s);
@@ -348,12 +368,19 @@ StreamPlan w8a8_plan(int n, int k) {
   return pl;
 }
 
+// Column tiles per launched workgroup: w8a8_ctw(n), or four for a single
+// matrix beyond 64 rows (each converted fragment then feeds four MFMAs).
+// The K plan stays that of w8a8_ctw(n) column tiles, so the K order of every
+// output does not change.
+static int w8a8_launch_ctw(int nmat, int m, int n) { return nmat == 1 && m > 64 ? 4 : w8a8_ctw(n); }
+
 size_t w8a8_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
-  // per workgroup: [nmat][ksplit][CTW][16*MT][16]
-  const int mt = m >= 64 ? 4 : cdiv(m, 16);
-  return pl.ksplit > 1
-             ? (size_t)pl.tiles * cdiv(m, 64) * nmat * pl.ksplit * w8a8_ctw(n) * 16 * mt * 16
-             : 0;
+  // per workgroup: [nmat][ksplit][CTW][16*MT][16], at most nmat*ksplit
+  // floats per element of the output padded to whole row and column blocks
+  if (pl.ksplit <= 1) return 0;
+  const size_t rows = m >= 64 ? (size_t)64 * cdiv(m, 64) : (size_t)16 * cdiv(m, 16);
+  const int ctw = w8a8_launch_ctw(nmat, m, n);
+  return (size_t)nmat * pl.ksplit * rows * 16 * ctw * cdiv(n, 16 * ctw);
 }
 
 hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const Fp8MatRef *w, void *y,
@@ -374,8 +401,11 @@ hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const 
   p.ksplit = pl.ksplit;
   p.steps_per_split = pl.steps_per_split;
   const int mt = m >= 64 ? 4 : cdiv(m, 16);
-  dim3 grid(pl.tiles, pl.ksplit, cdiv(m, 64));
-  if (w8a8_ctw(n) == 2)
+  const int ctw = w8a8_launch_ctw(nmat, m, n);
+  dim3 grid(cdiv(n, 16 * ctw) * pl.ksplit * cdiv(m, 64));
+  if (ctw == 4)
+    return nmat == 1 ? launch_mt<1, 4>(p, mt, grid, stream) : hipErrorInvalidValue;
+  if (ctw == 2)
     return nmat == 1 ? launch_mt<1, 2>(p, mt, grid, stream) : launch_mt<2, 2>(p, mt, grid, stream);
   return nmat == 1 ? launch_mt<1, 1>(p, mt, grid, stream) : launch_mt<2, 1>(p, mt, grid, stream);
 }
