@@ -51,6 +51,28 @@ def test_dequant_every_code_and_scale_exact(m):
     assert np.all(got[32:] & 0x7FFF == 0)
 
 
+@pytest.mark.parametrize("m", [8, 32, 96])  # streaming kernel; two-stage kernel: 32 rows, 64-row blocks
+def test_w4a4_dequant_every_code_and_scale(m):
+    """The fp16 dequantization of the W4A4 path (both operands NVFP4): rows
+    r < 32 of x are one-hot at K = r, so each output is one product a_r *
+    w[c][r] times the row scale -- exact in fp32 up to the row-scale
+    multiply -- and every code byte and finite scale byte of the weight
+    meets a unit activation.  Element by element within 2^-8 of the
+    oracle's value (the fp32 row-scale multiply and the bf16 rounding);
+    a wrong code, scale or fragment slot is off by far more."""
+    _say(f"w4a4 dequant identity m={m}")
+    w = _all_bytes_weight()
+    x = torch.zeros((m, 32), dtype=torch.bfloat16)
+    r = min(m, 32)
+    x[:r, :r] = torch.eye(r)
+    y = nv.nvfp4_gemm_w4a4(x.cuda(), g_weight(w))
+    sync()
+    _, ye = oracle.gemm_w4a4(bits(x), o_weight(w))
+    got = bf16_f64(bits(y))
+    assert np.all(np.abs(got - ye) <= 2.0 ** -8 * np.abs(ye)), np.max(np.abs(got - ye))
+    assert np.count_nonzero(ye[:r]) > 0.75 * ye[:r].size  # most products are nonzero
+
+
 # ---- W4A16 projection --------------------------------------------------------------
 
 SHAPES = [

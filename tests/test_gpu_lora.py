@@ -92,18 +92,21 @@ def test_dense_ffn_lora_single_pair(which):
     assert np.max(np.abs(got - ye) / bound) <= 1.0
 
 
-@pytest.mark.parametrize("m", [1, 3])
-def test_dense_ffn_lora_fused_epilogue_equals_composition(m):
+# ranks: gate and up at most 16 (their B rows are loaded with the batch's
+# weights) or above it (loaded in the epilogue), mismatched either way
+@pytest.mark.parametrize("m,rg,ru,rd", [(1, 16, 8, 24), (2, 16, 8, 24), (3, 16, 8, 24), (4, 16, 8, 24),
+                                        (1, 32, 8, 16), (2, 24, 32, 8), (3, 8, 24, 32), (4, 32, 16, 24)])
+def test_dense_ffn_lora_fused_epilogue_equals_composition(m, rg, ru, rd):
     """Up to four rows the GEMVs add the LoRA deltas in their epilogues; the
     result must equal, bit for bit, the same FFN composed from the separate
     entry points (gate and up GEMMs, LoRA deltas into the bf16 buffers,
     silu_mul, down GEMM, down delta): the same roundings in the same order."""
-    _say(f"ffn lora fused vs composed m={m}")
+    _say(f"ffn lora fused vs composed m={m} ranks {rg}/{ru}/{rd}")
     x, wg, wu, wd = si.workload("tiny", m=m)
     hidden, inter = x.shape[1], wg.n
-    pg, _ = _pair(inter, hidden, 16, 0, 2.0)
-    pu, _ = _pair(inter, hidden, 8, 1, -1.5)
-    pd, _ = _pair(hidden, inter, 24, 2, 0.5)
+    pg, _ = _pair(inter, hidden, rg, 0, 2.0)
+    pu, _ = _pair(inter, hidden, ru, 1, -1.5)
+    pd, _ = _pair(hidden, inter, rd, 2, 0.5)
     xd = x.cuda()
     Wg, Wu, Wd = g_weight(wg), g_weight(wu), g_weight(wd)
     y = nv.dense_ffn_forward_lora(xd, Wg, Wu, Wd, pg, pu, pd)
