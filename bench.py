@@ -244,6 +244,39 @@ def measure_mfma_peak():
     }
 
 
+def measure_read_floor(sizes, steps, warmup):
+    """HBM read rate of a launch that only streams: nvfp4_probe_read over
+    each byte count in `sizes`, back to back on cold buffers (rotated so
+    that their sum exceeds the caches), timed like the FFN.  This is what a
+    single launch of that size reaches with nothing but loads -- ramp,
+    latency and drain included -- the practical ceiling for the
+    memory-bound launches beside the 8 TB/s of the specification."""
+    import torch
+
+    import nvfp4_weight_dense_amd as nv
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    top = max(sizes)
+    top = (top + 15) // 16 * 16
+    nrep = max(2, math.ceil(REPLICA_BYTES / top))
+    # bytes 0x01: every 32-bit word is 0x01010101, and a lane folds sixteen
+    # of them (or zeros) by xor, so the fold is 0 and never equals 0x5A5A5A5A
+    bufs = [torch.full((top,), 1, dtype=torch.uint8, device=dev) for _ in range(nrep)]
+    out = []
+    for nb in sizes:
+        nb16 = nb // 16 * 16
+        ms = _time_loop(lambda b: nv.nvfp4_probe_read(b, nb16, 0x5A5A5A5A, sink, stream), bufs,
+                        steps, warmup, stream)
+        out.append({"bytes": nb16, "us": ms * 1e3, "gbs": nb16 / (ms * 1e-3) / 1e9})
+    assert float(sink.abs().sum()) == 0.0
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "k_read_probe (nvfp4_probe_read): 256-lane workgroups, four 16-byte loads "
+                      "in flight per lane, nothing else", "per_launch": out}
+
+
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in (DOMINANT_KERNEL_SRC,
@@ -272,6 +305,7 @@ def _traffic_per_launch():
 
 # launch patterns for the rocprofv3 counter passes: (workload, extra measure_ffn args)
 KERNEL_RUNS = {
+    "decode": ("decode", {}),
     "w4a4": ("w4a4", dict(m=1, w4a4=True)),
     "w8a8": ("w8a8", dict(m=1, w8a8=True)),
     "q2": ("decode", dict(m=1, q2=True)),
@@ -289,8 +323,9 @@ KERNEL_RUNS = {
 def traffic_run(steps, what="gemv"):
     """Launch pattern for the rocprofv3 counter passes: `steps` launches of
     the dominant kernel over rotating cold replicas (what="gemv"), `steps`
-    whole FFNs of one workload (KERNEL_RUNS), or `steps` runs of the MFMA
-    probe (what="probe"); then `steps` plain device copies of COPY_BYTES,
+    whole FFNs of one workload (KERNEL_RUNS), `steps` runs of the MFMA
+    probe (what="probe") or pairs of read-probe launches over the decode
+    weight byte counts (what="read"); then `steps` plain device copies of COPY_BYTES,
     whose counter readings calibrate the memory counters against a
     transfer of known size.  No clock ramp: every dispatch is counted."""
     import torch
@@ -303,6 +338,16 @@ def traffic_run(steps, what="gemv"):
         sink = torch.zeros(256, dtype=torch.float32, device=dev)
         for _ in range(steps):
             nv.nvfp4_probe_mfma_bf16(2 * cus, 2000, sink)
+        torch.cuda.synchronize()
+    elif what == "read":
+        # the read probe over the decode FFN's two weight byte counts, cold
+        sink = torch.zeros(256, dtype=torch.float32, device=dev)
+        sizes = (56623104, 28311552)
+        bufs = [torch.full((sizes[0],), 1, dtype=torch.uint8, device=dev) for _ in range(8)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            for nb in sizes:
+                nv.nvfp4_probe_read(bufs[(2 * i + (nb == sizes[1])) % 8], nb, 0x5A5A5A5A, sink)
         torch.cuda.synchronize()
     else:
         if what == "gemv":
@@ -485,7 +530,7 @@ def main():
                     help="comma-separated workload names to time besides the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--traffic-run", nargs="?", const="gemv", default=None,
-                    choices=("gemv", "probe") + tuple(KERNEL_RUNS),
+                    choices=("gemv", "probe", "read") + tuple(KERNEL_RUNS),
                     help="only launch the dominant kernel (or whole FFNs of one workload) "
                          "and a calibration copy (for rocprofv3 --pmc passes)")
     args = ap.parse_args()
@@ -509,8 +554,18 @@ def main():
     head, ctx = measure_ffn("decode", args.steps, args.warmup)
     checks = [(head, ctx["check"])]
     roof = measure_dominant_kernel(ctx, args.steps, args.warmup)
+    gu_bytes = weight_bytes(ctx["weights"][0][0]) + weight_bytes(ctx["weights"][0][1])
+    d_bytes = weight_bytes(ctx["weights"][0][2])
     del ctx
     mfma = measure_mfma_peak()
+    # the decode FFN's two launches, and one launch of all its bytes
+    floor = measure_read_floor([gu_bytes, d_bytes, gu_bytes + d_bytes], args.steps, args.warmup)
+    f_gu, f_d, f_all = floor["per_launch"]
+    roof["read_floor_gbs"] = f_gu["gbs"]
+    roof["frac_of_read_floor"] = roof["achieved"] / f_gu["gbs"]
+    head["read_floor_two_launches_us"] = f_gu["us"] + f_d["us"]
+    head["read_floor_one_launch_us"] = f_all["us"]
+    head["frac_of_read_floor_two_launches"] = (f_gu["us"] + f_d["us"]) / (head["ms_per_step"] * 1e3)
     workloads = []
     only = None if args.only is None else set(args.only.split(","))
     invariance = {}
@@ -576,6 +631,10 @@ def main():
         "hbm_frac": head["hbm_frac"],
         "roofline": roof,
         "mfma_peak": mfma,
+        "hbm_read_floor": floor,
+        "read_floor_two_launches_us": head["read_floor_two_launches_us"],
+        "read_floor_one_launch_us": head["read_floor_one_launch_us"],
+        "frac_of_read_floor_two_launches": head["frac_of_read_floor_two_launches"],
         "cpu_baseline": cpu,
         "workloads": workloads,
     }

@@ -328,6 +328,20 @@ void nvfp4_release(void);
 int nvfp4_probe_mfma_bf16(int32_t workgroups, int32_t iters, float *sink,
                           void *stream);
 
+/* Measurement aid, not a step of the FFN: enqueues one streaming read of
+ * `bytes` bytes of device memory at src (16-byte aligned; bytes a positive
+ * multiple of 16): workgroups of 256 lanes, each lane four 16-byte loads in
+ * flight, nothing else.  Timing back-to-back calls on buffers that no cache
+ * holds gives the HBM read rate a single launch of that size reaches --
+ * ramp, latency and drain included -- which benchmarks print beside the
+ * specification's 8 TB/s for the memory-bound kernels.  The loaded words are
+ * folded with xor; sink (device fp32 [256]) is written only if the fold
+ * equals `never`, a word the caller's buffer is not filled with.  src is
+ * only read.  NVFP4_EINVAL for a null pointer, a bad size or a misaligned
+ * src. */
+int nvfp4_probe_read(const void *src, int64_t bytes, uint32_t never, float *sink,
+                     void *stream);
+
 /* ABI version of this header (bumped on incompatible change). */
 int32_t nvfp4_abi_version(void);
 

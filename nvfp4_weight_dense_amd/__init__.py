@@ -41,6 +41,7 @@ __all__ = [
     "dense_ffn_forward_w8a8", "Q2Weight", "q2_gemm_w2a16", "dense_ffn_forward_q2",
     "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
     "nvfp4_probe_mfma_bf16",
+    "nvfp4_probe_read",
 ]
 
 
@@ -168,6 +169,8 @@ def load_library(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     L.nvfp4_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
     L.nvfp4_probe_mfma_bf16.restype = ctypes.c_int
+    L.nvfp4_probe_read.argtypes = [vp, i64, ctypes.c_uint32, vp, vp]
+    L.nvfp4_probe_read.restype = ctypes.c_int
     L.nvfp4_last_error.argtypes = []
     L.nvfp4_last_error.restype = ctypes.c_char_p
     L.nvfp4_release.argtypes = []
@@ -269,6 +272,19 @@ def nvfp4_probe_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor, strea
     if sink.dtype != torch.float32 or sink.numel() < 256 or not sink.is_cuda:
         raise ValueError("sink: expected a float32 GPU tensor of at least 256 elements")
     _check(L.nvfp4_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _stream(stream)))
+
+
+def nvfp4_probe_read(src: torch.Tensor, nbytes: int, never: int, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue one streaming read of the first nbytes bytes of src (a
+    measurement aid; a contiguous GPU tensor, nbytes a multiple of 16 within
+    it); sink is a float32 GPU tensor of at least 256 elements, written only
+    if the xor fold of the bytes equals `never`."""
+    L = load_library()
+    if not src.is_cuda or not src.is_contiguous() or nbytes > src.numel() * src.element_size():
+        raise ValueError("src: expected a contiguous GPU tensor holding nbytes bytes")
+    if sink.dtype != torch.float32 or sink.numel() < 256 or not sink.is_cuda:
+        raise ValueError("sink: expected a float32 GPU tensor of at least 256 elements")
+    _check(L.nvfp4_probe_read(_ptr(src), int(nbytes), int(never) & 0xFFFFFFFF, _ptr(sink), _stream(stream)))
 
 
 def nvfp4_gemm_w4a16(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):

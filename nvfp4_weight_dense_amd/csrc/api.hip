@@ -524,6 +524,15 @@ int nvfp4_probe_mfma_bf16(int32_t workgroups, int32_t iters, float *sink, void *
   return hip_status(launch_mfma_probe(workgroups, iters, sink, (hipStream_t)stream), "probe launch");
 }
 
+int nvfp4_probe_read(const void *src, int64_t bytes, uint32_t never, float *sink, void *stream) {
+  g_err.clear();
+  if (!src || !sink) return fail(NVFP4_EINVAL, "read probe: null pointer");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(NVFP4_EINVAL, "read probe: bytes must be a positive multiple of 16");
+  if (((uintptr_t)src & 15u) != 0) return fail(NVFP4_EINVAL, "read probe: src must be 16-byte aligned");
+  if (bytes / 16 > (int64_t)0xFFFFFFFFll * 1024) return fail(NVFP4_EINVAL, "read probe: too many bytes");
+  return hip_status(launch_read_probe(src, (size_t)bytes, never, sink, (hipStream_t)stream), "read probe launch");
+}
+
 const char *nvfp4_last_error(void) { return g_err.c_str(); }
 
 void nvfp4_release(void) {

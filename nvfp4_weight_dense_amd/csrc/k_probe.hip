@@ -1,7 +1,9 @@
-// k_probe.hip -- a measurement aid, not a step of the FFN: the bf16 matrix
-// throughput this part reaches in practice, to print beside the 2.5 PFLOP/s
-// specification when a many-row kernel's fraction of the peak is reported.
+// k_probe.hip -- measurement aids, not steps of the FFN: the bf16 matrix
+// throughput and the HBM read rate this part reaches in practice, to print
+// beside the specification's peaks (2.5 PFLOP/s, 8 TB/s) when a kernel's
+// fraction of its roofline is reported.
 //
+// MFMA probe:
 // Each wave runs `iters` rounds of four independent
 // v_mfma_f32_32x32x16_bf16 (32x32x16 multiply-adds, 32768 flops each) on
 // register operands: no memory traffic, no LDS, no dependence between the
@@ -38,7 +40,36 @@ __global__ __launch_bounds__(256) void k_mfma_probe(int iters, float *sink) {
   if (s == -1.0f) sink[threadIdx.x] = s;
 }
 
+// Read probe: one pass over n16 16-byte items with nothing else to do.
+// Workgroup b reads items [b * 1024, (b + 1) * 1024): each lane has four
+// 16-byte loads in flight (256 lanes x 4, consecutive lanes on consecutive
+// items), folds them with xor and stores only if the fold equals a value
+// the caller's buffer is never filled with -- so the loads stay, and the
+// probe writes nothing in practice.
+constexpr int kReadPerLane = 4;
+__global__ __launch_bounds__(256) void k_read_probe(const uint4 *src, size_t n16, uint32_t never, float *sink) {
+  const size_t base = (size_t)blockIdx.x * (256 * kReadPerLane) + threadIdx.x;
+  uint4 v[kReadPerLane];
+#pragma unroll
+  for (int i = 0; i < kReadPerLane; ++i) {
+    const size_t idx = base + (size_t)i * 256;
+    v[i] = idx < n16 ? src[idx] : uint4{0u, 0u, 0u, 0u};
+  }
+  uint32_t f = 0;
+#pragma unroll
+  for (int i = 0; i < kReadPerLane; ++i) f ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  if (f == never) sink[threadIdx.x] = 1.0f;
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t never, float *sink, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  const size_t per_wg = 256 * kReadPerLane;
+  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)((n16 + per_wg - 1) / per_wg)), dim3(256), 0, stream,
+                     (const uint4 *)src, n16, never, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(int workgroups, int iters, float *sink, hipStream_t stream) {
   hipLaunchKernelGGL(k_mfma_probe, dim3(workgroups), dim3(256), 0, stream, iters, sink);

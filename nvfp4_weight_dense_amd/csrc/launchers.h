@@ -213,5 +213,7 @@ hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat,
 // four waves, each wave iters x 4 v_mfma_f32_32x32x16_bf16.  sink: 256
 // floats, never written in practice.
 hipError_t launch_mfma_probe(int workgroups, int iters, float *sink, hipStream_t stream);
+// One streaming read of `bytes` (a multiple of 16) at src; see k_probe.hip.
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t never, float *sink, hipStream_t stream);
 
 }  // namespace nvfp4
