@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kNW * 64) void k_stream(StreamArgs p) {
 // current step is dequantized and multiplied, and only one step's raw bytes
 // wait in registers.  Activation fragments are formed one (row tile, K
 // sub-step) at a time and weight fragments one K sub-step at a time.
-template <int MT, int NMAT, int CTW>
+template <int MT, int NMAT, int CTW, int NS>
 __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -470,35 +470,48 @@ __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
   };
 
   // wave w takes steps s_begin + w, s_begin + w + 4, ... in increasing
-  // order.  The loop body is one basic block (loads of the next step, then
-  // the current step's arithmetic, twice), so each step waits only for its
-  // own loads; loads past the wave's last step are out of range and fetch
+  // order, NS - 1 of them in flight ahead of the one being computed.  The
+  // loop body is one basic block (NS times: the loads of a later step, then
+  // the current step's arithmetic), so each step waits only for its own
+  // loads; loads past the wave's last step are out of range and fetch
   // nothing.
   const int first = s_begin + wave;
   const int nmine = first < s_end ? (s_end - first + kNW - 1) / kNW : 0;
-  Step b0, b1;
-  load(first, b0);
-  int t = first;
-  for (int i = 0; i + 2 <= nmine; i += 2, t += 2 * kNW) {
-    // the barriers keep the scheduler from sinking a step's loads into the
-    // arithmetic that they are meant to overlap
-    load(t + kNW, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(t + 2 * kNW, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b1);
-    __builtin_amdgcn_sched_barrier(0);
+  Step buf[NS];
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) load(first + s * kNW, buf[s]);
+  int i = 0;
+  for (int t = first; i + NS <= nmine; i += NS, t += NS * kNW) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      // the barriers keep the scheduler from sinking a step's loads into
+      // the arithmetic that they are meant to overlap
+      load(t + (s + NS - 1) * kNW, buf[(s + NS - 1) % NS]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[s]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (nmine & 1) compute(b0);
+  // the last nmine - i (< NS) steps are already loaded, in buf[0..]
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nmine - i) compute(buf[s]);
 
   stream_finish<MT, NMAT, CTW, true>(p, acc, lane, wave, col0, row0, rb * cdiv(p.n, 16 * CTW) + cb, split);
 }
 
+// load stages of k_stream_tall: two.  Three or four stages (the single-matrix
+// tiles stay at two waves per SIMD with four) measured no faster at 32, 64 or
+// 512 rows; three on the gate+up tiles cost the second wave per SIMD.
+template <int MT, int NMAT, int CTW>
+constexpr int tall_stages() {
+  return 2;
+}
+
 template <int MT, int NMAT, int CTW>
 hipError_t launch_tall(const StreamArgs &p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_stream_tall<MT, NMAT, CTW>), grid, dim3(kNW * 64), 0, s, p);
+  hipLaunchKernelGGL((k_stream_tall<MT, NMAT, CTW, tall_stages<MT, NMAT, CTW>()>), grid, dim3(kNW * 64), 0, s,
+                     p);
   return hipGetLastError();
 }
 
