@@ -166,7 +166,8 @@ def _quant_rows(m, k, seed):
     return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("m,k", [(1, 32), (5, 4096), (7, 14336), (512, 4096), (4, 20480), (3, 67136)])
+@pytest.mark.parametrize("m,k", [(1, 32), (5, 4096), (7, 14336), (512, 4096), (4, 20480), (3, 67136),
+                                 (64, 4096), (100, 14336)])
 def test_quantize_rows_bit_exact(m, k):
     _say(f"quantize m={m} k={k}")
     x = _quant_rows(m, k, seed=m * 7 + k)

@@ -48,7 +48,7 @@ def _rows_with_edge_cases(m, k, seed):
     return x
 
 
-@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (7, 4096), (5, 14336), (2, 17408 * 2)])
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (7, 4096), (5, 14336), (2, 17408 * 2), (64, 4096), (100, 14336)])
 def test_fp8_quantizer_bit_exact(m, k):
     _say(f"fp8 quantize m={m} k={k}")
     x = _rows_with_edge_cases(m, k, seed=m + k)
