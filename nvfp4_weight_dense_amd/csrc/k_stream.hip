@@ -361,8 +361,6 @@ template <int MT, int NMAT, int CTW, int NS>
 __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int c16 = lane & 15;
-  const int g = lane >> 4;
   const int src_addr = load_layout_src_addr(lane);
   const uint32_t lrow = (uint32_t)(lane >> 2), lpiece = (uint32_t)(lane & 3);
   const int k = p.k;
@@ -395,8 +393,12 @@ __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
   const __amdgpu_buffer_rsrc_t ax = rsrc(p.xc + (size_t)row0 * kb2, (size_t)nrows * kb2);
   const __amdgpu_buffer_rsrc_t axs = rsrc(p.xs + (size_t)row0 * kb16, (size_t)nrows * kb16);
 
-  // one step's raw bytes: weights in the row-contiguous load layout,
-  // activations already in MFMA layout (lane (c, g): row c, 32 K at 32 g)
+  // one step's raw bytes, weights and activations both in the row-contiguous
+  // load layout (lane s: row s/4, the 16 bytes at K 32 (s%4) of the step);
+  // ds_bpermute hands lane (c, g) its operand bytes.  Loading the
+  // activations in the operand layout instead (lane (c, g) reading row c
+  // directly, four neighbouring lanes on four rows) cost 11% at 512 rows
+  // (W4A4 FFN 340 -> 302 us with the permute), as it did for the weights.
   struct Step {
     uint4 bw[NMAT][CTW];
     uint32_t bsc[NMAT][CTW];
@@ -404,8 +406,6 @@ __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
     uint32_t asc[MT];
   };
   auto load = [&](int t, Step &b) {
-    const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
-    const bool ok = t < s_end && kk < (uint32_t)k;
     const uint32_t kl = (uint32_t)t * 128u + 32u * lpiece;
     const bool okl = t < s_end && kl < (uint32_t)k;
 #pragma unroll
@@ -418,9 +418,9 @@ __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
       }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t r = (uint32_t)(mt * 16 + c16);
-      b.aw[mt] = ld16(ax, ok ? r * kb2 + (kk >> 1) : kOOB);
-      b.asc[mt] = ld2(axs, ok ? r * kb16 + (kk >> 4) : kOOB);
+      const uint32_t r = (uint32_t)(mt * 16) + lrow;
+      b.aw[mt] = ld16(ax, okl ? r * kb2 + (kl >> 1) : kOOB);
+      b.asc[mt] = ld2(axs, okl ? r * kb16 + (kl >> 4) : kOOB);
     }
   };
 
@@ -443,8 +443,12 @@ __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
         wsc[i][ct] = e4m3x2_to_f16x2(from_load_layout(b.bsc[i][ct], src_addr));
       }
     f16x2 asc[MT];
+    uint4 aw[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) asc[mt] = e4m3x2_to_f16x2(b.asc[mt]);
+    for (int mt = 0; mt < MT; ++mt) {
+      asc[mt] = e4m3x2_to_f16x2(from_load_layout(b.asc[mt], src_addr));
+      aw[mt] = from_load_layout(b.aw[mt], src_addr);
+    }
     // K sub-step outermost, as in k_stream
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(kNW * 64) void k_stream_tall(StreamArgs p) {
         }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t word = j == 0 ? b.aw[mt].x : j == 1 ? b.aw[mt].y : j == 2 ? b.aw[mt].z : b.aw[mt].w;
+        const uint32_t word = j == 0 ? aw[mt].x : j == 1 ? aw[mt].y : j == 2 ? aw[mt].z : aw[mt].w;
         const f16x8 af = dequant8_f16(word, asc[mt][j >> 1]);
 #pragma unroll
         for (int i = 0; i < NMAT; ++i)
