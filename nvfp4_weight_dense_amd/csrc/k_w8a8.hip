@@ -25,8 +25,9 @@
 //     the m=1 FFN 53.6 us with such loads, 49.5 us with these).  So lane s
 //     loads 16 bytes at 16(s%4) (and 64 + 16(s%4)) of row s/4 -- four
 //     lanes cover 64 contiguous bytes -- and a ds_bpermute hands lane
-//     (c, g) the registers of lane 4c + g.  Activations are few rows, read
-//     from cache, and are loaded in place.
+//     (c, g) the registers of lane 4c + g.  Activation rows are loaded the
+//     same way (loaded in the operand layout they cost 14% at 512 rows:
+//     FFN 394 -> 339 us, 93.5 -> 89.7 us at 64 rows).
 //     The hardware FP8 -> fp16 conversion
 //     (exact: an E4M3 value has 4 significant bits and lies in
 //     [2^-9, 448]) turns them into four operand fragments of
@@ -153,14 +154,12 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
     float sc[NMAT][CTW];
   };
   auto load = [&](int t, Step &b) {
-    // K offsets of the 16-byte loads: weights (load layout), activations
-    // (operand layout); each is checked on its own (k is only a multiple
-    // of 32, so the second 64 bytes of the last step can lie past k)
+    // K offsets of this lane's 16-byte loads (load layout, weights and
+    // activations alike); each half is checked on its own (k is only a
+    // multiple of 32, so the second 64 bytes of the last step can lie past k)
     const bool in_split = t < s_end;
     const uint32_t kw = (uint32_t)t * 128u + 16u * (uint32_t)(lane & 3);
-    const uint32_t ka = (uint32_t)t * 128u + 16u * (uint32_t)g;
     const bool okw0 = in_split && kw < (uint32_t)k, okw1 = in_split && kw + 64u < (uint32_t)k;
-    const bool oka0 = in_split && ka < (uint32_t)k, oka1 = in_split && ka + 64u < (uint32_t)k;
 #pragma unroll
     for (int i = 0; i < NMAT; ++i)
 #pragma unroll
@@ -180,9 +179,10 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
       }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t roff = (uint32_t)(mt * 16 + c16) * (uint32_t)k;
-      b.aw[mt][0] = ld16(ax, oka0 ? roff + ka : kOOB);
-      b.aw[mt][1] = ld16(ax, oka1 ? roff + ka + 64u : kOOB);
+      // activations in the weights' load layout too (row wrow, K offsets kw)
+      const uint32_t roff = (uint32_t)(mt * 16 + (int)wrow) * (uint32_t)k;
+      b.aw[mt][0] = ld16(ax, okw0 ? roff + kw : kOOB);
+      b.aw[mt][1] = ld16(ax, okw1 ? roff + kw + 64u : kOOB);
     }
   };
   // P_b = the step's four MFMAs from zero, then acc = fma(scale_b, P_b, acc)
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kNW * 64) void k_w8a8(W8Args p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f16x8 af[4];
-      fp8x32_to_f16(b.aw[mt][0], b.aw[mt][1], af);
+      fp8x32_to_f16(from_load_layout(b.aw[mt][0], src_addr), from_load_layout(b.aw[mt][1], src_addr), af);
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
