@@ -84,6 +84,10 @@ __global__ __launch_bounds__(kNW * 64) void k_q2(Q2Args p) {
   const int g = lane >> 4;
   const int src_addr = load_layout_src_addr(lane);
   constexpr bool kRowLoads = MT == 1;
+  // activation rows: row-contiguous loads plus the permute for 17..48 rows
+  // (FFN m=32 124 -> 112 us); at one row tile and at four they measured
+  // 1.5-2 us slower or even, so those load the operand layout directly
+  constexpr bool kRowAct = MT == 2 || MT == 3;
   const uint32_t lrow = kRowLoads ? (uint32_t)(lane >> 2) : (uint32_t)c16;  // weight row loaded
   const uint32_t lpiece = kRowLoads ? (uint32_t)(lane & 3) : (uint32_t)g;   // 32-K chunk loaded
   const int k = p.k;
@@ -122,10 +126,11 @@ __global__ __launch_bounds__(kNW * 64) void k_q2(Q2Args p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = base + u * kNW;
-      const uint32_t kk = (uint32_t)t * 128u + 32u * (uint32_t)g;
-      const bool ok = t < s_end && kk < (uint32_t)k;
       const uint32_t kl = (uint32_t)t * 128u + 32u * lpiece;  // K of this lane's weight load
       const bool okl = t < s_end && kl < (uint32_t)k;
+      const uint32_t ka = (uint32_t)t * 128u + 32u * (kRowAct ? (uint32_t)(lane & 3) : (uint32_t)g);
+      const bool oka = t < s_end && ka < (uint32_t)k;
+      const uint32_t arow = kRowAct ? (uint32_t)(lane >> 2) : (uint32_t)c16;
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(kNW * 64) void k_q2(Q2Args p) {
         }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t off = ok ? ((uint32_t)(mt * 16 + c16) * (uint32_t)k + kk) * 2u : kOOB;
+        const uint32_t off = oka ? (((uint32_t)(mt * 16) + arow) * (uint32_t)k + ka) * 2u : kOOB;
 #pragma unroll
         for (int q = 0; q < 4; ++q) aw[u][mt][q] = ld16(ax, off + 16u * q);
       }
@@ -161,6 +166,12 @@ __global__ __launch_bounds__(kNW * 64) void k_q2(Q2Args p) {
           bf[i][ct][2] = dequant_q2x8(w.y & 0xFFFFu, d, m2d);
           bf[i][ct][3] = dequant_q2x8(w.y >> 16, d, m2d);
         }
+      if constexpr (kRowAct) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) aw[u][mt][q] = from_load_layout(aw[u][mt][q], src_addr);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
