@@ -71,7 +71,7 @@ struct StreamArgs {
   const uint8_t *codes1, *scales1;
   float ts0, ts1;
   void *y;
-  float *partial;         // [nmat][ksplit][m][n]
+  float *partial;         // per workgroup tile [nmat][ksplit][CTW][16*MT rows][16 columns]
   unsigned *counters;     // [row blocks][column blocks], zero between calls
   int ksplit, steps_per_split;
 };

@@ -23,11 +23,13 @@ struct ActRef {
   const float *row_scale;    // [m]
 };
 
-// Weight-streaming projection for few rows, nmat = 1 (y = x.W^T) or 2
-// (y = bf16(silu(bf16(x.W0^T)) * bf16(x.W1^T))).  With ksplit > 1,
-// `partial` must hold stream_partial_floats(...) floats and `counters`
-// stream_counter_words(...) words that are zero on entry (the kernel leaves
-// them zero).  The plan depends on (n, k) only.
+// Weight-streaming projection, nmat = 1 (y = x.W^T) or 2
+// (y = bf16(silu(bf16(x.W0^T)) * bf16(x.W1^T))): bf16 activations up to 16
+// rows; NVFP4 activations (W4A4) at every row count, from 17 rows through
+// the pipelined many-row variant with the same per-output schedule.  With
+// ksplit > 1, `partial` must hold stream_partial_floats(...) floats and
+// `counters` stream_counter_words(...) words that are zero on entry (the
+// kernel leaves them zero).  The plan depends on (n, k) only.
 // Reduction length below which no projection splits K over workgroups
 // (NVFP4_SPLITK_MIN_K, read once; 0 = split wherever the plan wants).
 // Every split plan below honours it; it depends on k only, so the W4A4 and
