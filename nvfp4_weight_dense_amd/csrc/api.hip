@@ -290,10 +290,7 @@ size_t proj_scratch_bytes(int m, int n, int k, int nmat, Path path) {
 
 // split-K arrival counters a projection needs (zero on entry, left zero)
 size_t proj_counter_words(int m, int n, int k, int nmat, Path path) {
-  if (path == Path::Small) {
-    const SmallPlan pl = smallm_plan(m, n, k, nmat);
-    return pl.ksplit > 1 ? (size_t)pl.tiles : 0;
-  }
+  if (path == Path::Small) return smallm_counter_words(smallm_plan(m, n, k, nmat));
   if (path == Path::StreamLds) {
     const LdsPlan pl = stream_lds_plan(m, n, k, nmat);
     return pl.ksplit > 1 ? stream_lds_counter_words(pl) : 0;
@@ -314,8 +311,8 @@ int run_proj(const ActRef &a, int m, int k, int n, int nmat, const MatRef *w, vo
   if (path == Path::Small) {
     SmallPlan pl = smallm_plan(m, n, k, nmat);
     unsigned *counters = counters_in;
-    if (pl.ksplit > 1 && !counters) {
-      int rc = counters_get((size_t)pl.tiles, &counters);
+    if (!counters) {
+      int rc = counters_get(smallm_counter_words(pl), &counters);
       if (rc) return rc;
     }
     return hip_status(launch_smallm(a.x_bf16, m, k, n, nmat, w, y, (float *)scratch, counters, pl, s),

@@ -2,41 +2,39 @@
 //
 // Regime: the pages' small-m edge (page layers/dense_ffn_prefill.rs,
 // `w4a16_prefill_gemm`: m <= 64 takes the small-m kernels).  With tens of
-// rows the weights are still the whole HBM stream, so the kernel is built
-// around moving them at full bandwidth:
+// rows the weights are still the whole HBM stream and every weight is
+// dequantized exactly once, so the VALU work of the dequantization is as
+// large as the matrix-core work: one 8-weight fragment per lane (16 VALU
+// instructions) feeds MT 16x16x32 MFMAs.  Both pipes only stay busy when
+// every SIMD holds two waves with the same amount of work, so the kernel is
+// built around an even split:
 //
-//   * weights move in groups of four 64-K steps -- 128 code bytes, one cache
-//     line, of each weight row -- straight into LDS with 16-byte LDS-DMA
-//     loads (buffer_load ... lds; one instruction moves eight whole lines).
-//     Each wave owns its region of a two-slot ring and requests a group
-//     three steps before use.
-//     Within a row the eight 16-byte chunks are XOR-swizzled by row, which
-//     keeps the per-lane 16-byte reads in MFMA operand order free of bank
-//     conflicts.  A group's E4M3 scales (16 bytes per row) come in one
-//     register load.
-//   * a workgroup is two waves; each wave owns 32 columns of gate and of up
-//     (fused silu epilogue), or 64 columns of one matrix, for all 32 or 64
-//     rows (v_mfma_f32_32x32x16_bf16); three workgroups share a CU, and K
-//     is split until every SIMD has a wave.
-//   * the activation chunk of a step (rows x 64 K, bf16) is loaded into
-//     registers two steps ahead and written into a two-slot LDS ring one
-//     step ahead; the step barrier waits for LDS operations only, so weight
-//     and activation requests stay in flight.
-//   * deep K is split over workgroups (blockIdx.y) by whole weight groups;
-//     each split writes fp32 partial tiles.  For gate+up (two splits at
-//     most on these shapes) the last split to arrive sums them in split
-//     order and runs the silu epilogue; for one matrix a second launch sums
-//     them in split order over the whole output in parallel.
+//   * one workgroup of eight waves per CU (about 100 KB of LDS keeps it to
+//     one), at most 256 workgroups.  Output columns come in column groups
+//     (64 gate columns and the same 64 up columns, or 128 columns of one
+//     matrix) and K in units of 256; the (group, unit) pairs, group-major,
+//     are cut into equal contiguous ranges, one per workgroup (stream-K).
+//     A range is walked in segments, one per column group it touches.
+//   * wave w owns column slot w % 4 -- 16 gate and 16 up columns (fused
+//     silu epilogue), or 32 columns of one matrix -- for all rows, and K
+//     half w / 4 of every unit, so the two waves on a SIMD do the same
+//     work.  Within its 128 K of a unit, lane group g = lane / 16 of a wave
+//     takes K 32g .. 32g + 31 and MFMA step s sums K {32g + 8s .. + 7 : g};
+//     the activation fragments are read at the same K, so each step is an
+//     ordinary 16x16x32 product over a permuted K.
+//   * weights move as whole 128-byte lines (eight lanes per line) and the
+//     activations of a unit (rows x 256 K, bf16) as whole rows; both are
+//     requested three units ahead and written to a two-unit LDS ring one
+//     unit ahead, in the order the MFMA operands are read back (one 16-byte
+//     read per lane and fragment, bank-conflict free); the unit barrier
+//     waits for LDS operations only.
+//   * at the end of a segment the two K halves are summed through LDS.  A
+//     segment that covers its whole column group is finished at once; a
+//     partial one is stored as an fp32 piece, and the last of a group's
+//     pieces to arrive sums them in K order and finishes the group.
 //
-// Lane (c = lane%32, h = lane/32) holds for weight row col+c the 32 codes at
-// K offset 32h of a step; MFMA j sums K offsets {8j..8j+7} U
-// {32+8j..32+8j+7}, and the A fragment of row tile mt is read at LDS row
-// 32mt+c at the same offsets.  Requires k % 64 == 0 (whole steps).  When
-// k % 256 != 0 the last weight group of the last split is partial: the
-// steps it lacks are never run (the code bytes its requests bring from
-// beyond each row's end are never read), and the scales come a dword (one
-// step) at a time, since the scale rows are then only 4-byte aligned and a
-// 16-byte load could straddle the end of the last row.
+// Requires k % 64 == 0 (K pieces of 32 are whole or absent); K beyond k,
+// rows beyond m and columns beyond n read as zero and are not stored.
 #include <algorithm>
 #include <type_traits>
 
@@ -47,26 +45,25 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int kNW = 2;                     // waves per workgroup
-constexpr int kStep = 64;                  // K elements per step
-constexpr int kGroup = 4;                  // steps per weight group
-constexpr int kRing = 2;                   // weight groups in the LDS ring
-constexpr int kRowBytes = kStep * 2 + 16;  // LDS row pitch of the activation chunk
-constexpr int kNB = 2;                     // B tiles per wave
-constexpr int kTileBytes = 32 * 32 * kGroup;  // one B tile's group: 32 rows x 128 B
+constexpr int kNW = 8;                    // waves per workgroup
+constexpr int kColSlots = 4;              // column slots per workgroup
+constexpr int kUnitK = 256;               // K per unit (two halves of 128)
+constexpr int kMaxWG = 256;               // workgroups: one per CU
+constexpr int kNS = 4;                    // weight stages: three units in flight
+static_assert(kNS == 4, "the unit loop is written out for four stages");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct SmallArgs {
   const void *x;  // bf16 [m][k]
   int m, k, n;
-  const uint8_t *codes0, *scales0;  // gate (SWIGLU) or the matrix
-  const uint8_t *codes1, *scales1;  // up (SWIGLU) or unused
+  const uint8_t *codes0, *scales0;  // gate (two matrices) or the matrix
+  const uint8_t *codes1, *scales1;  // up (two matrices) or unused
   float ts0, ts1;
   void *y;
-  float *partial;      // [tiles][ksplit][kNW][kNB * 32MT * 32]
-  unsigned *counters;  // [tiles], zero between calls
-  int ksplit, steps_per_split;
+  float *partial;      // [nwg][2][kColSlots][2 MT][64 lanes][4]
+  unsigned *counters;  // [groups], zero between calls
+  int kunits, units, nwg;
 };
 
 __device__ __forceinline__ void st16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
@@ -77,307 +74,345 @@ __device__ __forceinline__ f32x4 ld16_coherent(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCoherent));
 }
 
-template <int MT, bool SWIGLU>
+// first unit of workgroup w's range (range w is [begin(w), begin(w + 1)))
+__host__ __device__ __forceinline__ int range_begin(int units, int nwg, int w) {
+  return (int)(((int64_t)units * w) / nwg);
+}
+// the workgroup whose range holds unit u: the w with begin(w) <= u < begin(w + 1)
+__host__ __device__ __forceinline__ int range_owner(int units, int nwg, int u) {
+  return (int)((((int64_t)u + 1) * nwg + units - 1) / units) - 1;
+}
+
+template <int MT, int NMAT>
 __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
-  constexpr int kRows = 32 * MT;
-  constexpr int NBC = SWIGLU ? 1 : 2;  // column tiles per wave and matrix
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[kRows * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[kRows * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t wb0[kNW * kNB * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t wb1[kNW * kNB * kTileBytes];
-  __shared__ unsigned last;
+  constexpr int kRows = 16 * MT;
+  constexpr int kQ = 2 * MT;  // accumulator tiles per wave: two column tiles x MT row tiles
+  constexpr int kGroupCols = NMAT == 2 ? 64 : 128;
+  constexpr int kXPieces = kRows * (kUnitK * 2 / 16) / (kNW * 64);  // 16-byte pieces per thread
+  __shared__ uint4 xs[2][8 * MT][64];                 // activations, two units
+  __shared__ uint4 wsm[2][kColSlots][2][2][64];       // weight codes, two units
+  __shared__ uint16_t ssm[2][kColSlots][2][2][64];    // weight scales, two units
+  __shared__ f32x4 red[kColSlots][kQ][64];
+  __shared__ unsigned last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c32 = lane & 31;
-  const int h = lane >> 5;
+  const int slot = wave & 3, kh = wave >> 2;
+  const int c16 = lane & 15, gq = lane >> 4;
   const int k = p.k;
   const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
-  const int nsteps = k / kStep;
-  const int tile = (int)blockIdx.x;
-  const int split = (int)blockIdx.y;
-  const int s_begin = split * p.steps_per_split;
-  const int len = max(0, min(nsteps, s_begin + p.steps_per_split) - s_begin);
-  const int rows = min(kRows, p.m);
+  const int KU = p.kunits;
+  const int w = (int)blockIdx.x;
+  const int ub = range_begin(p.units, p.nwg, w);
+  const int nloc = range_begin(p.units, p.nwg, w + 1) - ub;
 
-  // this wave's B tiles: columns col[i] .. col[i]+31
-  int col[kNB];
-  __amdgpu_buffer_rsrc_t wc[kNB], ws[kNB];
-#pragma unroll
-  for (int i = 0; i < kNB; ++i) {
-    col[i] = (tile * kNW + wave) * (32 * NBC) + 32 * (i % NBC);
-    const bool up = SWIGLU && i >= NBC;
-    const uint8_t *cb = up ? p.codes1 : p.codes0;
-    const uint8_t *sb = up ? p.scales1 : p.scales0;
-    const int nc = max(0, min(32, p.n - col[i]));
-    const size_t base = (size_t)min(col[i], p.n);
-    wc[i] = rsrc_uniform(cb + base * kb2, (size_t)nc * kb2);
-    ws[i] = rsrc_uniform(sb + base * kb16, (size_t)nc * kb16);
-  }
-  const __amdgpu_buffer_rsrc_t xres = rsrc_uniform(p.x, (size_t)rows * k * 2);
-
-  // activation chunk: 16-byte pieces, row = piece / 8, byte 16 * (piece % 8);
-  // thread tid moves pieces tid + 128 i (row tid/8 + 16 i); rows past m fall
-  // outside xres and read as zero
-  constexpr int kPerThread = kRows * 8 / (kNW * 64);
-  const uint32_t kin = 8u * (uint32_t)(tid & 7);
-  const uint32_t avoff = ((uint32_t)(tid >> 3) * (uint32_t)k + kin) * 2u;
-  uint4 areg[2][kPerThread];
-  auto load_a = [&](int tl, uint4 (&a)[kPerThread]) {
-    const uint32_t kk = (uint32_t)(s_begin + tl) * kStep;
-    const uint32_t vo = tl < len ? avoff + kk * 2u : kOOB;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) a[i] = ld16s(xres, vo, (uint32_t)(16 * i) * (uint32_t)k * 2u);
-  };
-  auto store_a = [&](uint8_t *slot, const uint4 (&a)[kPerThread]) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int piece = tid + kNW * 64 * i;
-      *(uint4 *)&slot[(piece >> 3) * kRowBytes + 16 * (piece & 7)] = a[i];
-    }
+  // first column of this wave's column tile j in group g
+  auto tile_col = [&](int g, int j) __attribute__((always_inline)) {
+    return g * kGroupCols + (NMAT == 2 ? 16 * slot : 32 * slot + 16 * j);
   };
 
-  // weight groups: DMA lane l moves row 8g + l/8, chunk (l%8) ^ (l/8) of
-  // instruction g and lands at 16 l; row c32 = 8g + a is read back from
-  // instruction g, lane 8a + (x ^ a) for chunk x = 2q + h of step q
-  const uint32_t drow = (uint32_t)lane >> 3, dchunk = ((uint32_t)lane & 7) ^ drow;
-  const uint32_t ra = (uint32_t)c32 & 7;
-  uint32_t coff[kGroup];
-#pragma unroll
-  for (int q = 0; q < kGroup; ++q)
-    coff[q] = (uint32_t)(wave * kNB * 4 + (c32 >> 3)) * 1024u + 16u * (8u * ra + ((2u * q + h) ^ ra));
-  auto load_group = [&](int G, uint8_t *slot) {
-    const uint32_t goff = (uint32_t)(s_begin + kGroup * G) * 32u;
-    const bool ok = kGroup * G < len;
-#pragma unroll
-    for (int i = 0; i < kNB; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        dma16(wc[i], slot + ((wave * kNB + i) * 4 + g) * 1024,
-              ok ? (8u * g + drow) * kb2 + goff + 16u * dchunk : kOOB);
+  // ---- weights: per unit and column tile the two waves of a slot load the
+  // tile's 16 rows as whole 128-byte lines (wave kh rows 8 kh .. 8 kh + 7;
+  // lane s: row s / 8, 16-byte piece s % 8 = K 32 (s % 8) of the unit) and
+  // their scale bytes (two per lane, the same K), two units ahead; one unit
+  // ahead they are written to LDS in operand order, so each lane reads its
+  // 16 code bytes and 2 scale bytes back with one instruction apiece
+  struct WStage {
+    uint4 c[2];
+    uint32_t s[2];
   };
-  uint4 sc[kRing][kNB];
-  auto load_scales = [&](int G, uint4 (&sv)[kNB]) {
-    const uint32_t goff = (uint32_t)(s_begin + kGroup * G) * 4u;
-    const int nst = len - kGroup * G;  // steps of this group that run (uniform)
-    if (nst >= kGroup && (kb16 & 15u) == 0) {
+  const uint32_t wrow = 8u * (uint32_t)kh + ((uint32_t)lane >> 3), wpiece = (uint32_t)lane & 7;
+  // (units past the range get a K start beyond every k: their requests are
+  // out of range and fetch nothing, with no branch)
+  auto load_w = [&](int i, WStage &b) __attribute__((always_inline)) {
+    const bool live = i < nloc;
+    const int u = ub + (live ? i : 0);
+    const int g = u / KU;
+    const uint32_t k0 = live ? (uint32_t)(u - g * KU) * kUnitK : 0x40000000u;
+    const uint32_t kp = k0 + 32u * wpiece;
+    const bool ok = kp < (uint32_t)k;
 #pragma unroll
-      for (int i = 0; i < kNB; ++i) sv[i] = ld16(ws[i], (uint32_t)c32 * kb16 + goff);
-    } else {
-      const uint32_t o = (uint32_t)c32 * kb16 + goff;
-#pragma unroll
-      for (int i = 0; i < kNB; ++i)
-        sv[i] = uint4{ld4(ws[i], nst > 0 ? o : kOOB), ld4(ws[i], nst > 1 ? o + 4u : kOOB),
-                      ld4(ws[i], nst > 2 ? o + 8u : kOOB), ld4(ws[i], nst > 3 ? o + 12u : kOOB)};
+    for (int j = 0; j < 2; ++j) {
+      const int col = tile_col(g, j);
+      const bool second = NMAT == 2 && j == 1;
+      const uint8_t *cb = second ? p.codes1 : p.codes0;
+      const uint8_t *sb = second ? p.scales1 : p.scales0;
+      const int nc = max(0, min(16, p.n - col));
+      const size_t base = (size_t)min(col, p.n);
+      const __amdgpu_buffer_rsrc_t rc = rsrc_uniform(cb + base * kb2, (size_t)nc * kb2);
+      const __amdgpu_buffer_rsrc_t rs = rsrc_uniform(sb + base * kb16, (size_t)nc * kb16);
+      b.c[j] = ld16(rc, ok ? wrow * kb2 + (kp >> 1) : kOOB);
+      b.s[j] = ld2(rs, ok ? wrow * kb16 + (kp >> 4) : kOOB);
     }
   };
-  auto dequant_j = [&](const uint4 (&w)[kNB], const uint32_t (&s)[kNB], int j, bf16x8 (&out)[kNB]) {
+  // LDS image of a unit's weights: per (slot, tile, K half) 64 lanes x 16
+  // code bytes and 64 x 2 scale bytes; lane (c, g) of K half h holds row c,
+  // piece 4 h + g, at code position 16 g + (c ^ 2 (g + 4 h)) (the XOR keeps
+  // the 16 lanes of a write or read phase on distinct banks) and scale
+  // position 16 g + c
+  auto store_w = [&](int buf, const WStage &b) __attribute__((always_inline)) {
+    const uint32_t h = wpiece >> 2, g4 = wpiece & 3;
+    const uint32_t cpos = 16u * g4 + (wrow ^ (2u * (g4 + 4u * h)));
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) {
-      const float sc_ = j < 2 ? e4m3_to_f32_sel<0>(s[i]) : e4m3_to_f32_sel<1>(s[i]);
-      const uint32_t word = j == 0 ? w[i].x : j == 1 ? w[i].y : j == 2 ? w[i].z : w[i].w;
-      out[i] = dequant8(word, sc_);
+    for (int j = 0; j < 2; ++j) {
+      wsm[buf][slot][j][h][cpos] = b.c[j];
+      ssm[buf][slot][j][h][16u * g4 + wrow] = (uint16_t)b.s[j];
     }
   };
-  auto read_a = [&](const uint8_t *slot, int j, bf16x8 (&af)[MT]) {
+  const int wpos = 16 * gq + (c16 ^ (2 * (gq + 4 * kh)));
+
+  // ---- activations: a unit's rows x 256 K; thread tid moves 16-byte
+  // pieces tid + 512 q (row piece / 32, K 8 (piece % 32) of the unit).  In
+  // LDS each MFMA fragment is one 1 KB block -- block (4 kh + s) MT + mt of
+  // a buffer holds row tile mt at K 128 kh + 32 g + 8 s -- with lane (c, g)
+  // at position 16 g + (c ^ (4 g + s)).
+  const __amdgpu_buffer_rsrc_t xres = rsrc_uniform(p.x, (size_t)min(kRows, p.m) * (size_t)k * 2);
+  uint4 xr[2][kXPieces];
+  auto load_x = [&](int i, uint4 (&xv)[kXPieces]) __attribute__((always_inline)) {
+    const uint32_t k0 = i < nloc ? (uint32_t)((ub + i) % KU) * kUnitK : 0x40000000u;
+#pragma unroll
+    for (int q = 0; q < kXPieces; ++q) {
+      const int piece = tid + kNW * 64 * q;
+      const uint32_t kk = k0 + 8u * (uint32_t)(piece & 31);
+      xv[q] = ld16(xres, kk < (uint32_t)k ? ((uint32_t)(piece >> 5) * (uint32_t)k + kk) * 2u : kOOB);
+    }
+  };
+  auto store_x = [&](int buf, const uint4 (&xv)[kXPieces]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kXPieces; ++q) {
+      const int piece = tid + kNW * 64 * q;
+      const int r = piece >> 5, ch = piece & 31;
+      const int h = ch >> 4, g4 = (ch >> 2) & 3, st = ch & 3;
+      xs[buf][(4 * h + st) * MT + (r >> 4)][16 * g4 + ((r & 15) ^ (4 * g4 + st))] = xv[q];
+    }
+  };
+  auto read_a = [&](int buf, int s, bf16x8 (&a)[MT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      af[mt] = as_bf16x8(*(const uint4 *)&slot[(mt * 32 + c32) * kRowBytes + 2 * (32 * h + 8 * j)]);
+      a[mt] = as_bf16x8(xs[buf][(4 * kh + s) * MT + mt][16 * gq + (c16 ^ (4 * gq + s))]);
   };
 
-  f32x16 acc[kNB][MT];
+  f32x4 acc[2][MT];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < kNB; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][mt][e] = 0.f;
+      for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  zero_acc();
 
-  // prologue: weight group 0 requested, A chunk 0 in LDS, chunk 1 in
-  // registers
-  load_group(0, wb0);
-  load_scales(0, sc[0]);
-  load_a(0, areg[0]);
-  load_a(1, areg[1]);
-  store_a(lds0, areg[0]);
-  lds_barrier();
-
-  // one step; slot_c = t % 8 fixes at compile time the A slot and register
-  // set (t % 2), the ring slot of the step's group (t / 4 % 2) and the step
-  // within it (t % 4).  Activation chunks are loaded two steps ahead and
-  // written to LDS one step ahead (into the slot read two steps ago).
-  auto step = [&](int tl, auto slot_c) {
-    constexpr int s8 = decltype(slot_c)::value;
-    constexpr int q = s8 % kGroup, bsl = (s8 / kGroup) % kRing, sa = s8 % 2;
-    const uint8_t *cur = sa ? lds1 : lds0;
-    uint8_t *nxt = sa ? lds0 : lds1;
-    const uint8_t *bcur = bsl ? wb1 : wb0;
-    uint4 w[kNB];
-    uint32_t sw[kNB];
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    uint4 wc[2];
+    float sc[2][2];
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) {
-      w[i] = *(const uint4 *)&bcur[coff[q] + i * 4 * 1024];
-      const uint32_t d = q == 0 ? sc[bsl][i].x : q == 1 ? sc[bsl][i].y : q == 2 ? sc[bsl][i].z : sc[bsl][i].w;
-      sw[i] = d >> (16u * h);
+    for (int j = 0; j < 2; ++j) {
+      wc[j] = wsm[buf][slot][j][kh][wpos];
+      const uint32_t sv = ssm[buf][slot][j][kh][16 * gq + c16];
+      sc[j][0] = e4m3_to_f32_sel<0>(sv);  // block 2g: steps 0, 1
+      sc[j][1] = e4m3_to_f32_sel<1>(sv);  // block 2g + 1: steps 2, 3
     }
-    if constexpr (q == 1) {
-      // request the next group into the other slot (read during the previous
-      // group, finished before the last barrier), three steps ahead of use;
-      // pinned after this step's reads so the load-counter wait before a
-      // ring read covers only older requests
-      __builtin_amdgcn_sched_barrier(0);
-      load_group(tl / kGroup + 1, bsl ? wb0 : wb1);
-      load_scales(tl / kGroup + 1, sc[bsl ^ 1]);
-    }
-    bf16x8 af[2][MT];
-    bf16x8 bf[2][kNB];
-    read_a(cur, 0, af[0]);
-    dequant_j(w, sw, 0, bf[0]);
+    bf16x8 a[2][MT];
+    bf16x8 bb[2][2];
+    auto dq = [&](int s, bf16x8 (&out)[2]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < 3) {
-        read_a(cur, j + 1, af[(j + 1) & 1]);
-        dequant_j(w, sw, j + 1, bf[(j + 1) & 1]);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t word = s == 0 ? wc[j].x : s == 1 ? wc[j].y : s == 2 ? wc[j].z : wc[j].w;
+        out[j] = dequant8(word, sc[j][s >> 1]);
+      }
+    };
+    read_a(buf, 0, a[0]);
+    dq(0, bb[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+        read_a(buf, s + 1, a[(s + 1) & 1]);
+        dq(s + 1, bb[(s + 1) & 1]);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < kNB; ++i)
-          acc[i][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][mt], bf[j & 1][i], acc[i][mt], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s & 1][mt], bb[s & 1][j], acc[j][mt], 0, 0, 0);
     }
-    // (unconditional, so the step stays one basic block: after the last
-    // step the slot is not read again)
-    store_a(nxt, areg[sa ^ 1]);
-    load_a(tl + 2, areg[sa]);
-    lds_barrier();
   };
-  for (int tl = 0; tl < len; tl += 8) {
-    step(tl, std::integral_constant<int, 0>{});
-    if (tl + 1 < len) step(tl + 1, std::integral_constant<int, 1>{});
-    if (tl + 2 < len) step(tl + 2, std::integral_constant<int, 2>{});
-    if (tl + 3 < len) step(tl + 3, std::integral_constant<int, 3>{});
-    if (tl + 4 < len) step(tl + 4, std::integral_constant<int, 4>{});
-    if (tl + 5 < len) step(tl + 5, std::integral_constant<int, 5>{});
-    if (tl + 6 < len) step(tl + 6, std::integral_constant<int, 6>{});
-    if (tl + 7 < len) step(tl + 7, std::integral_constant<int, 7>{});
-  }
-  // group requests past the split may still be in flight; they must land
-  // before the workgroup's LDS is released
-  wait_all_memory();
 
-  if (p.ksplit > 1) {
-    // per wave: [q = (i*MT + mt)*4 + e/4][lane][e%4], 16 contiguous bytes
-    // per lane and 1 KB per instruction
-    constexpr int kWaveFloats = kNB * kRows * 32;
-    const uint32_t pvoff = (uint32_t)lane * 16u;
-    auto pres_of = [&](int sp) {
-      return rsrc_uniform(p.partial + (((size_t)tile * p.ksplit + sp) * kNW + wave) * kWaveFloats,
-                          (size_t)kWaveFloats * 4);
-    };
-    {
-      const __amdgpu_buffer_rsrc_t pres = pres_of(split);
+  // element i of row tile mt, column tile j: row 16 mt + 4 g + i, column
+  // tile_col(g, j) + c; rows past m fall outside the output resource
+  const __amdgpu_buffer_rsrc_t yres = rsrc_uniform(p.y, (size_t)min(kRows, p.m) * (size_t)p.n * 2);
+  const uint32_t n2 = (uint32_t)p.n * 2u;
+  auto epilogue = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kNB; ++i)
+    for (int j = 0; j < (NMAT == 2 ? 1 : 2); ++j) {
+      const int col = tile_col(g, j) + c16;
+      const uint32_t vo = col < p.n ? (uint32_t)(4 * gq) * n2 + (uint32_t)col * 2u : kOOB;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 out = NMAT == 2 ? swiglu_bf16(acc[0][mt][e] * p.ts0, acc[1][mt][e] * p.ts1)
+                                       : (__bf16)(acc[j][mt][e] * p.ts0);
+          st2s(yres, vo, (uint32_t)(mt * 16 + e) * n2, out);
+        }
+    }
+  };
+
+  // piece of workgroup v for the group starting at or before its range:
+  // slot 0 holds the segment of its first group, slot 1 that of its last
+  auto piece_rsrc = [&](int v, int pslot) __attribute__((always_inline)) {
+    return rsrc_uniform(p.partial + ((size_t)(v * 2 + pslot) * kColSlots + slot) * (kQ * 256),
+                        (size_t)kQ * 256 * 4);
+  };
+
+  // the last of a split group's pieces to arrive finishes the group: every
+  // wave sums column tile kh of its slot over the pieces in K (workgroup)
+  // order, four pieces' loads in flight together
+  auto finish_split = [&](int g) __attribute__((always_inline)) {
+    const int v0 = range_owner(p.units, p.nwg, g * KU);
+    const int v1 = range_owner(p.units, p.nwg, g * KU + KU - 1);
+    f32x4 sum[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int v = v0; v <= v1; v += 4) {
+      f32x4 t[4][MT];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int vv = min(v + d, v1);
+        const int ps = g == range_begin(p.units, p.nwg, vv) / KU ? 0 : 1;
+        const __amdgpu_buffer_rsrc_t pr = piece_rsrc(vv, ps);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
+          t[d][mt] = ld16_coherent(pr, (uint32_t)lane * 16u, (uint32_t)(kh * MT + mt) * 1024u);
+      }
 #pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const f32x4 v = {acc[i][mt][4 * e4], acc[i][mt][4 * e4 + 1], acc[i][mt][4 * e4 + 2],
-                             acc[i][mt][4 * e4 + 3]};
-            st16_coherent(pres, pvoff, (uint32_t)((i * MT + mt) * 4 + e4) * 1024u, v);
-          }
+      for (int d = 0; d < 4; ++d)
+        if (v + d <= v1) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) sum[mt] += t[d][mt];
+        }
     }
-    if (!SWIGLU) return;  // k_smallm_reduce sums the splits
+    // column tile 1 goes to the K-half-0 wave of the slot
+    if (kh == 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[slot][mt][lane] = sum[mt];
+    }
+    lds_barrier();
+    if (kh == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[0][mt] = sum[mt];
+        acc[1][mt] = red[slot][mt][lane];
+      }
+      epilogue(g);
+    }
+    if (tid == 0) __hip_atomic_store(&p.counters[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // end of a segment of group g: sum the K halves through LDS; finish a
+  // whole group at once, or store this workgroup's piece of a split one and
+  // count its arrival (the last piece to arrive finishes the group).
+  // Counting every arrival after the whole range instead, so that the
+  // stores need no wait mid-stream, measured slower: the finishing work
+  // then all lands at the end of the launch.
+  auto flush = [&](int g, bool whole, int pslot) __attribute__((always_inline)) {
+    if (kh == 1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[slot][j * MT + mt][lane] = acc[j][mt];
+    }
+    lds_barrier();
+    if (kh == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[j][mt] += red[slot][j * MT + mt][lane];
+      if (whole) {
+        epilogue(g);
+      } else {
+        const __amdgpu_buffer_rsrc_t pr = piece_rsrc(w, pslot);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            st16_coherent(pr, (uint32_t)lane * 16u, (uint32_t)(j * MT + mt) * 1024u, acc[j][mt]);
+      }
+    }
+    if (!whole) {
+      const int v0 = range_owner(p.units, p.nwg, g * KU);
+      const int v1 = range_owner(p.units, p.nwg, g * KU + KU - 1);
+      wait_all_memory();
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned old =
+            __hip_atomic_fetch_add(&p.counters[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = old == (unsigned)(v1 - v0);
+      }
+      __syncthreads();
+      if (last_flag) finish_split(g);
+    }
+    zero_acc();
+    // every request of this path is complete again when the unit loop
+    // resumes (its wait-count bookkeeping then matches the other path's);
+    // red is rewritten only after the next unit's barrier
     wait_all_memory();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned old =
-          __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = old == (unsigned)(p.ksplit - 1);
-    }
-    __syncthreads();
-    if (!last) return;
-#pragma unroll
-    for (int i = 0; i < kNB; ++i)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][mt][e] = 0.f;
-    // split order outermost; all of one split's loads in flight together
-    for (int sp = 0; sp < p.ksplit; ++sp) {
-      const __amdgpu_buffer_rsrc_t pres = pres_of(sp);
-      f32x4 v[kNB * MT * 4];
-#pragma unroll
-      for (int q = 0; q < kNB * MT * 4; ++q) v[q] = ld16_coherent(pres, pvoff, (uint32_t)q * 1024u);
-#pragma unroll
-      for (int q = 0; q < kNB * MT * 4; ++q) {
-        const int i = q / (4 * MT), mt = (q / 4) % MT, e4 = q % 4;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][mt][4 * e4 + t] += v[q][t];
-      }
-    }
-    if (tid == 0)
-      __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  };
 
-  // element (mt, e): row 32mt + 8(e/4) + 4h + e%4; the 4h row and the column
-  // are the per-lane part of the offset, the rest is uniform; rows past m
-  // fall outside the output resource and are dropped
-  const __amdgpu_buffer_rsrc_t yres = rsrc_uniform(p.y, (size_t)rows * p.n * 2);
-  const uint32_t n2 = (uint32_t)p.n * 2u;
-#pragma unroll
-  for (int i = 0; i < (SWIGLU ? 1 : kNB); ++i) {
-    const int c = col[i] + c32;
-    const uint32_t vo = c < p.n ? (uint32_t)(4 * h) * n2 + (uint32_t)c * 2u : kOOB;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const __bf16 out = SWIGLU ? swiglu_bf16(acc[0][mt][e] * p.ts0, acc[1][mt][e] * p.ts1)
-                                  : (__bf16)(acc[i][mt][e] * p.ts0);
-        st2s(yres, vo, (uint32_t)(mt * 32 + 8 * (e >> 2) + (e & 3)) * n2, out);
-      }
-  }
-}
+  // ---- main loop: units in order.  Each unit first writes the activations
+  // and weights of the next unit into LDS (loaded two units earlier, into
+  // two and four register sets), then requests those of the unit three
+  // ahead.  Vector-memory loads complete in issue order as far as the wait
+  // counter goes, so the wait before a write to LDS also covers every
+  // older request -- all of them for units already due.
+  WStage wb[kNS];
+  load_x(0, xr[0]);
+  load_w(0, wb[0]);
+  load_x(1, xr[1]);
+  load_w(1, wb[1]);
+  store_x(0, xr[0]);
+  store_w(0, wb[0]);
+  load_x(2, xr[0]);
+  load_w(2, wb[2]);
+  lds_barrier();
 
-// The split sum of a one-matrix launch, in parallel over the whole output:
-// one thread per 16-byte partial chunk (four rows of one column), summing
-// the splits in split order -- the order the in-kernel sum of the fused
-// gate+up launch uses -- then the epilogue.  With one workgroup per tile
-// doing the sum, a deep K split left one CU per tile reading every split's
-// partials at the end of the launch.
-template <int MT>
-__global__ __launch_bounds__(256) void k_smallm_reduce(const float *__restrict__ partial, int tiles,
-                                                       int ksplit, int m, int n, float ts, void *y) {
-  constexpr int kRows = 32 * MT;
-  constexpr int kWaveFloats = kNB * kRows * 32;
-  constexpr int kChunks = kNB * MT * 4 * 64;  // 16-byte chunks per wave
-  const int gid = (int)(blockIdx.x * 256 + threadIdx.x);
-  if (gid >= tiles * kNW * kChunks) return;
-  const int tile = gid / (kNW * kChunks);
-  const int rem = gid - tile * (kNW * kChunks);
-  const int wave = rem / kChunks;
-  const int q = (rem - wave * kChunks) >> 6, lane = rem & 63;
-  const int i = q / (4 * MT), mt = (q >> 2) % MT, e4 = q & 3;
-  const float4 *src = (const float4 *)(partial + ((size_t)tile * ksplit * kNW + wave) * kWaveFloats) +
-                      (size_t)q * 64 + lane;
-  const size_t split_stride = (size_t)kNW * kWaveFloats / 4;  // in float4
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < ksplit; ++sp) {
-    const float4 v = src[sp * split_stride];
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  // Segment bookkeeping (all wave-uniform): the current segment covers
+  // local units [seg_first, seg_end) of column group g.
+  int g = ub / KU;
+  int seg_first = 0;
+  int seg_end = min(nloc, (g + 1) * KU - ub);
+
+  // One unit.  Every unit issues the same requests and barrier whether or
+  // not it computes (the last block of four may run past the range), so
+  // the compiler's wait-count bookkeeping sees the same request sequence
+  // on every path and waits for each unit's own requests only.
+  auto unit = [&](int i, auto phase) __attribute__((always_inline)) {
+    constexpr int S = decltype(phase)::value;  // i % kNS (kNS even: also the LDS slot parity)
+    store_x((S + 1) & 1, xr[(S + 1) & 1]);
+    store_w((S + 1) & 1, wb[(S + 1) % kNS]);
+    load_x(i + 3, xr[(S + 1) & 1]);
+    load_w(i + 3, wb[(S + 3) % kNS]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < nloc) compute(S & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    if (i + 1 == seg_end) {
+      const bool whole = ub + seg_first == g * KU && (g + 1) * KU - ub <= nloc;
+      flush(g, whole, seg_first == 0 ? 0 : 1);
+      seg_first = seg_end;
+      ++g;
+      seg_end = min(nloc, (g + 1) * KU - ub);
+    }
+  };
+
+  for (int i0 = 0; i0 < nloc; i0 += kNS) {
+    unit(i0, std::integral_constant<int, 0>{});
+    unit(i0 + 1, std::integral_constant<int, 1>{});
+    unit(i0 + 2, std::integral_constant<int, 2>{});
+    unit(i0 + 3, std::integral_constant<int, 3>{});
   }
-  const int col = (tile * kNW + wave) * 64 + 32 * i + (lane & 31);
-  if (col >= n) return;
-  const int row0 = 32 * mt + 8 * e4 + 4 * (lane >> 5);
-  const float v[4] = {acc.x, acc.y, acc.z, acc.w};
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    if (row0 + t < m) ((__bf16 *)y)[(size_t)(row0 + t) * n + col] = (__bf16)(v[t] * ts);
+  // weight and activation requests past the range fetch nothing, but any
+  // still in flight must land before the workgroup ends
+  wait_all_memory();
 }
 
 }  // namespace
@@ -386,26 +421,19 @@ bool smallm_eligible(int m, int k) { return m >= 17 && m <= 64 && k % 64 == 0; }
 
 SmallPlan smallm_plan(int m, int n, int k, int nmat) {
   SmallPlan pl;
-  pl.mt = m <= 32 ? 1 : 2;
-  pl.tiles = cdiv(n, kNW * 32 * (nmat == 2 ? 1 : 2));
-  const int nsteps = k / kStep;
-  // Three workgroups per CU are resident (about 50 KB of LDS each); split K
-  // as far as every split workgroup still fits in one round, by whole
-  // weight groups and with at least eight steps per split, so that all
-  // SIMDs get a wave.  The split depends on (n, k) only.
-  const int slots = 3 * 256;
-  int ksplit = std::max(1, slots / pl.tiles);
-  ksplit = std::min(ksplit, std::max(1, nsteps / 8));
-  if (k < splitk_min_k()) ksplit = 1;
-  pl.steps_per_split = cdiv(cdiv(nsteps, ksplit), kGroup) * kGroup;
-  pl.ksplit = cdiv(nsteps, pl.steps_per_split);
-  (void)m;
+  pl.mt = m <= 32 ? 2 : 4;
+  pl.groups = cdiv(n, nmat == 2 ? 64 : 128);
+  pl.kunits = cdiv(k, kUnitK);
+  pl.units = pl.groups * pl.kunits;
+  pl.nwg = std::min(kMaxWG, pl.units);
   return pl;
 }
 
 size_t smallm_partial_floats(const SmallPlan &pl) {
-  return pl.ksplit > 1 ? (size_t)pl.tiles * pl.ksplit * kNW * kNB * 32 * pl.mt * 32 : 0;
+  return (size_t)pl.nwg * 2 * kColSlots * (2 * pl.mt) * 256;
 }
+
+size_t smallm_counter_words(const SmallPlan &pl) { return (size_t)pl.groups; }
 
 hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat, const MatRef *w, void *y,
                          float *partial, unsigned *counters, const SmallPlan &pl,
@@ -424,27 +452,18 @@ hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat, const Mat
   p.y = y;
   p.partial = partial;
   p.counters = counters;
-  p.ksplit = pl.ksplit;
-  p.steps_per_split = pl.steps_per_split;
-  dim3 grid(pl.tiles, pl.ksplit), block(kNW * 64);
+  p.kunits = pl.kunits;
+  p.units = pl.units;
+  p.nwg = pl.nwg;
+  // (the static LDS, about 84 or 132 KB, keeps it to one workgroup per CU)
+  const dim3 grid(pl.nwg), block(kNW * 64);
+  const unsigned pad = 0;
   if (nmat == 2) {
-    if (pl.mt == 1) hipLaunchKernelGGL((k_smallm<1, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((k_smallm<2, true>), grid, block, 0, stream, p);
-    return hipGetLastError();
-  }
-  if (pl.mt == 1) hipLaunchKernelGGL((k_smallm<1, false>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((k_smallm<2, false>), grid, block, 0, stream, p);
-  if (pl.ksplit > 1) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int threads = pl.tiles * kNW * kNB * pl.mt * 4 * 64;
-    const dim3 rgrid((threads + 255) / 256);
-    if (pl.mt == 1)
-      hipLaunchKernelGGL((k_smallm_reduce<1>), rgrid, dim3(256), 0, stream, partial, pl.tiles, pl.ksplit, m,
-                         n, p.ts0, y);
-    else
-      hipLaunchKernelGGL((k_smallm_reduce<2>), rgrid, dim3(256), 0, stream, partial, pl.tiles, pl.ksplit, m,
-                         n, p.ts0, y);
+    if (pl.mt == 2) hipLaunchKernelGGL((k_smallm<2, 2>), grid, block, pad, stream, p);
+    else hipLaunchKernelGGL((k_smallm<4, 2>), grid, block, pad, stream, p);
+  } else {
+    if (pl.mt == 2) hipLaunchKernelGGL((k_smallm<2, 1>), grid, block, pad, stream, p);
+    else hipLaunchKernelGGL((k_smallm<4, 1>), grid, block, pad, stream, p);
   }
   return hipGetLastError();
 }

@@ -73,19 +73,23 @@ hipError_t launch_stream_lds(const void *x, int m, int k, int n, int nmat,
                              hipStream_t stream);
 
 // Weight-streaming projection for 17..64 rows (bf16 activations, k % 64
-// == 0): two-wave workgroups of 64 (nmat 2, gate+up+silu fused) or 128
-// (nmat 1) columns, K split over blockIdx.y with the in-kernel fixup;
-// `partial` holds smallm_partial_floats(...) floats and `counters` tiles
-// words that are zero on entry (the kernel leaves them zero).
+// == 0): one eight-wave workgroup per CU walks an equal share of the
+// (column group, 256-K unit) pairs -- column groups of 64 gate + 64 up
+// columns (nmat 2, silu fused) or 128 columns (nmat 1) -- and column groups
+// split between workgroups are finished in the kernel by the last piece to
+// arrive.  `partial` holds smallm_partial_floats(...) floats and `counters`
+// smallm_counter_words(...) words that are zero on entry (left zero).
 struct SmallPlan {
-  int mt;     // 32-row tiles (1 or 2)
-  int tiles;  // workgroups along N
-  int ksplit;
-  int steps_per_split;
+  int mt;      // 16-row tiles (2 or 4)
+  int groups;  // column groups
+  int kunits;  // 256-K units per column group
+  int units;   // groups * kunits
+  int nwg;     // workgroups (at most 256)
 };
 bool smallm_eligible(int m, int k);
 SmallPlan smallm_plan(int m, int n, int k, int nmat);
 size_t smallm_partial_floats(const SmallPlan &pl);
+size_t smallm_counter_words(const SmallPlan &pl);
 hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat,
                          const MatRef *w, void *y, float *partial,
                          unsigned *counters, const SmallPlan &pl,

@@ -82,6 +82,9 @@ SHAPES = [
     # 17..64 rows: k % 64 == 0 with a partial last weight group (LDS-DMA
     # ring), and k % 64 != 0 (LDS-shared activations)
     (40, 70, 2176), (20, 64, 160), (64, 48, 96),
+    # 17..64 rows, stream-K plan: one column group split over 16 workgroups,
+    # many groups with two pieces each, a ragged last group and K unit
+    (48, 48, 4096), (33, 3000, 320), (17, 129, 2176), (64, 200, 64),
     (65, 130, 1024), (130, 300, 416), (257, 129, 96), (200, 64, 2048),
     # many-row kernel with several tile rounds per persistent workgroup
     (600, 520, 2048), (300, 1000, 1024),
@@ -257,6 +260,32 @@ def test_gate_up_silu_matches_oracle(m):
     assert np.all((same_sign & (d <= 1)) | zero_pair)
 
 
+@pytest.mark.parametrize("m,n,k", [(17, 300, 1024), (32, 48, 4096), (40, 1000, 2176), (64, 130, 64),
+                                   (64, 4100, 512)])
+def test_gate_up_silu_small_m_split_groups(m, n, k):
+    """17..64 rows: column groups of 64 gate + 64 up columns cut between
+    workgroups (16 pieces of one group at n=48, two or more elsewhere, ragged
+    n and a partial last K unit).  gate and up meet the tolerance against the
+    oracle; act equals silu_mul of the GPU's own gate and up within one ulp."""
+    _say(f"gate_up_silu small m={m} n={n} k={k}")
+    x = si.activations(m, k, seed=m + 7)
+    wg = si.weight(n, k, seed=n + 1, code_stream=1, scale_stream=2, ts=0.75)
+    wu = si.weight(n, k, seed=n + 2, code_stream=3, scale_stream=4, ts=1.25)
+    xd = x.cuda()
+    act = nv.nvfp4_gate_up_silu_w4a16(xd, g_weight(wg), g_weight(wu))
+    g = nv.nvfp4_gemm_w4a16(xd, g_weight(wg))
+    u = nv.nvfp4_gemm_w4a16(xd, g_weight(wu))
+    sync()
+    assert_close(bits(g), oracle.gemm_w4a16(bits(x), o_weight(wg))[1], f"gate m={m} n={n} k={k}")
+    assert_close(bits(u), oracle.gemm_w4a16(bits(x), o_weight(wu))[1], f"up m={m} n={n} k={k}")
+    ref = oracle.silu_mul(bits(g), bits(u))
+    got = bits(act)
+    d = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    same_sign = (got & 0x8000) == (ref & 0x8000)
+    zero_pair = ((got & 0x7FFF) == 0) & ((ref & 0x7FFF) <= 1)
+    assert np.all((same_sign & (d <= 1)) | zero_pair)
+
+
 def test_gate_up_silu_many_rows_split_tiles():
     """300 rows, hidden 2048, inter 640: two row blocks x five column groups,
     each split over several workgroups by K steps; act must still equal
@@ -335,12 +364,15 @@ def test_exact_case_every_row_many_row_kernel(name, m, n, k):
     assert np.array_equal(bits(y)[:, cols], yo)
 
 
-def test_exact_case_every_row_gate_up_silu_many_rows():
-    """The fused gate+up+silu launch at the prefill shape: every row, and
-    columns of both of its column launches.  gate and up are exact, so act
-    must be the silu_mul of the oracle's gate and up within one bf16 ulp."""
-    m, hidden, inter = 2048, 5120, 17408
-    _say("exact case, every row: prefill gate+up+silu")
+@pytest.mark.parametrize("m", [2048, 64, 40])
+def test_exact_case_every_row_gate_up_silu(m):
+    """The fused gate+up+silu launch at the prefill shape (every row, and
+    columns of both of the many-row kernel's column launches) and at the
+    small-m shape (64 and 40 rows: column groups split between workgroups
+    and finished by the last piece).  gate and up are exact, so act must be
+    the silu_mul of the oracle's gate and up within one bf16 ulp."""
+    hidden, inter = 5120, 17408
+    _say(f"exact case, every row: gate+up+silu m={m}")
     x, wg = si.exact_case(m, inter, hidden, seed=7)
     _, wu = si.exact_case(1, inter, hidden, seed=8)
     act = nv.nvfp4_gate_up_silu_w4a16(x.cuda(), g_weight(wg), g_weight(wu))
