@@ -452,6 +452,7 @@ int check_q2_weight(const q2_weight *w, const char *name, int *gshift) {
 Q2MatRef q2_mat(const q2_weight *w) { return Q2MatRef{w->codes, w->scales}; }
 
 size_t q2_scratch_bytes(int m, int n, int k, int nmat) {
+  if (smallm_eligible(m, k)) return align256(4 * smallm_partial_floats(smallm_plan(m, n, k, nmat)));
   return align256(4 * q2_partial_floats(q2_plan(m, n, k), nmat, m, n));
 }
 
@@ -462,8 +463,18 @@ size_t q2_scratch_bytes(int m, int n, int k, int nmat) {
 bool q2_tiled(int m, int k) { return m > cfg().smallm_max_m && k % 64 == 0; }
 
 
+// up to 64 rows: 17..64 (k % 64 == 0) on the small-m kernel, else the
+// packed-Q2 streaming kernel
 int run_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w, void *y,
            void *scratch, hipStream_t s) {
+  if (smallm_eligible(m, k)) {
+    const SmallPlan sp = smallm_plan(m, n, k, nmat);
+    unsigned *counters = nullptr;
+    int rc = counters_get(smallm_counter_words(sp), &counters);
+    if (rc) return rc;
+    return hip_status(launch_smallm_q2(x, m, k, n, gshift, nmat, w, y, (float *)scratch, counters, sp, s),
+                      "packed-Q2 small-m projection launch");
+  }
   StreamPlan pl = q2_plan(m, n, k);
   unsigned *counters = nullptr;
   int rc = counters_get(stream_counter_words(pl, m), &counters);

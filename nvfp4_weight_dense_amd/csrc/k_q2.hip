@@ -11,6 +11,9 @@
 // the pages' dequantized BF16 weight; the GEMM then runs on the bf16 matrix
 // cores with fp32 sums, and the weights never exist as bf16 in memory.
 //
+// Serves up to 16 rows, and 17..64 rows when k % 64 != 0 (17..64 rows with
+// k % 64 == 0 take k_smallm's packed-Q2 variant).
+//
 // Work decomposition (the weight-streaming skeleton of the other few-row
 // kernels): a workgroup owns CTW tiles of 16 columns of NMAT matrices (2:
 // gate and up with the silu epilogue), up to 64 rows and a range of K; its 4

@@ -64,6 +64,7 @@ struct SmallArgs {
   float *partial;      // [nwg][2][kColSlots][2 MT][64 lanes][4]
   unsigned *counters;  // [groups], zero between calls
   int kunits, units, nwg;
+  int gshift;  // packed-Q2 weights: fp16 scale per 1 << gshift of K
 };
 
 __device__ __forceinline__ void st16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
@@ -83,15 +84,18 @@ __host__ __device__ __forceinline__ int range_owner(int units, int nwg, int u) {
   return (int)((((int64_t)u + 1) * nwg + units - 1) / units) - 1;
 }
 
-template <int MT, int NMAT>
+// Q2: packed-Q2 weights (2-bit codes, fp16 scale per group of K; the
+// values bf16((q - 2) d) come from q2_table / q2_dequant8) instead of NVFP4.
+template <int MT, int NMAT, bool Q2>
 __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
   constexpr int kRows = 16 * MT;
   constexpr int kQ = 2 * MT;  // accumulator tiles per wave: two column tiles x MT row tiles
   constexpr int kGroupCols = NMAT == 2 ? 64 : 128;
   constexpr int kXPieces = kRows * (kUnitK * 2 / 16) / (kNW * 64);  // 16-byte pieces per thread
-  __shared__ uint4 xs[2][8 * MT][64];                 // activations, two units
-  __shared__ uint4 wsm[2][kColSlots][2][2][64];       // weight codes, two units
-  __shared__ uint16_t ssm[2][kColSlots][2][2][64];    // weight scales, two units
+  __shared__ uint4 xs[2][8 * MT][64];                             // activations, two units
+  __shared__ uint4 wsm[2][kColSlots][2][2][Q2 ? 1 : 64];          // NVFP4 codes, two units
+  __shared__ uint16_t ssm[2][kColSlots][2][2][Q2 ? 1 : 64];       // NVFP4 scales, two units
+  __shared__ uint2 wsq[2][kColSlots][2][2][Q2 ? 64 : 1];          // packed-Q2 codes, two units
   __shared__ f32x4 red[kColSlots][kQ][64];
   __shared__ unsigned last_flag;
 
@@ -101,7 +105,9 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
   const int slot = wave & 3, kh = wave >> 2;
   const int c16 = lane & 15, gq = lane >> 4;
   const int k = p.k;
-  const uint32_t kb2 = (uint32_t)k >> 1, kb16 = (uint32_t)k >> 4;
+  // bytes per weight row: codes, and scales (E4M3 per 16 K; fp16 per group)
+  const uint32_t kb2 = Q2 ? (uint32_t)k >> 2 : (uint32_t)k >> 1;
+  const uint32_t kb16 = Q2 ? ((uint32_t)k >> p.gshift) * 2u : (uint32_t)k >> 4;
   const int KU = p.kunits;
   const int w = (int)blockIdx.x;
   const int ub = range_begin(p.units, p.nwg, w);
@@ -130,6 +136,30 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
     const int u = ub + (live ? i : 0);
     const int g = u / KU;
     const uint32_t k0 = live ? (uint32_t)(u - g * KU) * kUnitK : 0x40000000u;
+    if constexpr (Q2) {
+      // codes of tile kh: 16 rows x 64 bytes (lane s: row s / 4, 16 bytes
+      // = K 64 (s % 4) of the unit); fp16 scales of both tiles for this
+      // lane's operand K range (row c, K 128 kh + 32 g, one group)
+      const uint32_t lr = (uint32_t)lane >> 2, lp = (uint32_t)lane & 3;
+      const uint32_t kp = k0 + 64u * lp;
+      const uint32_t ks = k0 + 128u * (uint32_t)kh + 32u * (uint32_t)gq;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = tile_col(g, j);
+        const bool second = NMAT == 2 && j == 1;
+        const uint8_t *cb = second ? p.codes1 : p.codes0;
+        const uint8_t *sb = second ? p.scales1 : p.scales0;
+        const int nc = max(0, min(16, p.n - col));
+        const size_t base = (size_t)min(col, p.n);
+        if (j == kh) {
+          const __amdgpu_buffer_rsrc_t rc = rsrc_uniform(cb + base * kb2, (size_t)nc * kb2);
+          b.c[0] = ld16(rc, kp < (uint32_t)k ? lr * kb2 + (kp >> 2) : kOOB);
+        }
+        const __amdgpu_buffer_rsrc_t rs = rsrc_uniform(sb + base * kb16, (size_t)nc * kb16);
+        b.s[j] = ld2(rs, ks < (uint32_t)k ? (uint32_t)c16 * kb16 + ((ks >> p.gshift) << 1) : kOOB);
+      }
+      return;
+    }
     const uint32_t kp = k0 + 32u * wpiece;
     const bool ok = kp < (uint32_t)k;
 #pragma unroll
@@ -151,7 +181,16 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
   // piece 4 h + g, at code position 16 g + (c ^ 2 (g + 4 h)) (the XOR keeps
   // the 16 lanes of a write or read phase on distinct banks) and scale
   // position 16 g + c
+  // packed Q2: per (slot, tile, K half) 64 lanes x 8 code bytes; lane (c, g)
+  // of K half h holds row c, K 128 h + 32 g .. + 31, at position 16 g + c
   auto store_w = [&](int buf, const WStage &b) __attribute__((always_inline)) {
+    if constexpr (Q2) {
+      const uint32_t lr = (uint32_t)lane >> 2, lp = (uint32_t)lane & 3;
+      const uint32_t h = lp >> 1, g4 = 2u * (lp & 1u);
+      wsq[buf][slot][kh][h][16u * g4 + lr] = uint2{b.c[0].x, b.c[0].y};
+      wsq[buf][slot][kh][h][16u * (g4 + 1u) + lr] = uint2{b.c[0].z, b.c[0].w};
+      return;
+    }
     const uint32_t h = wpiece >> 2, g4 = wpiece & 3;
     const uint32_t cpos = 16u * g4 + (wrow ^ (2u * (g4 + 4u * h)));
 #pragma unroll
@@ -202,23 +241,37 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
   };
   zero_acc();
 
-  auto compute = [&](int buf) __attribute__((always_inline)) {
+  // (b: the unit's register stage, for the packed-Q2 scales)
+  auto compute = [&](int buf, const WStage &b) __attribute__((always_inline)) {
     uint4 wc[2];
     float sc[2][2];
+    uint32_t lo[2], hi[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      wc[j] = wsm[buf][slot][j][kh][wpos];
-      const uint32_t sv = ssm[buf][slot][j][kh][16 * gq + c16];
-      sc[j][0] = e4m3_to_f32_sel<0>(sv);  // block 2g: steps 0, 1
-      sc[j][1] = e4m3_to_f32_sel<1>(sv);  // block 2g + 1: steps 2, 3
+      if constexpr (Q2) {
+        const uint2 v = wsq[buf][slot][j][kh][16 * gq + c16];
+        wc[j] = uint4{v.x, v.y, 0u, 0u};
+        q2_table(b.s[j], lo[j], hi[j]);
+      } else {
+        wc[j] = wsm[buf][slot][j][kh][wpos];
+        const uint32_t sv = ssm[buf][slot][j][kh][16 * gq + c16];
+        sc[j][0] = e4m3_to_f32_sel<0>(sv);  // block 2g: steps 0, 1
+        sc[j][1] = e4m3_to_f32_sel<1>(sv);  // block 2g + 1: steps 2, 3
+      }
     }
     bf16x8 a[2][MT];
     bf16x8 bb[2][2];
     auto dq = [&](int s, bf16x8 (&out)[2]) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t word = s == 0 ? wc[j].x : s == 1 ? wc[j].y : s == 2 ? wc[j].z : wc[j].w;
-        out[j] = dequant8(word, sc[j][s >> 1]);
+        if constexpr (Q2) {
+          // step s: the 8 codes at bits 16 s of the lane's 64 bits
+          const uint32_t word = s < 2 ? wc[j].x : wc[j].y;
+          out[j] = q2_dequant8((s & 1) ? word >> 16 : word & 0xFFFFu, lo[j], hi[j]);
+        } else {
+          const uint32_t word = s == 0 ? wc[j].x : s == 1 ? wc[j].y : s == 2 ? wc[j].z : wc[j].w;
+          out[j] = dequant8(word, sc[j][s >> 1]);
+        }
       }
     };
     read_a(buf, 0, a[0]);
@@ -392,7 +445,7 @@ __global__ __launch_bounds__(kNW * 64) void k_smallm(SmallArgs p) {
     load_x(i + 3, xr[(S + 1) & 1]);
     load_w(i + 3, wb[(S + 3) % kNS]);
     __builtin_amdgcn_sched_barrier(0);
-    if (i < nloc) compute(S & 1);
+    if (i < nloc) compute(S & 1, wb[S]);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     if (i + 1 == seg_end) {
@@ -435,6 +488,24 @@ size_t smallm_partial_floats(const SmallPlan &pl) {
 
 size_t smallm_counter_words(const SmallPlan &pl) { return (size_t)pl.groups; }
 
+namespace {
+// One workgroup per CU: the static LDS (84 to 132 KB) keeps it so, except
+// for packed Q2 with two row tiles (64 KB), which takes 20 KB more.
+template <bool Q2>
+hipError_t launch_kernel(const SmallArgs &p, int nmat, const SmallPlan &pl, hipStream_t stream) {
+  const dim3 grid(pl.nwg), block(kNW * 64);
+  const unsigned pad = Q2 && pl.mt == 2 ? 20480u : 0u;
+  if (nmat == 2) {
+    if (pl.mt == 2) hipLaunchKernelGGL((k_smallm<2, 2, Q2>), grid, block, pad, stream, p);
+    else hipLaunchKernelGGL((k_smallm<4, 2, Q2>), grid, block, pad, stream, p);
+  } else {
+    if (pl.mt == 2) hipLaunchKernelGGL((k_smallm<2, 1, Q2>), grid, block, pad, stream, p);
+    else hipLaunchKernelGGL((k_smallm<4, 1, Q2>), grid, block, pad, stream, p);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat, const MatRef *w, void *y,
                          float *partial, unsigned *counters, const SmallPlan &pl,
                          hipStream_t stream) {
@@ -455,17 +526,31 @@ hipError_t launch_smallm(const void *x, int m, int k, int n, int nmat, const Mat
   p.kunits = pl.kunits;
   p.units = pl.units;
   p.nwg = pl.nwg;
-  // (the static LDS, about 84 or 132 KB, keeps it to one workgroup per CU)
-  const dim3 grid(pl.nwg), block(kNW * 64);
-  const unsigned pad = 0;
-  if (nmat == 2) {
-    if (pl.mt == 2) hipLaunchKernelGGL((k_smallm<2, 2>), grid, block, pad, stream, p);
-    else hipLaunchKernelGGL((k_smallm<4, 2>), grid, block, pad, stream, p);
-  } else {
-    if (pl.mt == 2) hipLaunchKernelGGL((k_smallm<2, 1>), grid, block, pad, stream, p);
-    else hipLaunchKernelGGL((k_smallm<4, 1>), grid, block, pad, stream, p);
-  }
-  return hipGetLastError();
+  return launch_kernel<false>(p, nmat, pl, stream);
+}
+
+hipError_t launch_smallm_q2(const void *x, int m, int k, int n, int gshift, int nmat, const Q2MatRef *w,
+                            void *y, float *partial, unsigned *counters, const SmallPlan &pl,
+                            hipStream_t stream) {
+  SmallArgs p{};
+  p.x = x;
+  p.m = m;
+  p.k = k;
+  p.n = n;
+  p.codes0 = w[0].codes;
+  p.scales0 = (const uint8_t *)w[0].scales;
+  p.ts0 = 1.0f;
+  p.codes1 = nmat > 1 ? w[1].codes : nullptr;
+  p.scales1 = nmat > 1 ? (const uint8_t *)w[1].scales : nullptr;
+  p.ts1 = 1.0f;
+  p.y = y;
+  p.partial = partial;
+  p.counters = counters;
+  p.kunits = pl.kunits;
+  p.units = pl.units;
+  p.nwg = pl.nwg;
+  p.gshift = gshift;
+  return launch_kernel<true>(p, nmat, pl, stream);
 }
 
 }  // namespace nvfp4

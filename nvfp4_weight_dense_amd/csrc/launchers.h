@@ -197,6 +197,14 @@ hipError_t launch_q2(const void *x, int m, int k, int n, int gshift, int nmat,
                      unsigned *counters, const StreamPlan &pl,
                      hipStream_t stream);
 
+// 17..64 rows on packed-Q2 weights (k % 64 == 0): the kernel of
+// launch_smallm with the codes dequantized as bf16((q - 2) * d); plan,
+// partials and counters as there.
+hipError_t launch_smallm_q2(const void *x, int m, int k, int n, int gshift, int nmat,
+                            const Q2MatRef *w, void *y, float *partial,
+                            unsigned *counters, const SmallPlan &pl,
+                            hipStream_t stream);
+
 // Many-row projection on packed-Q2 weights (k % 64 == 0): the many-row
 // kernel of launch_prefill with the weights' codes dequantized in registers
 // as bf16((q - 2) * d); plan prefill_plan, no scratch.

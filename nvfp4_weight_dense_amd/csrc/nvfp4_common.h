@@ -109,6 +109,41 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Packed-Q2 weights (page layers/dense_ffn_prefill.rs, `prefill_q2`: Q2_0
+// weights with a group size, dequantized to BF16 for the BF16 GEMM; the code
+// is this library's reading): a 2-bit code q per element, four per byte from
+// the low bits, one fp16 scale d per row and group of K; the value is
+// bf16((q - 2) * d).  A lane's 32 K values of a step lie in one group
+// (group >= 32), so the four values it can meet form a table, T_q =
+// bf16(fma(q, d, -2d)) -- exact in fp32 and rounded once, the bits of the
+// dequantized BF16 weight -- packed two per dword: lo = T0 | T1 << 16,
+// hi = T2 | T3 << 16.
+__device__ __forceinline__ void q2_table(uint32_t d_bits16, uint32_t &lo, uint32_t &hi) {
+  const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)d_bits16);
+  const float m2d = -2.0f * d;
+  const bf16x2 t01 = {(__bf16)__builtin_fmaf(0.0f, d, m2d), (__bf16)__builtin_fmaf(1.0f, d, m2d)};
+  const bf16x2 t23 = {(__bf16)__builtin_fmaf(2.0f, d, m2d), (__bf16)__builtin_fmaf(3.0f, d, m2d)};
+  lo = __builtin_bit_cast(uint32_t, t01);
+  hi = __builtin_bit_cast(uint32_t, t23);
+}
+
+// Eight codes (16 bits, element e in bits 2e..2e+1) -> their eight table
+// values.  z = cw | cw << 14 puts the codes of elements 2i and 2i+1 at bits
+// 4i and 4i+16, so (z >> 4i) & 0x30003 = q_2i + q_2i+1 << 16; times 0x0202
+// plus 0x01000100 that is the byte selector {2q, 2q+1} of each half for
+// v_perm_b32 over the 8-byte table {hi, lo} (bytes 0-3 lo, 4-7 hi).
+__device__ __forceinline__ bf16x8 q2_dequant8(uint32_t cw, uint32_t lo, uint32_t hi) {
+  const uint32_t z = cw | (cw << 14);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t y = (z >> (4 * i)) & 0x00030003u;
+    o[i] = __builtin_amdgcn_perm(hi, lo, y * 0x0202u + 0x01000100u);
+  }
+  return __builtin_bit_cast(bf16x8, uint4{o[0], o[1], o[2], o[3]});
+}
+
+
 // ---- buffer loads -------------------------------------------------------------
 // A raw buffer resource over [base, base + bytes): loads at offsets beyond
 // the range return zero instead of touching memory, which handles ragged

@@ -53,7 +53,12 @@ def oq(w: si.Q2Weight) -> oracle.Q2Weight:
                                          # != 0), 32-element groups, two column launches; k % 64
                                          # != 0 takes the streaming kernel with 64-row blocks
                                          (300, 200, 2176, 128), (257, 96, 320, 32), (65, 40, 64, 32),
-                                         (600, 1100, 1024, 128), (100, 72, 96, 32)])
+                                         (600, 1100, 1024, 128), (100, 72, 96, 32),
+                                         # 17..64 rows, k % 64 == 0 (the small-m kernel):
+                                         # groups of 32 to 256, a partial last 256-K unit, one
+                                         # column group split over 16 workgroups, ragged n
+                                         (40, 300, 320, 32), (17, 129, 2176, 64), (64, 70, 512, 256),
+                                         (48, 48, 4096, 128), (33, 1000, 1088, 32)])
 def test_q2_gemm_matches_oracle(m, n, k, group):
     _say(f"q2 gemm m={m} n={n} k={k} group={group}")
     x = si.activations(m, k, seed=n, outliers=True)
