@@ -358,20 +358,25 @@ int check_ffn(const void *x, int m, int hidden, int inter, const nvfp4_weight *w
   return NVFP4_OK;
 }
 
+// quantized activation rows; from kFixedTallMinRows rows also their fp16
+// operand tiles (read by the many-row kernel)
 struct QuantBuf {
   uint8_t *codes;
   uint8_t *scales;
   float *rs;
+  uint16_t *tiles;
   size_t bytes;
 };
 
 QuantBuf quant_layout(char *base, int m, int k) {
   QuantBuf q;
   size_t c = align256((size_t)m * k / 2), s = align256((size_t)m * k / 16), r = align256((size_t)m * 4);
+  size_t t = fixed_tall_eligible(m) ? align256(operand_tile_bytes(m, k)) : 0;
   q.codes = (uint8_t *)base;
   q.scales = base ? (uint8_t *)(base + c) : nullptr;
   q.rs = base ? (float *)(base + c + s) : nullptr;
-  q.bytes = c + s + r;
+  q.tiles = base && t ? (uint16_t *)(base + c + s + r) : nullptr;
+  q.bytes = c + s + r + t;
   return q;
 }
 
@@ -403,15 +408,18 @@ Fp8MatRef fp8_mat(const fp8_weight *w) { return Fp8MatRef{w->codes, w->scales}; 
 struct Fp8QuantBuf {
   uint8_t *codes;
   float *rs;
+  uint16_t *tiles;
   size_t bytes;
 };
 
 Fp8QuantBuf fp8_quant_layout(char *base, int m, int k) {
   Fp8QuantBuf q;
-  const size_t c = align256((size_t)m * k);
+  const size_t c = align256((size_t)m * k), r = align256((size_t)m * 4);
+  const size_t t = fixed_tall_eligible(m) ? align256(operand_tile_bytes(m, k)) : 0;
   q.codes = (uint8_t *)base;
   q.rs = base ? (float *)(base + c) : nullptr;
-  q.bytes = c + align256((size_t)m * 4);
+  q.tiles = base && t ? (uint16_t *)(base + c + r) : nullptr;
+  q.bytes = c + r + t;
   return q;
 }
 
@@ -579,7 +587,7 @@ int nvfp4_quantize_rows(const void *x, int32_t m, int32_t k, uint8_t *codes, uin
   if (!codes || !scales || !row_scale) return fail(NVFP4_EINVAL, "quantize_rows: null output pointer");
   if (misaligned(codes) || ((uintptr_t)row_scale & 3u))
     return fail(NVFP4_EINVAL, "quantize_rows: codes must be 16-byte and row_scale 4-byte aligned");
-  return hip_status(launch_quantize_rows(x, m, k, codes, scales, row_scale, (hipStream_t)stream),
+  return hip_status(launch_quantize_rows(x, m, k, codes, scales, row_scale, nullptr, (hipStream_t)stream),
                     "quantize_rows launch");
 }
 
@@ -832,10 +840,10 @@ int nvfp4_gemm_w4a4(const void *x, int32_t m, const nvfp4_weight *w, void *y, vo
   if ((rc = arena_get(q.bytes + part, &base))) return rc;
   q = quant_layout((char *)base, m, w->k);
   ProfileScope ps("gemm_w4a4", m, s);
-  if ((rc = hip_status(launch_quantize_rows(x, m, w->k, q.codes, q.scales, q.rs, s), "quantize launch")))
+  if ((rc = hip_status(launch_quantize_rows(x, m, w->k, q.codes, q.scales, q.rs, q.tiles, s), "quantize launch")))
     return rc;
   MatRef wm = mat(w);
-  return run_proj(ActRef{nullptr, q.codes, q.scales, q.rs}, m, w->k, w->n, 1, &wm, y,
+  return run_proj(ActRef{nullptr, q.codes, q.scales, q.rs, q.tiles}, m, w->k, w->n, 1, &wm, y,
                   (char *)base + q.bytes, Path::Stream, s);
 }
 
@@ -864,16 +872,16 @@ int dense_ffn_forward_w4a4(const void *x, int32_t m, int32_t hidden, int32_t int
   ProfileScope ps("dense_total w4a4", m, s);
   MatRef w2[2] = {mat(wg), mat(wu)};
   MatRef wdm = mat(wd);
-  if ((rc = hip_status(launch_quantize_rows(x, m, hidden, qx.codes, qx.scales, qx.rs, s),
+  if ((rc = hip_status(launch_quantize_rows(x, m, hidden, qx.codes, qx.scales, qx.rs, qx.tiles, s),
                        "quantize launch")))
     return rc;
-  if ((rc = run_proj(ActRef{nullptr, qx.codes, qx.scales, qx.rs}, m, hidden, inter, 2, w2, act, scr,
+  if ((rc = run_proj(ActRef{nullptr, qx.codes, qx.scales, qx.rs, qx.tiles}, m, hidden, inter, 2, w2, act, scr,
                      Path::Stream, s)))
     return rc;
-  if ((rc = hip_status(launch_quantize_rows(act, m, inter, qa.codes, qa.scales, qa.rs, s),
+  if ((rc = hip_status(launch_quantize_rows(act, m, inter, qa.codes, qa.scales, qa.rs, qa.tiles, s),
                        "quantize launch")))
     return rc;
-  return run_proj(ActRef{nullptr, qa.codes, qa.scales, qa.rs}, m, inter, hidden, 1, &wdm, out, scr,
+  return run_proj(ActRef{nullptr, qa.codes, qa.scales, qa.rs, qa.tiles}, m, inter, hidden, 1, &wdm, out, scr,
                   Path::Stream, s);
 }
 
@@ -890,7 +898,7 @@ int fp8_quantize_rows(const void *x, int32_t m, int32_t k, uint8_t *codes, float
   if (!codes || !row_scale) return fail(NVFP4_EINVAL, "fp8_quantize_rows: null output pointer");
   if (misaligned(codes) || ((uintptr_t)row_scale & 3u))
     return fail(NVFP4_EINVAL, "fp8_quantize_rows: codes must be 16-byte and row_scale 4-byte aligned");
-  return hip_status(launch_quantize_rows_fp8(x, m, k, codes, row_scale, (hipStream_t)stream),
+  return hip_status(launch_quantize_rows_fp8(x, m, k, codes, row_scale, nullptr, (hipStream_t)stream),
                     "fp8 quantize_rows launch");
 }
 
@@ -909,10 +917,10 @@ int fp8_gemm_w8a8(const void *x, int32_t m, const fp8_weight *w, void *y, void *
   if ((rc = arena_get(q.bytes + part, &base))) return rc;
   q = fp8_quant_layout((char *)base, m, w->k);
   ProfileScope ps("gemm_w8a8", m, s);
-  if ((rc = hip_status(launch_quantize_rows_fp8(x, m, w->k, q.codes, q.rs, s), "fp8 quantize launch")))
+  if ((rc = hip_status(launch_quantize_rows_fp8(x, m, w->k, q.codes, q.rs, q.tiles, s), "fp8 quantize launch")))
     return rc;
   Fp8MatRef wm = fp8_mat(w);
-  return run_w8a8(Fp8ActRef{q.codes, q.rs}, m, w->k, w->n, 1, &wm, y, (char *)base + q.bytes, s);
+  return run_w8a8(Fp8ActRef{q.codes, q.rs, q.tiles}, m, w->k, w->n, 1, &wm, y, (char *)base + q.bytes, s);
 }
 
 int dense_ffn_forward_w8a8(const void *x, int32_t m, int32_t hidden, int32_t inter,
@@ -952,12 +960,12 @@ int dense_ffn_forward_w8a8(const void *x, int32_t m, int32_t hidden, int32_t int
   ProfileScope ps("dense_total w8a8", m, s);
   Fp8MatRef w2[2] = {fp8_mat(wg), fp8_mat(wu)};
   Fp8MatRef wdm = fp8_mat(wd);
-  if ((rc = hip_status(launch_quantize_rows_fp8(x, m, hidden, qx.codes, qx.rs, s), "fp8 quantize launch")))
+  if ((rc = hip_status(launch_quantize_rows_fp8(x, m, hidden, qx.codes, qx.rs, qx.tiles, s), "fp8 quantize launch")))
     return rc;
-  if ((rc = run_w8a8(Fp8ActRef{qx.codes, qx.rs}, m, hidden, inter, 2, w2, act, scr, s))) return rc;
-  if ((rc = hip_status(launch_quantize_rows_fp8(act, m, inter, qa.codes, qa.rs, s), "fp8 quantize launch")))
+  if ((rc = run_w8a8(Fp8ActRef{qx.codes, qx.rs, qx.tiles}, m, hidden, inter, 2, w2, act, scr, s))) return rc;
+  if ((rc = hip_status(launch_quantize_rows_fp8(act, m, inter, qa.codes, qa.rs, qa.tiles, s), "fp8 quantize launch")))
     return rc;
-  return run_w8a8(Fp8ActRef{qa.codes, qa.rs}, m, inter, hidden, 1, &wdm, out, scr, s);
+  return run_w8a8(Fp8ActRef{qa.codes, qa.rs, qa.tiles}, m, inter, hidden, 1, &wdm, out, scr, s);
 }
 
 int q2_gemm_w2a16(const void *x, int32_t m, const q2_weight *w, void *y, void *stream) {

@@ -149,10 +149,30 @@ __device__ __forceinline__ void encode_blocks(const uint4 *xv4, int nblk, const 
   }
 }
 
+// Operand tiles (layout in launchers.h): the 16-byte slot of row r holding
+// the eight K values from K0 (a multiple of 8), in fp16 units, for the
+// NVFP4 (FP8 = false) or FP8 sub-step order.
+template <bool FP8>
+__device__ __forceinline__ size_t tile_slot(int r, int K0, int nsteps) {
+  const int t = K0 >> 7, kw = K0 & 127;
+  const int g = FP8 ? (kw >> 4) & 3 : kw >> 5;
+  const int j = FP8 ? 2 * (kw >> 6) + ((kw >> 3) & 1) : (kw >> 3) & 3;
+  return ((((size_t)(r >> 4) * nsteps + t) * 4 + j) * 64 + (r & 15) + 16 * g) * 8;
+}
+// Zero the tile slots of K in [k, whole steps) of row r (slice 0 only).
+template <bool FP8>
+__device__ __forceinline__ void zero_tile_tail(uint16_t *tiles, int r, int k) {
+  const int nsteps = (k + 127) >> 7;
+  if (blockIdx.y != 0) return;
+  for (int K0 = k + 8 * (int)threadIdx.x; K0 < nsteps * 128; K0 += 8 * (int)blockDim.x)
+    *(uint4 *)(tiles + tile_slot<FP8>(r, K0, nsteps)) = make_uint4(0u, 0u, 0u, 0u);
+}
+
 __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16_t *__restrict__ x, int k,
                                                                    uint8_t *__restrict__ codes,
                                                                    uint8_t *__restrict__ scales,
-                                                                   float *__restrict__ row_scale) {
+                                                                   float *__restrict__ row_scale,
+                                                                   uint16_t *__restrict__ tiles) {
   const int r = blockIdx.x;
   const int nblk = k >> 4;
   const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
@@ -191,8 +211,18 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
     }
     *(uint2 *)(codes + (size_t)r * (k >> 1) + 8 * b) = make_uint2(packed[0], packed[1]);
     scales[(size_t)r * nblk + b] = (uint8_t)sb;
+    if (tiles) {
+      // the decoded block (exact in fp16), as the streaming kernels decode it
+      const _Float16 sh = e4m3x2_to_f16x2(sb)[0];
+      const int nsteps = (k + 127) >> 7;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        *(uint4 *)(tiles + tile_slot<false>(r, 16 * b + 8 * hh, nsteps)) =
+            __builtin_bit_cast(uint4, dequant8_f16(packed[hh], sh));
+    }
   };
   encode_blocks(xv4, nblk, keep, encode_block);
+  if (tiles) zero_tile_tail<false>(tiles, r, k);
 }
 
 // ---- per-row FP8 quantizer of the W8A8 arm ---------------------------------------
@@ -203,7 +233,8 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
 __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const uint16_t *__restrict__ x,
                                                                        int k,
                                                                        uint8_t *__restrict__ codes,
-                                                                       float *__restrict__ row_scale) {
+                                                                       float *__restrict__ row_scale,
+                                                                       uint16_t *__restrict__ tiles) {
   const int r = blockIdx.x;
   const int nblk = k >> 4;
   const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
@@ -225,8 +256,16 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const ui
       out[i >> 2] |= code << (8 * (i & 3));
     }
     *(uint4 *)(codes + (size_t)r * k + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
+    if (tiles) {
+      const int nsteps = (k + 127) >> 7;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        *(uint4 *)(tiles + tile_slot<true>(r, 16 * b + 8 * hh, nsteps)) =
+            __builtin_bit_cast(uint4, fp8x8_to_f16(out[2 * hh], out[2 * hh + 1]));
+    }
   };
   encode_blocks(xv4, nblk, keep, encode_block);
+  if (tiles) zero_tile_tail<true>(tiles, r, k);
 }
 
 // Quantizer launch shape: below kQuantSliceRows rows, slices of at least
@@ -263,11 +302,15 @@ hipError_t launch_zero_words(unsigned *words, int count, hipStream_t stream) {
   return hipGetLastError();
 }
 
+size_t operand_tile_bytes(int m, int k) {
+  return (size_t)cdiv(m, 16) * 16 * (size_t)cdiv(k, 128) * 128 * 2;
+}
+
 hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes, float *row_scale,
-                                    hipStream_t stream) {
+                                    uint16_t *tiles, hipStream_t stream) {
   const QuantShape q = quant_shape(m, k);
   hipLaunchKernelGGL(k_quantize_rows_fp8, q.grid, q.block, 0, stream, (const uint16_t *)x, k, codes,
-                     row_scale);
+                     row_scale, tiles);
   return hipGetLastError();
 }
 
@@ -284,10 +327,10 @@ hipError_t launch_silu_mul(const void *gate, const void *up, void *out, int64_t 
 
 
 hipError_t launch_quantize_rows(const void *x, int m, int k, uint8_t *codes, uint8_t *scales,
-                                float *row_scale, hipStream_t stream) {
+                                float *row_scale, uint16_t *tiles, hipStream_t stream) {
   const QuantShape q = quant_shape(m, k);
   hipLaunchKernelGGL(k_quantize_rows, q.grid, q.block, 0, stream, (const uint16_t *)x, k, codes, scales,
-                     row_scale);
+                     row_scale, tiles);
   return hipGetLastError();
 }
 

@@ -589,7 +589,9 @@ size_t stream_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
                               : (rows_tall > (size_t)64 * cdiv(m, 64) ? rows_tall : (size_t)64 * cdiv(m, 64));
   const size_t cols_stream = (size_t)pl.tiles * 16 * stream_ctw(n);
   const size_t cols_tall = (size_t)16 * kTallCtwWide * cdiv(n, 16 * kTallCtwWide);
-  return (size_t)nmat * pl.ksplit * rows * (cols_stream > cols_tall ? cols_stream : cols_tall);
+  const size_t own = (size_t)nmat * pl.ksplit * rows * (cols_stream > cols_tall ? cols_stream : cols_tall);
+  const size_t many = fixed_tall_partial_floats(false, nmat, m, n, pl.ksplit);
+  return own > many ? own : many;
 }
 
 // (also sizes the counters of the FP8 and Q2 streaming kernels; k_stream_tall
@@ -621,6 +623,8 @@ hipError_t launch_stream(const ActRef &a, int m, int k, int n, int nmat, const M
   p.ksplit = pl.ksplit;
   p.steps_per_split = pl.steps_per_split;
   const bool afp4 = a.x_bf16 == nullptr;
+  if (afp4 && fixed_tall_eligible(m) && a.tiles)
+    return launch_fixed_tall_w4a4(a, m, k, n, nmat, w, y, partial, counters, pl, stream);
   if (afp4 && m >= kTallMinRows) {
     const int mt = m > 64 ? kTallRowTiles : cdiv(m, 16);
     const int ctw = tall_ctw(nmat, m);

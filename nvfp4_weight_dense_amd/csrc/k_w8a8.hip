@@ -76,16 +76,6 @@ struct W8Cfg {
   static constexpr int U = kRegsPerStep * 4 <= 128 ? 4 : (kRegsPerStep * 2 < 128 ? 2 : 1);
 };
 
-// Eight E4M3 bytes (K order from the low byte of lo) -> eight exact fp16
-// values, one MFMA operand fragment.
-__device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
-  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 // the four fragments of a lane's 32 bytes (q0 = K offsets 16g.., q1 =
 // 64 + 16g..): fragment j covers bytes 8j..8j+7 of q0 then q1, so MFMA j of
 // a step sums the 32 K offsets 16g' + 8j (j < 2) or 64 + 16g' + 8(j-2)
@@ -380,7 +370,9 @@ size_t w8a8_partial_floats(const StreamPlan &pl, int nmat, int m, int n) {
   if (pl.ksplit <= 1) return 0;
   const size_t rows = m >= 64 ? (size_t)64 * cdiv(m, 64) : (size_t)16 * cdiv(m, 16);
   const int ctw = w8a8_launch_ctw(nmat, m, n);
-  return (size_t)nmat * pl.ksplit * rows * 16 * ctw * cdiv(n, 16 * ctw);
+  const size_t own = (size_t)nmat * pl.ksplit * rows * 16 * ctw * cdiv(n, 16 * ctw);
+  const size_t many = fixed_tall_partial_floats(true, nmat, m, n, pl.ksplit);
+  return own > many ? own : many;
 }
 
 hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const Fp8MatRef *w, void *y,
@@ -400,6 +392,7 @@ hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat, const 
   p.counters = counters;
   p.ksplit = pl.ksplit;
   p.steps_per_split = pl.steps_per_split;
+  if (fixed_tall_eligible(m) && a.tiles) return launch_fixed_tall_w8a8(a, m, k, n, nmat, w, y, partial, counters, pl, stream);
   const int mt = m >= 64 ? 4 : cdiv(m, 16);
   const int ctw = w8a8_launch_ctw(nmat, m, n);
   dim3 grid(cdiv(n, 16 * ctw) * pl.ksplit * cdiv(m, 64));

@@ -21,7 +21,18 @@ struct ActRef {
   const uint8_t *codes;      // [m][k/2]
   const uint8_t *scales;     // [m][k/16]
   const float *row_scale;    // [m]
+  const uint16_t *tiles;     // fp16 operand tiles (operand_tile_bytes) or nullptr
 };
+
+// fp16 operand tiles of quantized activation rows, written by the row
+// quantizers for the many-row fixed-format kernel (which copies them into
+// LDS with LDS-DMA).  For row tile rt (16 rows), 128-element K step t and
+// MFMA sub-step j there is one 1 KB block, block ((rt * nsteps + t) * 4 + j):
+// lane (c, g) = (l % 16, l / 16) holds, at bytes 16 l, the eight exact fp16
+// values of row 16 rt + c at K offsets 128 t + 32 g + 8 j + 0..7 (NVFP4
+// activations) or 128 t + 16 g + 8 j (j < 2) / 128 t + 64 + 16 g + 8 (j - 2)
+// (FP8 activations).  K past k is zero; rows past m are not written.
+size_t operand_tile_bytes(int m, int k);
 
 // Weight-streaming projection, nmat = 1 (y = x.W^T) or 2
 // (y = bf16(silu(bf16(x.W0^T)) * bf16(x.W1^T))): bf16 activations up to 16
@@ -163,8 +174,10 @@ hipError_t launch_zero_words(unsigned *words, int count, hipStream_t stream);
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out,
                            int64_t count, hipStream_t stream);
 
+// Per-row NVFP4 quantizer; with `tiles` (operand_tile_bytes(m, k) bytes)
+// it also writes the decoded rows as fp16 operand tiles.
 hipError_t launch_quantize_rows(const void *x, int m, int k, uint8_t *codes,
-                                uint8_t *scales, float *row_scale,
+                                uint8_t *scales, float *row_scale, uint16_t *tiles,
                                 hipStream_t stream);
 
 // Column tiles per workgroup of the weight-streaming kernels (1 or 2).
@@ -178,10 +191,12 @@ struct Fp8MatRef {
 struct Fp8ActRef {
   const uint8_t *codes;    // E4M3 [m][k]
   const float *row_scale;  // [m]
+  const uint16_t *tiles;   // fp16 operand tiles (operand_tile_bytes) or nullptr
 };
-// Per-row FP8 quantizer: s_row = amax/448, codes = E4M3(x / s_row).
+// Per-row FP8 quantizer: s_row = amax/448, codes = E4M3(x / s_row); with
+// `tiles`, also the decoded rows as fp16 operand tiles.
 hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes,
-                                    float *row_scale, hipStream_t stream);
+                                    float *row_scale, uint16_t *tiles, hipStream_t stream);
 // ---- packed-Q2 weights: 2-bit codes, fp16 scale per group, bf16 activations ----
 struct Q2MatRef {
   const uint8_t *codes;    // [n][k/4]
@@ -222,6 +237,25 @@ hipError_t launch_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat,
                        const Fp8MatRef *w, void *y, float *partial,
                        unsigned *counters, const StreamPlan &pl,
                        hipStream_t stream);
+
+// Many-row fixed-format projections (W4A4 NVFP4 activations, W8A8 FP8),
+// from kFixedTallMinRows rows: eight-wave workgroups of 64 or 128 rows
+// share every decoded activation fragment, and every output keeps the K
+// order of the streaming kernels' plan `pl` (stream_plan for W4A4,
+// w8a8_plan for W8A8), so a row's bits do not depend on m.  With
+// pl.ksplit > 1, `partial` holds fixed_tall_partial_floats(...) floats and
+// `counters` stream_counter_words(pl, m) zero words (left zero).
+constexpr int kFixedTallMinRows = 65;
+bool fixed_tall_eligible(int m);
+size_t fixed_tall_partial_floats(bool fp8, int nmat, int m, int n, int ksplit);
+hipError_t launch_fixed_tall_w4a4(const ActRef &a, int m, int k, int n, int nmat,
+                                  const MatRef *w, void *y, float *partial,
+                                  unsigned *counters, const StreamPlan &pl,
+                                  hipStream_t stream);
+hipError_t launch_fixed_tall_w8a8(const Fp8ActRef &a, int m, int k, int n, int nmat,
+                                  const Fp8MatRef *w, void *y, float *partial,
+                                  unsigned *counters, const StreamPlan &pl,
+                                  hipStream_t stream);
 
 // Register-only bf16 MFMA loop (a measurement aid): `workgroups` groups of
 // four waves, each wave iters x 4 v_mfma_f32_32x32x16_bf16.  sink: 256

@@ -51,7 +51,7 @@ def test_dequant_every_code_and_scale_exact(m):
     assert np.all(got[32:] & 0x7FFF == 0)
 
 
-@pytest.mark.parametrize("m", [8, 32, 96])  # streaming kernel; two-stage kernel: 32 rows, 64-row blocks
+@pytest.mark.parametrize("m", [8, 32, 96])  # streaming kernel; two-stage kernel: 32 rows; many-row kernel: 96
 def test_w4a4_dequant_every_code_and_scale(m):
     """The fp16 dequantization of the W4A4 path (both operands NVFP4): rows
     r < 32 of x are one-hot at K = r, so each output is one product a_r *
@@ -232,6 +232,45 @@ def test_gemm_w4a4_rows_independent_of_m():
         y = nv.nvfp4_gemm_w4a4(x[:m].contiguous(), w)
         sync()
         assert torch.equal(y.view(torch.int16), ref[:m].view(torch.int16)), ("split", m)
+
+
+def _by_row_blocks(fn, x, block=16):
+    """fn over consecutive blocks of `block` rows (the few-row kernels),
+    stacked: the reference for a many-row launch, row for row."""
+    return torch.cat([fn(x[r:r + block].contiguous()) for r in range(0, x.shape[0], block)])
+
+
+# The many-row fixed-format kernel (from 65 rows) walks each output's four
+# step classes one after another; its rows must equal the few-row streaming
+# kernel's bit for bit.  Shapes: K split over four workgroups (n = 64,
+# k = 4096) and over two (the down projection's 4096 x 14336), splits of two
+# and three steps (k = 160, 384: idle classes), ragged rows and columns, and
+# two column tiles per workgroup on the streaming side (n = 16400).
+@pytest.mark.parametrize("m,n,k", [(65, 64, 4096), (200, 300, 160), (130, 1000, 384), (257, 16400, 512),
+                                   (129, 4096, 14336)])
+def test_gemm_w4a4_many_rows_equal_few_rows(m, n, k):
+    _say(f"w4a4 many rows vs 16-row blocks m={m} n={n} k={k}")
+    x = si.activations(m, k, seed=n + k, outliers=True).cuda()
+    w = g_weight(si.weight(n, k, seed=m, code_stream=5, scale_stream=6, ts=0.75))
+    y = nv.nvfp4_gemm_w4a4(x, w)
+    ref = _by_row_blocks(lambda xb: nv.nvfp4_gemm_w4a4(xb, w), x)
+    sync()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("m", [65, 200])
+def test_dense_ffn_w4a4_many_rows_equal_few_rows(m):
+    """gate+up+silu (two matrices per workgroup) and the down projection on
+    the tiny FFN: a two-step gate+up split (two idle classes) and a six-step
+    down projection."""
+    _say(f"ffn w4a4 many rows vs 16-row blocks m={m}")
+    x, wg, wu, wd = si.workload("tiny", m=m)
+    W = [g_weight(w) for w in (wg, wu, wd)]
+    xd = x.cuda()
+    y = nv.dense_ffn_forward_w4a4(xd, *W)
+    ref = _by_row_blocks(lambda xb: nv.dense_ffn_forward_w4a4(xb, *W), xd)
+    sync()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
 
 
 # ---- gate+up+silu entry point -----------------------------------------------------------------

@@ -173,6 +173,38 @@ def test_dense_ffn_w8a8_batch_invariance():
     assert torch.equal(y.view(torch.int16), ref[perm].view(torch.int16))
 
 
+def _by_row_blocks(fn, x, block=16):
+    return torch.cat([fn(x[r:r + block].contiguous()) for r in range(0, x.shape[0], block)])
+
+
+# The many-row kernel (from 65 rows) against the few-row kernel, row for row
+# and bit for bit: K split over workgroups (n = 64, k = 4096; the down
+# projection's 4096 x 14336), splits of two and three steps (idle classes),
+# ragged rows, columns and K, a partial scale block along N and K.
+@pytest.mark.parametrize("m,n,k", [(65, 64, 4096), (200, 300, 160), (130, 1000, 352), (257, 16400, 512),
+                                   (129, 4096, 14336)])
+def test_fp8_gemm_w8a8_many_rows_equal_few_rows(m, n, k):
+    _say(f"fp8 gemm many rows vs 16-row blocks m={m} n={n} k={k}")
+    x = _rows_with_edge_cases(m, k, seed=n + k).cuda()
+    w = g8(si.fp8_weight(n, k, seed=m, which=1))
+    y = nv.fp8_gemm_w8a8(x, w)
+    ref = _by_row_blocks(lambda xb: nv.fp8_gemm_w8a8(xb, w), x)
+    sync()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("m", [65, 200])
+def test_dense_ffn_w8a8_many_rows_equal_few_rows(m):
+    _say(f"ffn w8a8 many rows vs 16-row blocks m={m}")
+    x, wg, wu, wd = si.fp8_workload("tiny", m=m)
+    W = [g8(w) for w in (wg, wu, wd)]
+    xd = x.cuda()
+    y = nv.dense_ffn_forward_w8a8(xd, *W)
+    ref = _by_row_blocks(lambda xb: nv.dense_ffn_forward_w8a8(xb, *W), xd)
+    sync()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
 def test_w8a8_m_zero_and_errors_touch_nothing():
     _say("w8a8 m=0 / errors")
     x, wg, wu, wd = si.fp8_workload("tiny", m=4)
