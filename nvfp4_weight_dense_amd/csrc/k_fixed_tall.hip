@@ -114,15 +114,18 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
   constexpr int kWgCols = NMAT == 2 ? 16 * kNW : 16 * kTiles;  // output columns per workgroup
   constexpr int kABytes = MT * 4 * 1024;                       // activation fragments per step
   constexpr int kBTile = FP8 ? 2048 : 1024;                    // codes of a weight tile per step
-  constexpr int kStageBytes = kABytes + kTiles * kBTile;
+  constexpr int kWBytes = kTiles * kBTile;                     // weight codes per step
   constexpr int kADma = MT / 2;                                // 1 KB activation blocks per wave
   constexpr int kReqs = kADma + (kBTile / 1024 + 1) * kNC;     // vector-memory requests per wave and step
   static_assert(MT % 2 == 0 && (MT * 4) % kNW == 0, "activation blocks per wave");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
-  __shared__ unsigned last_flag;
+  // activation fragments: three stages (shared by all waves); weight codes:
+  // two stages (each wave reads only its own tiles, at the start of a step,
+  // so the copy two steps ahead may overwrite them right after)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kABytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kABytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kABytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ldsw[2][kWBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,8 +188,9 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
   // pair (row c, K 32 g of the step), FP8 the tile's block scale
   uint32_t scs[kStages][kNC];
 
-  // ---- copies of step i into stage s ----
-  auto issue = [&](int i, int s) __attribute__((always_inline)) {
+  // ---- copies of step i: activations into stage s, weights into weight
+  // stage ws (scales into register slot s) ----
+  auto issue = [&](int i, int s, int ws) __attribute__((always_inline)) {
     const int t = step_at(i);
     const bool live = t < s_end;
     uint8_t *st = stage(s);
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
 #pragma unroll
     for (int ct = 0; ct < kNC; ++ct) {
       const int mat = tile_mat(ct);
-      uint8_t *bt = st + kABytes + (kNC * wave + ct) * kBTile;
+      uint8_t *bt = ldsw[ws] + (kNC * wave + ct) * kBTile;
       if constexpr (FP8) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -247,8 +251,8 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
     uint4 w[kNC][FP8 ? 2 : 1];
     uint32_t sc[kNC];
   };
-  auto read_w = [&](int s, WOps &wo) __attribute__((always_inline)) {
-    const uint8_t *sbw = stage(s) + kABytes + kNC * wave * kBTile;
+  auto read_w = [&](int s, int ws, WOps &wo) __attribute__((always_inline)) {
+    const uint8_t *sbw = ldsw[ws] + kNC * wave * kBTile;
 #pragma unroll
     for (int ct = 0; ct < kNC; ++ct) {
       if constexpr (FP8) {
@@ -271,42 +275,60 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
     };
     f16x8 af[2][MT];
     if constexpr (FP8) {
-      f16x8 bf[kNC][4];
+      // fragment j of the lane's weight bytes: q0 bytes 8 j.. (j < 2), q1
+      // bytes 8 (j - 2).. (j >= 2)
+      auto bdec8 = [&](int j, f16x8 (&b)[kNC]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ct = 0; ct < kNC; ++ct) {
+          const uint4 &q = wo.w[ct][j >> 1];
+          b[ct] = (j & 1) ? fp8x8_to_f16(q.z, q.w) : fp8x8_to_f16(q.x, q.y);
+        }
+      };
       float sv[kNC];
 #pragma unroll
-      for (int ct = 0; ct < kNC; ++ct) {
-        const uint4 q0 = wo.w[ct][0];
-        const uint4 q1 = wo.w[ct][FP8 ? 1 : 0];
-        bf[ct][0] = fp8x8_to_f16(q0.x, q0.y);
-        bf[ct][1] = fp8x8_to_f16(q0.z, q0.w);
-        bf[ct][2] = fp8x8_to_f16(q1.x, q1.y);
-        bf[ct][3] = fp8x8_to_f16(q1.z, q1.w);
-        sv[ct] = __uint_as_float(wo.sc[ct]);
-      }
-      f32x4 pb[MT][kNC];
+      for (int ct = 0; ct < kNC; ++ct) sv[ct] = __uint_as_float(wo.sc[ct]);
+      // block products of up to four row tiles at a time (eight independent
+      // MFMA chains), then cur = fma(scale, block product, cur)
+      constexpr int kH = MT < 4 ? MT : 4;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int m0 = 0; m0 < MT; m0 += kH) {
+        f32x4 pb[kH][kNC];
 #pragma unroll
-        for (int ct = 0; ct < kNC; ++ct) pb[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      aread(0, af[0]);
+        for (int mt = 0; mt < kH; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j < 3) aread(j + 1, af[(j + 1) & 1]);
+          for (int ct = 0; ct < kNC; ++ct) pb[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f16x8 ah[2][kH], bf[2][kNC];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < kH; ++mt) ah[0][mt] = *(const f16x8 *)(sa + ((m0 + mt) * 4) * 1024 + lane * 16);
+        bdec8(0, bf[0]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < 3) {
+#pragma unroll
+            for (int mt = 0; mt < kH; ++mt)
+              ah[(j + 1) & 1][mt] = *(const f16x8 *)(sa + ((m0 + mt) * 4 + j + 1) * 1024 + lane * 16);
+            bdec8(j + 1, bf[(j + 1) & 1]);
+          }
+#pragma unroll
+          for (int mt = 0; mt < kH; ++mt)
+#pragma unroll
+            for (int ct = 0; ct < kNC; ++ct)
+              pb[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[j & 1][mt], bf[j & 1][ct], pb[mt][ct], 0, 0, 0);
+          if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, kH, 0);
+#pragma unroll
+          for (int qq = 0; qq < kH * kNC; ++qq) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < kH; ++mt)
 #pragma unroll
           for (int ct = 0; ct < kNC; ++ct)
-            pb[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j & 1][mt], bf[ct][j], pb[mt][ct], 0, 0, 0);
-        if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, MT * kNC, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              cur[m0 + mt][ct][e] = __builtin_fmaf(sv[ct], pb[mt][ct][e], cur[m0 + mt][ct][e]);
       }
-      // the block product, scaled into the class sum
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ct = 0; ct < kNC; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) cur[mt][ct][e] = __builtin_fmaf(sv[ct], pb[mt][ct][e], cur[mt][ct][e]);
     } else {
       f16x2 s01[kNC];
 #pragma unroll
@@ -355,25 +377,30 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
   };
 
   // ---- main loop over the class-by-class step sequence ----
-  issue(0, 0);
-  issue(1, 1);
+  issue(0, 0, 0);
+  issue(1, 1, 1);
   wait_vm<kReqs>();
   lds_barrier();
 
   int cls = 0;                   // class in progress
   int cls_end = class_count(0);  // sequence position where it ends
-  // One sequence position: copy step i + 2 into the stage step i - 1 used
-  // (free since the last barrier), multiply step i (stage i % 3), wait for
-  // step i + 1's copies, barrier: every copy has two steps' MFMAs to land.
-  // Every position issues the same requests and barrier whether or not it
+  // One sequence position: read this wave's weight bytes of step i (weight
+  // stage i % 2), copy step i + 2 into the activation stage step i - 1
+  // used (free since the last barrier) and into the weight stage just
+  // read, multiply step i (activation stage i % 3), wait for step i + 1's
+  // copies, barrier: every copy has two steps' MFMAs to land.  Every
+  // position issues the same requests and barrier whether or not it
   // computes (the last group may run past the split), so the compiler's
   // wait counts see one request sequence.
   auto unit = [&](int i, auto phase) __attribute__((always_inline)) {
     constexpr int PH = decltype(phase)::value;  // i % 3
+    const int ws = i & 1;                       // weight stage (wave-uniform)
     WOps wo;
-    read_w(PH, wo);
+    read_w(PH, ws, wo);
+    // the reads are complete before the copy into the same weight stage
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
-    issue(i + 2, (PH + 2) % 3);
+    issue(i + 2, (PH + 2) % 3, ws);
     __builtin_amdgcn_sched_barrier(0);
     if (i < S) compute(PH, wo);
     __builtin_amdgcn_sched_barrier(0);
@@ -415,12 +442,15 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
     }
     wait_all_memory();
     __syncthreads();
+    // (the weight stages are free: every wave has passed its loop and its
+    // final wait for all requests)
+    unsigned *last_flag = (unsigned *)ldsw[0];
     if (tid == 0) {
       const unsigned old = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_flag = old == (unsigned)(p.ksplit - 1);
+      *last_flag = old == (unsigned)(p.ksplit - 1);
     }
     __syncthreads();
-    if (!last_flag) return;
+    if (!*last_flag) return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -481,12 +511,11 @@ __global__ __launch_bounds__(kThreads) void k_fixed_tall(TallArgs p) {
 constexpr int kTargetWG = 256;  // one workgroup per CU
 
 // Row tiles per workgroup: eight (each decoded weight fragment feeds eight
-// MFMAs) when that still gives every CU a workgroup, else four.  FP8 keeps
-// four: with eight its register stages do not fit two waves per SIMD.
+// MFMAs, and every weight byte is copied half as often) when that still
+// gives every CU a workgroup, else four.
 template <bool FP8, int NMAT>
 int tall_mt(int m, int n, int ksplit) {
   constexpr int wg_cols = NMAT == 2 ? 16 * kNW : 16 * kTiles;
-  if (FP8) return 4;
   return cdiv(m, 128) * ksplit * cdiv(n, wg_cols) >= kTargetWG ? 8 : 4;
 }
 
@@ -494,13 +523,10 @@ template <bool FP8, int NMAT>
 hipError_t launch_tall(const TallArgs &p, int mt, hipStream_t s) {
   constexpr int wg_cols = NMAT == 2 ? 16 * kNW : 16 * kTiles;
   const dim3 grid(cdiv(p.m, 16 * mt) * p.ksplit * cdiv(p.n, wg_cols));
-  if constexpr (!FP8) {
-    if (mt == 8) {
-      hipLaunchKernelGGL((k_fixed_tall<FP8, NMAT, 8>), grid, dim3(kThreads), 0, s, p);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((k_fixed_tall<FP8, NMAT, 4>), grid, dim3(kThreads), 0, s, p);
+  if (mt == 8)
+    hipLaunchKernelGGL((k_fixed_tall<FP8, NMAT, 8>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_fixed_tall<FP8, NMAT, 4>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
