@@ -358,8 +358,9 @@ int check_ffn(const void *x, int m, int hidden, int inter, const nvfp4_weight *w
   return NVFP4_OK;
 }
 
-// quantized activation rows; from kFixedTallMinRows rows also their fp16
-// operand tiles (read by the many-row kernel)
+// quantized activation rows: codes, scales and row scales; from
+// kFixedTallMinRows rows the row scales and fp16 operand tiles instead
+// (all the many-row kernel reads)
 struct QuantBuf {
   uint8_t *codes;
   uint8_t *scales;
@@ -370,12 +371,13 @@ struct QuantBuf {
 
 QuantBuf quant_layout(char *base, int m, int k) {
   QuantBuf q;
-  size_t c = align256((size_t)m * k / 2), s = align256((size_t)m * k / 16), r = align256((size_t)m * 4);
-  size_t t = fixed_tall_eligible(m) ? align256(operand_tile_bytes(m, k)) : 0;
-  q.codes = (uint8_t *)base;
-  q.scales = base ? (uint8_t *)(base + c) : nullptr;
+  const bool tiled = fixed_tall_eligible(m);
+  const size_t c = tiled ? 0 : align256((size_t)m * k / 2), s = tiled ? 0 : align256((size_t)m * k / 16);
+  const size_t r = align256((size_t)m * 4), t = tiled ? align256(operand_tile_bytes(m, k)) : 0;
+  q.codes = base && !tiled ? (uint8_t *)base : nullptr;
+  q.scales = base && !tiled ? (uint8_t *)(base + c) : nullptr;
   q.rs = base ? (float *)(base + c + s) : nullptr;
-  q.tiles = base && t ? (uint16_t *)(base + c + s + r) : nullptr;
+  q.tiles = base && tiled ? (uint16_t *)(base + c + s + r) : nullptr;
   q.bytes = c + s + r + t;
   return q;
 }
@@ -414,11 +416,12 @@ struct Fp8QuantBuf {
 
 Fp8QuantBuf fp8_quant_layout(char *base, int m, int k) {
   Fp8QuantBuf q;
-  const size_t c = align256((size_t)m * k), r = align256((size_t)m * 4);
-  const size_t t = fixed_tall_eligible(m) ? align256(operand_tile_bytes(m, k)) : 0;
-  q.codes = (uint8_t *)base;
+  const bool tiled = fixed_tall_eligible(m);  // as quant_layout: tiles instead of codes
+  const size_t c = tiled ? 0 : align256((size_t)m * k), r = align256((size_t)m * 4);
+  const size_t t = tiled ? align256(operand_tile_bytes(m, k)) : 0;
+  q.codes = base && !tiled ? (uint8_t *)base : nullptr;
   q.rs = base ? (float *)(base + c) : nullptr;
-  q.tiles = base && t ? (uint16_t *)(base + c + r) : nullptr;
+  q.tiles = base && tiled ? (uint16_t *)(base + c + r) : nullptr;
   q.bytes = c + r + t;
   return q;
 }

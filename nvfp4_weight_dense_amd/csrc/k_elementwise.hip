@@ -209,9 +209,10 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
         code = e2m1_encode_sat(xv[i] / den);
       packed[i >> 3] |= code << (4 * (i & 7));
     }
-    *(uint2 *)(codes + (size_t)r * (k >> 1) + 8 * b) = make_uint2(packed[0], packed[1]);
-    scales[(size_t)r * nblk + b] = (uint8_t)sb;
-    if (tiles) {
+    if (!tiles) {
+      *(uint2 *)(codes + (size_t)r * (k >> 1) + 8 * b) = make_uint2(packed[0], packed[1]);
+      scales[(size_t)r * nblk + b] = (uint8_t)sb;
+    } else {
       // the decoded block (exact in fp16), as the streaming kernels decode it
       const _Float16 sh = e4m3x2_to_f16x2(sb)[0];
       const int nsteps = (k + 127) >> 7;
@@ -255,8 +256,9 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const ui
       const uint32_t code = ((__float_as_uint(q) >> 31) << 7) | e4m3_encode_sat(q);
       out[i >> 2] |= code << (8 * (i & 3));
     }
-    *(uint4 *)(codes + (size_t)r * k + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
-    if (tiles) {
+    if (!tiles) {
+      *(uint4 *)(codes + (size_t)r * k + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
+    } else {
       const int nsteps = (k + 127) >> 7;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)

@@ -174,8 +174,10 @@ hipError_t launch_zero_words(unsigned *words, int count, hipStream_t stream);
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out,
                            int64_t count, hipStream_t stream);
 
-// Per-row NVFP4 quantizer; with `tiles` (operand_tile_bytes(m, k) bytes)
-// it also writes the decoded rows as fp16 operand tiles.
+// Per-row NVFP4 quantizer: codes, scales and row scales; with `tiles`
+// (operand_tile_bytes(m, k) bytes) it writes the row scales and the decoded
+// rows as fp16 operand tiles instead of the codes and scales (the many-row
+// kernel reads nothing else).
 hipError_t launch_quantize_rows(const void *x, int m, int k, uint8_t *codes,
                                 uint8_t *scales, float *row_scale, uint16_t *tiles,
                                 hipStream_t stream);
@@ -194,7 +196,7 @@ struct Fp8ActRef {
   const uint16_t *tiles;   // fp16 operand tiles (operand_tile_bytes) or nullptr
 };
 // Per-row FP8 quantizer: s_row = amax/448, codes = E4M3(x / s_row); with
-// `tiles`, also the decoded rows as fp16 operand tiles.
+// `tiles`, the decoded rows as fp16 operand tiles instead of the codes.
 hipError_t launch_quantize_rows_fp8(const void *x, int m, int k, uint8_t *codes,
                                     float *row_scale, uint16_t *tiles, hipStream_t stream);
 // ---- packed-Q2 weights: 2-bit codes, fp16 scale per group, bf16 activations ----
