@@ -130,10 +130,27 @@ __device__ __forceinline__ float row_amax(const uint4 *xv4, int nblk, uint4 (&ke
   return amax;
 }
 
+// The (row, slice) of this workgroup.  Workgroups go to the eight XCDs in
+// turn (dispatch index L to XCD L mod 8), and each XCD takes one contiguous
+// run of (row, slice) pairs, rows outermost: the slices of a row share its
+// amax reads through one L2, and the 16 rows of an operand tile -- whose
+// 16-byte pieces interleave in memory -- are written through one L2, so
+// whole lines reach memory instead of pieces from several XCDs.
+struct RowSlice {
+  int r, s;
+};
+__device__ __forceinline__ RowSlice row_slice() {
+  const int S = (int)gridDim.y, total = (int)gridDim.x * S;
+  const int L = (int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x;
+  const int q = total >> 3, rem = total & 7, xcd = L & 7;
+  const int u = xcd * q + min(xcd, rem) + (L >> 3);
+  return RowSlice{u / S, u % S};
+}
+
 // Encode this workgroup's blocks: all of the row (one slice: the kept blocks
-// from registers), or slice blockIdx.y's run of blocks.
+// from registers), or slice s's run of blocks.
 template <class Enc>
-__device__ __forceinline__ void encode_blocks(const uint4 *xv4, int nblk, const uint4 (&keep)[kKeep][2],
+__device__ __forceinline__ void encode_blocks(const uint4 *xv4, int nblk, int s, const uint4 (&keep)[kKeep][2],
                                               Enc &&encode_block) {
   const int nt = blockDim.x, t = threadIdx.x;
   if (gridDim.y == 1) {
@@ -144,7 +161,7 @@ __device__ __forceinline__ void encode_blocks(const uint4 *xv4, int nblk, const 
     for (; b < nblk; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
   } else {
     const int per = (nblk + (int)gridDim.y - 1) / (int)gridDim.y;
-    const int b0 = (int)blockIdx.y * per, b1 = min(nblk, b0 + per);
+    const int b0 = s * per, b1 = min(nblk, b0 + per);
     for (int b = b0 + t; b < b1; b += nt) encode_block(b, xv4[2 * b], xv4[2 * b + 1]);
   }
 }
@@ -161,9 +178,9 @@ __device__ __forceinline__ size_t tile_slot(int r, int K0, int nsteps) {
 }
 // Zero the tile slots of K in [k, whole steps) of row r (slice 0 only).
 template <bool FP8>
-__device__ __forceinline__ void zero_tile_tail(uint16_t *tiles, int r, int k) {
+__device__ __forceinline__ void zero_tile_tail(uint16_t *tiles, int r, int s, int k) {
   const int nsteps = (k + 127) >> 7;
-  if (blockIdx.y != 0) return;
+  if (s != 0) return;
   for (int K0 = k + 8 * (int)threadIdx.x; K0 < nsteps * 128; K0 += 8 * (int)blockDim.x)
     *(uint4 *)(tiles + tile_slot<FP8>(r, K0, nsteps)) = make_uint4(0u, 0u, 0u, 0u);
 }
@@ -173,7 +190,8 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
                                                                    uint8_t *__restrict__ scales,
                                                                    float *__restrict__ row_scale,
                                                                    uint16_t *__restrict__ tiles) {
-  const int r = blockIdx.x;
+  const RowSlice rs = row_slice();
+  const int r = rs.r;
   const int nblk = k >> 4;
   const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
 
@@ -181,7 +199,7 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
   const float amax = row_amax(xv4, nblk, keep);
   float s_row = amax / 2688.0f;
   if (amax == 0.0f) s_row = 1.0f;
-  if (threadIdx.x == 0 && blockIdx.y == 0) row_scale[r] = s_row;
+  if (threadIdx.x == 0 && rs.s == 0) row_scale[r] = s_row;
 
   auto encode_block = [&](int b, const uint4 &v0, const uint4 &v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -222,8 +240,8 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
             __builtin_bit_cast(uint4, dequant8_f16(packed[hh], sh));
     }
   };
-  encode_blocks(xv4, nblk, keep, encode_block);
-  if (tiles) zero_tile_tail<false>(tiles, r, k);
+  encode_blocks(xv4, nblk, rs.s, keep, encode_block);
+  if (tiles) zero_tile_tail<false>(tiles, r, rs.s, k);
 }
 
 // ---- per-row FP8 quantizer of the W8A8 arm ---------------------------------------
@@ -236,7 +254,8 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const ui
                                                                        uint8_t *__restrict__ codes,
                                                                        float *__restrict__ row_scale,
                                                                        uint16_t *__restrict__ tiles) {
-  const int r = blockIdx.x;
+  const RowSlice rs = row_slice();
+  const int r = rs.r;
   const int nblk = k >> 4;
   const uint4 *xv4 = (const uint4 *)(x + (size_t)r * k);
 
@@ -244,7 +263,7 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const ui
   const float amax = row_amax(xv4, nblk, keep);
   float s_row = amax / 448.0f;
   if (amax == 0.0f) s_row = 1.0f;
-  if (threadIdx.x == 0 && blockIdx.y == 0) row_scale[r] = s_row;
+  if (threadIdx.x == 0 && rs.s == 0) row_scale[r] = s_row;
 
   auto encode_block = [&](int b, const uint4 &v0, const uint4 &v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -266,8 +285,8 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const ui
             __builtin_bit_cast(uint4, fp8x8_to_f16(out[2 * hh], out[2 * hh + 1]));
     }
   };
-  encode_blocks(xv4, nblk, keep, encode_block);
-  if (tiles) zero_tile_tail<true>(tiles, r, k);
+  encode_blocks(xv4, nblk, rs.s, keep, encode_block);
+  if (tiles) zero_tile_tail<true>(tiles, r, rs.s, k);
 }
 
 // Quantizer launch shape: below kQuantSliceRows rows, slices of at least
