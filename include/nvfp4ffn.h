@@ -342,6 +342,20 @@ int nvfp4_probe_mfma_bf16(int32_t workgroups, int32_t iters, float *sink,
 int nvfp4_probe_read(const void *src, int64_t bytes, uint32_t never, float *sink,
                      void *stream);
 
+/* Test aid, not a step of the FFN: the division and rounding steps of the
+ * activation quantizers (nvfp4_quantize_rows, fp8_quantize_rows) applied to
+ * arbitrary inputs, so that tests can compare them with their definitions on
+ * any fp32 value.  x: device fp32 [n], n a positive multiple of 8.  Outputs
+ * (device): q fp32 [n], q[i] = x[i] / d rounded to nearest as the
+ * quantizers divide; e2m1 uint8 [n], the E2M1 code of x[i] (nearest, ties to
+ * the even code, saturating at 6, sign kept: the code step of
+ * nvfp4_quantize_rows); e4m3 uint8 [n], the E4M3FN byte of x[i] (nearest-even,
+ * saturating at 448, sign kept: the code step of fp8_quantize_rows).  NaN
+ * inputs have no defined codes.  NVFP4_EINVAL for a null pointer, a bad n
+ * or a d that is not a positive finite number. */
+int nvfp4_probe_encode(const float *x, int64_t n, float d, float *q, uint8_t *e2m1,
+                       uint8_t *e4m3, void *stream);
+
 /* ABI version of this header (bumped on incompatible change). */
 int32_t nvfp4_abi_version(void);
 

@@ -42,6 +42,7 @@ __all__ = [
     "nvfp4_last_error", "nvfp4_release", "nvfp4_abi_version", "load_library",
     "nvfp4_probe_mfma_bf16",
     "nvfp4_probe_read",
+    "nvfp4_probe_encode",
 ]
 
 
@@ -171,6 +172,8 @@ def load_library(path: str = LIB_PATH):
     L.nvfp4_probe_mfma_bf16.restype = ctypes.c_int
     L.nvfp4_probe_read.argtypes = [vp, i64, ctypes.c_uint32, vp, vp]
     L.nvfp4_probe_read.restype = ctypes.c_int
+    L.nvfp4_probe_encode.argtypes = [vp, i64, ctypes.c_float, vp, vp, vp, vp]
+    L.nvfp4_probe_encode.restype = ctypes.c_int
     L.nvfp4_last_error.argtypes = []
     L.nvfp4_last_error.restype = ctypes.c_char_p
     L.nvfp4_release.argtypes = []
@@ -285,6 +288,24 @@ def nvfp4_probe_read(src: torch.Tensor, nbytes: int, never: int, sink: torch.Ten
     if sink.dtype != torch.float32 or sink.numel() < 256 or not sink.is_cuda:
         raise ValueError("sink: expected a float32 GPU tensor of at least 256 elements")
     _check(L.nvfp4_probe_read(_ptr(src), int(nbytes), int(never) & 0xFFFFFFFF, _ptr(sink), _stream(stream)))
+
+
+def nvfp4_probe_encode(x: torch.Tensor, d: float, stream=None):
+    """The activation quantizers' division and rounding steps on arbitrary
+    values (a test aid): x a contiguous float32 GPU tensor with a multiple of
+    8 elements, d a positive finite divisor.  Returns (q, e2m1, e4m3): q =
+    x / d as the quantizers divide (fp32), and the E2M1 code and E4M3FN byte
+    of each x (uint8), as the quantizers encode."""
+    L = load_library()
+    if not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous() or x.numel() % 8 != 0 \
+            or x.numel() == 0:
+        raise ValueError("x: expected a contiguous float32 GPU tensor, a positive multiple of 8 elements")
+    q = torch.empty_like(x)
+    e2m1 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    e4m3 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(L.nvfp4_probe_encode(_ptr(x), x.numel(), float(d), _ptr(q), _ptr(e2m1), _ptr(e4m3),
+                                _stream(stream)))
+    return q, e2m1, e4m3
 
 
 def nvfp4_gemm_w4a16(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None):

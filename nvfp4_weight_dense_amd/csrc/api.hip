@@ -552,6 +552,16 @@ int nvfp4_probe_read(const void *src, int64_t bytes, uint32_t never, float *sink
   return hip_status(launch_read_probe(src, (size_t)bytes, never, sink, (hipStream_t)stream), "read probe launch");
 }
 
+int nvfp4_probe_encode(const float *x, int64_t n, float d, float *q, uint8_t *e2m1, uint8_t *e4m3,
+                       void *stream) {
+  g_err.clear();
+  if (!x || !q || !e2m1 || !e4m3) return fail(NVFP4_EINVAL, "encode probe: null pointer");
+  if (n <= 0 || n % 8 != 0 || n / 8 > (int64_t)0x7FFFFFFF * 256)
+    return fail(NVFP4_EINVAL, "encode probe: n must be a positive multiple of 8");
+  if (!(d > 0.0f) || !(d < INFINITY)) return fail(NVFP4_EINVAL, "encode probe: d must be positive and finite");
+  return hip_status(launch_encode_probe(x, n, d, q, e2m1, e4m3, (hipStream_t)stream), "encode probe launch");
+}
+
 const char *nvfp4_last_error(void) { return g_err.c_str(); }
 
 void nvfp4_release(void) {

@@ -2,13 +2,16 @@
 // quantizers (gfx950).  All are HBM-bound passes over bf16 rows.
 #include <algorithm>
 
+#include "encode_hw.h"
 #include "launchers.h"
 #include "nvfp4_common.h"
 
 // The quantizer's codes must equal the CPU definition bit for bit: every
-// float operation below is one IEEE fp32 operation in the written order
-// (no FMA contraction; fp32 division is correctly rounded: the library is
-// compiled with -fhip-fp32-correctly-rounded-divide-sqrt).
+// float operation below is one IEEE fp32 operation in the written order (no
+// FMA contraction; fp32 division is correctly rounded: the library is
+// compiled with -fhip-fp32-correctly-rounded-divide-sqrt), and the
+// per-element quotients, computed from a rounded reciprocal with one FMA
+// correction, are the correctly rounded ones (encode_hw.h).
 #pragma clang fp contract(off)
 
 namespace nvfp4 {
@@ -61,24 +64,6 @@ __device__ __forceinline__ uint32_t e4m3_encode_sat(float t) {
   v = v + 0x7FFFFu + ((v >> 20) & 1u);
   v &= 0xFFF00000u;
   return (((v >> 23) - 120u) << 3) | ((v >> 20) & 7u);
-}
-
-// fp32 -> E2M1 code, nearest with ties to the even code, saturating at 6,
-// sign kept.  The grid spacing is 0.5 on [0,2), 1 on [2,4), 2 on [4,6]; in
-// each interval the code parity equals the parity of the scaled integer.
-__device__ __forceinline__ uint32_t e2m1_encode_sat(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 31) << 3;
-  const float a = fabsf(q);
-  uint32_t mag;
-  if (!(a < 6.0f))
-    mag = 7u;
-  else if (a < 2.0f)
-    mag = (uint32_t)rintf(a * 2.0f);
-  else if (a < 4.0f)
-    mag = (uint32_t)rintf(a) + 2u;
-  else
-    mag = (uint32_t)rintf(a * 0.5f) + 4u;
-  return sign | mag;
 }
 
 // One workgroup per row, one thread per 16-element block (k % 32 == 0): the
@@ -218,14 +203,23 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows(const uint16
     const float v = e4m3_to_f32(sb);
     const float den = v * s_row;
     uint32_t packed[2] = {0u, 0u};
+    if (v == 0.0f) {
+      // a zero block scale: every code is the sign of its value
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t code;
-      if (xv[i] == 0.0f || v == 0.0f)
-        code = (__float_as_uint(xv[i]) >> 31) << 3;
-      else
-        code = e2m1_encode_sat(xv[i] / den);
-      packed[i >> 3] |= code << (4 * (i & 7));
+      for (int i = 0; i < 16; ++i) packed[i >> 3] |= (__float_as_uint(xv[i]) >> 31) << (4 * (i & 7) + 3);
+    } else {
+      float q[16];
+      if (recip_div_ok(den)) {
+        const float y = 1.0f / den;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = div_by_recip(xv[i], den, y);
+      } else {
+        // (den may underflow to zero here: a zero value keeps its signed zero)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = xv[i] == 0.0f ? xv[i] : xv[i] / den;
+      }
+      packed[0] = e2m1x8_hw(q);
+      packed[1] = e2m1x8_hw(q + 8);
     }
     if (!tiles) {
       *(uint2 *)(codes + (size_t)r * (k >> 1) + 8 * b) = make_uint2(packed[0], packed[1]);
@@ -265,16 +259,27 @@ __global__ __launch_bounds__(kQuantMaxThreads) void k_quantize_rows_fp8(const ui
   if (amax == 0.0f) s_row = 1.0f;
   if (threadIdx.x == 0 && rs.s == 0) row_scale[r] = s_row;
 
+  const bool fast = recip_div_ok(s_row);
+  const float y_row = 1.0f / s_row;
   auto encode_block = [&](int b, const uint4 &v0, const uint4 &v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    float q[16];
+    if (fast) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-      const float q = bf16_bits_to_f32(h) / s_row;
-      const uint32_t code = ((__float_as_uint(q) >> 31) << 7) | e4m3_encode_sat(q);
-      out[i >> 2] |= code << (8 * (i & 3));
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        q[i] = div_by_recip(bf16_bits_to_f32(h), s_row, y_row);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        q[i] = bf16_bits_to_f32(h) / s_row;
+      }
     }
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = e4m3x4_hw(q + 4 * j);
     if (!tiles) {
       *(uint4 *)(codes + (size_t)r * k + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
     } else {

@@ -9,6 +9,7 @@
 // register operands: no memory traffic, no LDS, no dependence between the
 // four accumulators within a round, so the matrix pipe never waits on a
 // result.  Workgroups of four waves (one per SIMD).
+#include "encode_hw.h"
 #include "launchers.h"
 #include "nvfp4_common.h"
 
@@ -61,7 +62,39 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4 *src, size_t n16
   if (f == never) sink[threadIdx.x] = 1.0f;
 }
 
+// Encoder probe: the quantizers' quotient and rounding steps on arbitrary
+// inputs, for the tests.  Thread t takes elements 8t .. 8t + 7 (n % 8 == 0):
+// q = x / d as the quantizers divide, and the E2M1 and E4M3 codes of x
+// itself, one byte per element.
+__global__ __launch_bounds__(256) void k_encode_probe(const float *x, int64_t n8, float d, float *q,
+                                                      uint8_t *e2m1, uint8_t *e4m3) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = x[8 * t + i];
+  const bool fast = recip_div_ok(d);
+  const float y = 1.0f / d;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[8 * t + i] = fast ? div_by_recip(v[i], d, y) : v[i] / d;
+  const uint32_t c4 = e2m1x8_hw(v);
+  const uint32_t c8[2] = {e4m3x4_hw(v), e4m3x4_hw(v + 4)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    e2m1[8 * t + i] = (uint8_t)((c4 >> (4 * i)) & 0xFu);
+    e4m3[8 * t + i] = (uint8_t)(c8[i >> 2] >> (8 * (i & 3)));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_encode_probe(const float *x, int64_t n, float d, float *q, uint8_t *e2m1, uint8_t *e4m3,
+                               hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_encode_probe, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, x, n8, d, q,
+                     e2m1, e4m3);
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t never, float *sink, hipStream_t stream) {
   const size_t n16 = bytes / 16;

@@ -265,5 +265,7 @@ hipError_t launch_fixed_tall_w8a8(const Fp8ActRef &a, int m, int k, int n, int n
 hipError_t launch_mfma_probe(int workgroups, int iters, float *sink, hipStream_t stream);
 // One streaming read of `bytes` (a multiple of 16) at src; see k_probe.hip.
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t never, float *sink, hipStream_t stream);
+hipError_t launch_encode_probe(const float *x, int64_t n, float d, float *q, uint8_t *e2m1, uint8_t *e4m3,
+                               hipStream_t stream);
 
 }  // namespace nvfp4

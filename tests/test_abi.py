@@ -289,3 +289,17 @@ def test_binding_checks_shapes_before_any_launch():
     _match(nv.silu_mul, g, g, out=torch.zeros((2, 9), dtype=bf), msg="out")
     # shapes right, tensors on the CPU: refused as well
     _match(nv.nvfp4_gemm_w4a16, x, W(8, 64), msg="GPU")
+
+
+def test_encode_probe_rejects_bad_arguments_without_launching():
+    L = _lib()
+    p = ctypes.c_void_p(0x40000)
+    null = ctypes.c_void_p(None)
+    f = ctypes.c_float
+    assert L.nvfp4_probe_encode(null, 8, f(1.0), p, p, p, null) == nv.NVFP4_EINVAL
+    assert L.nvfp4_probe_encode(p, 8, f(1.0), p, null, p, null) == nv.NVFP4_EINVAL
+    assert L.nvfp4_probe_encode(p, 12, f(1.0), p, p, p, null) == nv.NVFP4_EINVAL
+    assert L.nvfp4_probe_encode(p, 0, f(1.0), p, p, p, null) == nv.NVFP4_EINVAL
+    assert L.nvfp4_probe_encode(p, 8, f(0.0), p, p, p, null) == nv.NVFP4_EINVAL
+    assert L.nvfp4_probe_encode(p, 8, f(float("inf")), p, p, p, null) == nv.NVFP4_EINVAL
+    assert L.nvfp4_probe_encode(p, 8, f(float("nan")), p, p, p, null) == nv.NVFP4_EINVAL

@@ -182,6 +182,43 @@ def test_quantize_rows_bit_exact(m, k):
     assert np.array_equal(c.cpu().numpy(), co)
 
 
+def test_quantize_rows_every_bf16_below_block_max():
+    """E2M1 rounding decisions under inexact scales.  Each row's maximum has
+    a random mantissa, so s_row = amax/2688 is an inexact fp32, and each run
+    of blocks shares a random block maximum M (element 0 of each block of the
+    run) while the other elements walk every bf16 value in [M/32, M) in
+    order, with random signs: quotients on both sides of every grid midpoint
+    for a few hundred (row scale, block scale) pairs.  Bit for bit against
+    the oracle."""
+    _say("quantize every bf16 below the block max")
+    rng = np.random.default_rng(11)
+    rows, k = 64, 4096
+    nblk = k // 16
+    xb = np.zeros((rows, k), np.uint16)
+    for r in range(rows):
+        amax = (int(rng.integers(127 - 30, 127 + 30)) << 7) | int(rng.integers(0, 128))
+        xb[r, 0] = amax
+        b = 1
+        while b < nblk:
+            mb = amax - int(rng.integers(0, 6 * 128))
+            sweep = np.arange(mb - 5 * 128, mb, dtype=np.uint16)
+            sweep |= (rng.integers(0, 2, sweep.size) << 15).astype(np.uint16)
+            for j in range(0, sweep.size, 15):
+                if b >= nblk:
+                    break
+                part = sweep[j:j + 15]
+                xb[r, 16 * b] = mb
+                xb[r, 16 * b + 1:16 * b + 1 + part.size] = part
+                b += 1
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16)
+    c, s, rs = nv.nvfp4_quantize_rows(x.cuda())
+    sync()
+    co, so, ro = oracle.quantize_rows(xb)
+    assert np.array_equal(rs.cpu().numpy().view(np.uint32), ro.view(np.uint32))
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(c.cpu().numpy(), co)
+
+
 def test_quantize_golden_rows_on_gpu():
     import test_oracle_compute as toc
     rows = toc._read_quant_golden()

@@ -82,6 +82,31 @@ def test_fp8_quantizer_every_bf16_quotient():
     assert np.array_equal(c.cpu().numpy(), co)
 
 
+def test_fp8_quantizer_every_bf16_below_inexact_row_max():
+    """E4M3 rounding decisions under an inexact row scale: each row's maximum
+    has a random mantissa, so s_row = amax/448 is an inexact fp32, and the
+    rest of the row walks every bf16 value in [amax 2^-20, amax) with random
+    signs -- quotients across the whole E4M3 range, subnormals included, on
+    both sides of every midpoint, for 64 row scales.  Bit for bit against
+    the oracle."""
+    _say("fp8 quantize every bf16 below an inexact row max")
+    rng = np.random.default_rng(12)
+    rows, k = 64, 4096
+    xb = np.zeros((rows, k), np.uint16)
+    for r in range(rows):
+        amax = (int(rng.integers(127 - 40, 127 + 40)) << 7) | int(rng.integers(1, 128))
+        sweep = np.arange(amax - 20 * 128, amax, dtype=np.uint16)
+        sweep |= (rng.integers(0, 2, sweep.size) << 15).astype(np.uint16)
+        xb[r, 0] = amax
+        xb[r, 1:1 + sweep.size] = sweep
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16)
+    c, rs = nv.fp8_quantize_rows(x.cuda())
+    sync()
+    co, ro = oracle.quantize_rows_fp8(xb)
+    assert np.array_equal(rs.cpu().numpy(), ro)
+    assert np.array_equal(c.cpu().numpy(), co)
+
+
 # (m, n, k): ragged columns and K; n = 64, k = 4096 splits K over 4
 # workgroups; n >= 16384 takes two column tiles per workgroup, 16400 with a
 # last 16-column tile and a partial scale block along N and K
