@@ -479,6 +479,10 @@ SmallPlan smallm_plan(int m, int n, int k, int nmat) {
   pl.kunits = cdiv(k, kUnitK);
   pl.units = pl.groups * pl.kunits;
   pl.nwg = std::min(kMaxWG, pl.units);
+  // with at most half as many column groups as workgroups, a whole number
+  // of workgroups per group: every range then lies in one group, so no
+  // workgroup holds two pieces (down projection at m=64: 33.2 -> 31.9 us)
+  if (pl.groups * 2 <= kMaxWG && pl.units >= kMaxWG) pl.nwg = (kMaxWG / pl.groups) * pl.groups;
   return pl;
 }
 
